@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention decode step on one MI355X.
+
+One step = one decode call (all kernels of the path) over the whole synthetic batch of
+the chosen workload. Inputs are resident in HBM before timing starts. So that every
+step reads its K/V from HBM and not from the 256 MB Infinity Cache or the L2s, the
+benchmark keeps R identical replicas of the K and V pools (R x pool >= 2 GiB) and step i
+reads replica i mod R, as a decode over many layers does.
+
+Prints ONE JSON line: KV GB/s (unique K/V bytes per step / time per step), % of the
+8 TB/s HBM peak, seq*tokens/s, the roofline of the decode kernel (its duration from
+HIP events on the launch stream) and the fp64 CPU oracle timed on a bounded sample.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--mode auto]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+METRIC = "paged-attn decode KV GB/s read and % of MI355X HBM peak; seqs·tokens/s"
+DEFAULT_MODE = {0: "direct", 1: "direct", 2: "direct", 3: "partitioned", 4: "partitioned"}
+KERNEL_SOURCES = ["pagedattention_block_table_amd/csrc/pa_decode_impl.h",
+                  "pagedattention_block_table_amd/csrc/pa_api.hip"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, mode: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if recorded for this exact
+    kernel source (profiles/traffic_<workload>_<mode>.md), else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{mode}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source_sha:\s*([0-9a-f]+)", text)
+    m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_val or m_hash.group(1) != source_hash():
+        return None
+    return float(m_val.group(1))
+
+
+def compulsory_bytes(b, kv_unique: int) -> int:
+    """Bytes every launch must move at least: unique K/V, q, out, used table entries, lengths."""
+    sp = b.spec
+    io = {"f32": 4, "f16": 2, "bf16": 2}[sp.io_dtype]
+    nblk = sum((int(L) + sp.block_size - 1) // sp.block_size for L in b.context_lens)
+    return kv_unique + 2 * b.q.size * io + 4 * nblk + 4 * b.num_seqs
+
+
+def cpu_baseline(b, seconds: float):
+    """Time the fp64 oracle (as it stands) on whole (sequence, KV head) units of the same
+    batch, round robin over the batch, until `seconds` of work; report KV GB/s."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    sp = b.spec
+    G = sp.num_heads // sp.num_kv_heads
+    e = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}[sp.kv_dtype]
+    units = [(s, g) for g in range(sp.num_kv_heads) for s in range(sp.num_seqs)]
+    # interleave so that a short sample still spans sequences and heads
+    order = [units[(i * 7919) % len(units)] for i in range(len(units))] if len(units) % 7919 else units
+    done = 0
+    nbytes = 0
+    tokens = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for s, g in order:
+            oracle.decode_batch(b, pairs=[(s, g * G + i) for i in range(G)])
+            L = int(b.context_lens[s])
+            nbytes += 2 * L * sp.head_dim * e
+            tokens += L
+            done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {len(units)} (sequence, KV head) units of {sp.name}, all {G} "
+                      f"query heads each, fp64 numpy oracle on 1 thread, {dt:.1f} s",
+            "seq_tokens_per_s": round(tokens / dt, 3) if G else None}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--mode", default="auto", choices=["auto", "direct", "partitioned"])
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--replica-bytes", type=float, default=2 * 2**30)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration for rocprofv3)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import pagedattention_block_table_amd as pa
+    from pagedattention_block_table_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(3)
+    pa._lib.lib()  # fail loudly if the HIP library is missing
+
+    cfg = args.config
+    mode = DEFAULT_MODE[cfg] if args.mode == "auto" else args.mode
+    t0 = time.time()
+    b = W.make_batch(cfg)
+    sp = b.spec
+    log(f"[bench] workload {sp.name}: S={sp.num_seqs} H={sp.num_heads} Hkv={sp.num_kv_heads} "
+        f"D={sp.head_dim} BS={sp.block_size} kv={sp.kv_dtype} sumL={int(b.context_lens.sum())} "
+        f"(generated in {time.time() - t0:.1f}s)")
+
+    import oracle
+    e = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}[sp.kv_dtype]
+    kv_unique = oracle.kv_unique_bytes(b.block_tables, b.context_lens, sp.block_size,
+                                       sp.num_kv_heads, sp.head_dim, e)
+    kv_logical = int(b.context_lens.sum()) * sp.num_kv_heads * sp.head_dim * e * 2
+    algo_bytes = compulsory_bytes(b, kv_unique)
+
+    def dev_t(x, dt):
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    q = dev_t(b.q, sp.io_dtype)
+    bt = torch.from_numpy(b.block_tables).cuda()
+    cl = torch.from_numpy(b.context_lens).cuda()
+    k0 = dev_t(b.k_pool, sp.kv_dtype)
+    v0 = dev_t(b.v_pool, sp.kv_dtype)
+    pool_bytes = k0.numel() * k0.element_size() * 2
+    R = max(2, int(math.ceil(args.replica_bytes / pool_bytes)))
+    ks = [k0] + [k0.clone() for _ in range(R - 1)]
+    vs = [v0] + [v0.clone() for _ in range(R - 1)]
+    out = torch.empty_like(q)
+    P = args.partition_size or sp.partition_size or 512
+    maxL = max(b.max_context_len, 1)
+    ws = None
+    if mode == "partitioned":
+        need = pa.pa_partitioned_workspace_bytes(sp.num_seqs, sp.num_heads, sp.head_dim, maxL, P)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    log(f"[bench] mode={mode} P={P if mode == 'partitioned' else '-'} replicas={R} "
+        f"(pool {pool_bytes / 1e6:.1f} MB each), KV unique {kv_unique / 1e6:.2f} MB")
+
+    def step(i):
+        r = i % R
+        if mode == "direct":
+            pa.pa_decode(q, ks[r], vs[r], bt, cl, scale=float(b.scale), k_scale=float(b.k_scale),
+                         v_scale=float(b.v_scale), out=out, stream=stream)
+        else:
+            pa.pa_decode_partitioned(q, ks[r], vs[r], bt, cl, maxL, scale=float(b.scale),
+                                     partition_size=P, workspace=ws, k_scale=float(b.k_scale),
+                                     v_scale=float(b.v_scale), out=out, stream=stream)
+
+    if args.calibrate_copy:
+        src = torch.empty(2**30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(K):
+        starts[i].record(stream)
+        step(args.warmup + i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    durs_ms = [s.elapsed_time(e_) for s, e_ in zip(starts, ends)]
+    kern_ms = float(np.mean(durs_ms))
+    ms_per_step = wall * 1e3 / K
+
+    value = kv_unique / (ms_per_step * 1e-3) / 1e9
+    achieved = algo_bytes / (kern_ms * 1e-3) / 1e9
+    traffic = read_traffic(sp.name, mode)
+    sum_l = int(b.context_lens.sum())
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": sp.name, "mode": mode,
+                   "partition_size": P if mode == "partitioned" else None,
+                   "num_seqs": sp.num_seqs, "num_heads": sp.num_heads,
+                   "num_kv_heads": sp.num_kv_heads, "head_dim": sp.head_dim,
+                   "block_size": sp.block_size, "io_dtype": sp.io_dtype, "kv_dtype": sp.kv_dtype,
+                   "accumulate": "f32", "sum_context_len": sum_l,
+                   "max_context_len": b.max_context_len, "pool_blocks": b.num_blocks,
+                   "kv_unique_bytes": kv_unique, "kv_logical_bytes": kv_logical,
+                   "kv_replicas": R},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "seq_tokens_per_s": round(sum_l / (ms_per_step * 1e-3), 1),
+        "seqs_per_s": round(sp.num_seqs / (ms_per_step * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel_ms": round(kern_ms, 6),
+                     "algorithmic_bytes_per_launch": algo_bytes,
+                     "p10_p90_ms": [round(float(np.percentile(durs_ms, 10)), 6),
+                                    round(float(np.percentile(durs_ms, 90)), 6)]},
+        "cpu_baseline": None,
+    }
+    log(f"[bench] {ms_per_step * 1e3:.2f} us/step wall, {kern_ms * 1e3:.2f} us/launch (events): "
+        f"{value:.1f} GB/s KV, roofline frac {achieved / HBM_PEAK_GBS:.3f}")
+    del ks, vs
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,158 @@
+/*
+ * pa.h — paged-attention decode over a block table, for AMD Instinct MI355X (gfx950).
+ *
+ * One query token per sequence attends over that sequence's cached keys and values.
+ * The cache lives in fixed-size physical blocks of a shared pool; a per-sequence
+ * block table maps logical block j (tokens j*block_size ... j*block_size +
+ * block_size - 1) to a physical block, and several sequences may name the same
+ * physical block (shared prefixes).
+ *
+ * Pages this interface follows (cited by title and section):
+ *   [P1] "突破GPU内存瓶颈：vLLM与PagedAttention技术深度解析" (ocdem.com), §2: fixed-size
+ *        KV blocks, block table from logical to physical blocks, shared blocks, only
+ *        the last block of a sequence partly filled.
+ *   [P2] vLLM architecture deep-dive (lshu.cn), §1.1: the paged-attention call takes
+ *        queries, blocked key cache, blocked value cache and block tables, and scores
+ *        are q.K^T / sqrt(head_dim); §2.2: attention metadata = block tables, context
+ *        lengths, head count, head size; §3.3 and §4.1: a second, split-context kernel
+ *        for long text; §4.2: FP8 KV cache.
+ *   [P3] "内存优化：KV Cache管理、PagedAttention原理与内存池配置" (5688vip.com): the
+ *        decode step scores the current token's query against all cached K/V; block
+ *        pool figure; KV-size formula.
+ *
+ * What every entry point computes, for sequence s of context length L = context_lens[s]
+ * and query head h (G = num_heads / num_kv_heads, KV head g = h / G):
+ *     z_t = scale * sum_d q[s][h][d] * K(s, g, t)[d]            t = 0 .. L-1
+ *     out[s][h][:] = sum_t softmax(z)_t * V(s, g, t)[:]          (L = 0: zeros)
+ *     K(s, g, t) = k_pool[ block_tables[s][t / block_size] ][g][t % block_size][:]
+ * with fp8 keys/values dequantized as code_value * k_scale (resp. v_scale).
+ * Accumulation is fp32; out is rounded to the io dtype (round to nearest even).
+ *
+ * Layouts (all row-major, all DEVICE memory, all owned by the caller):
+ *   q            [num_seqs][num_heads][head_dim]                 io_dtype
+ *   k_pool       [num_blocks][num_kv_heads][block_size][head_dim] kv_dtype
+ *   v_pool       [num_blocks][num_kv_heads][block_size][head_dim] kv_dtype
+ *   block_tables [num_seqs][max_blocks_per_seq] int32; entries at or past
+ *                ceil(L / block_size) are never read (pad them with anything)
+ *   context_lens [num_seqs] int32
+ *   out          [num_seqs][num_heads][head_dim]                 io_dtype
+ * Pointers to q, the pools and out must be 16-byte aligned.
+ *
+ * Ownership and ordering: the library allocates nothing, frees nothing, keeps no
+ * per-call state and never synchronizes. Each call enqueues its kernels on `stream`
+ * (a hipStream_t; NULL = the default stream) and returns. Inputs must stay unchanged,
+ * and out / workspace untouched, until the stream has passed the call; out must not
+ * alias any input. Calls that share one workspace must be ordered on one stream.
+ *
+ * Errors: the return value is a pa_status. Every argument check runs on the host
+ * before any HIP call; on an error nothing is enqueued. A failed launch returns
+ * PA_ERR_LAUNCH. No C++ exception crosses this interface. Device-side contract
+ * violations (a used block-table entry outside [0, num_blocks), a context length
+ * above max_blocks_per_seq * block_size or above max_context_len) never make the
+ * kernels read outside the buffers: ids are clamped into the pool and lengths into
+ * the bound, and the result for that sequence is unspecified. pa_check_tables reports
+ * such violations.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage types. PA_FP8_E4M3 is the OCP 8-bit e4m3 format (bias 7, max 448, NaN =
+ * S.1111.111, no infinities), valid only as kv_dtype. */
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = -1,     /* null pointer, non-positive size, bad dtype code, ... */
+  PA_ERR_UNSUPPORTED = -2, /* valid but not compiled: head_dim, block_size, group, dtype pair */
+  PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than pa_partitioned_workspace_bytes */
+  PA_ERR_LAUNCH = -4       /* the HIP launch itself failed */
+} pa_status;
+
+/* Supported shapes: head_dim in {64, 128}; block_size in {8, 16, 32} (with fp8 and
+ * head_dim 64, block_size >= 16); num_heads / num_kv_heads in {1, 2, 4, 8};
+ * io_dtype in {F32, F16, BF16}; kv_dtype == io_dtype or PA_FP8_E4M3.
+ * scale, k_scale, v_scale must be finite and > 0 (k_scale / v_scale are ignored unless
+ * kv_dtype is PA_FP8_E4M3). */
+
+/* Single-pass decode ([P2] §1.1 paged-attention call; [P3] decode step): one
+ * workgroup per (sequence, KV head) reads every cached token of that head once,
+ * shares it across the G query heads of the group, and writes out directly. Best for
+ * short and medium contexts; needs no workspace. num_blocks is the pool size. */
+int pa_decode(const void* q, const void* k_pool, const void* v_pool,
+              const int32_t* block_tables, const int32_t* context_lens,
+              int num_seqs, int max_blocks_per_seq, int num_blocks,
+              int num_heads, int num_kv_heads, int head_dim, int block_size,
+              float scale, int io_dtype, int kv_dtype, float k_scale, float v_scale,
+              void* out, void* stream);
+
+/* Workspace for pa_decode_partitioned, in bytes (0 on invalid sizes). Holds, per
+ * (sequence, query head, partition), the running max, the exp-sum and the fp32
+ * partial output. partition_size 0 means the library's default (512 tokens). */
+size_t pa_partitioned_workspace_bytes(int num_seqs, int num_heads, int head_dim,
+                                      int max_context_len, int partition_size);
+
+/* Split-context decode for long contexts ([P2] §3.3 and §4.1 second-version kernel).
+ * The context of every sequence is cut into partitions of partition_size tokens (a
+ * multiple of block_size; 0 = default 512); one workgroup per (sequence, KV head,
+ * partition) writes that partition's max, exp-sum and unnormalized output into the
+ * workspace, and a second kernel on the same stream merges the partitions of each
+ * (sequence, head) by log-sum-exp weighting. Sequences with one partition are written
+ * directly. max_context_len is a host-known bound >= every context_lens[s]; it sizes
+ * the grid and the workspace. */
+int pa_decode_partitioned(const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int num_seqs, int max_blocks_per_seq, int num_blocks,
+                          int num_heads, int num_kv_heads, int head_dim, int block_size,
+                          float scale, int io_dtype, int kv_dtype, float k_scale,
+                          float v_scale, int max_context_len, int partition_size,
+                          void* workspace, size_t workspace_bytes,
+                          void* out, void* stream);
+
+/* Instrumented decode for tests ([P1] §2 block-table reading; every cached position
+ * is read exactly once). Runs the same kernels as pa_decode (partition_size == 0) or
+ * pa_decode_partitioned (partition_size > 0, workspace required) and, as the kernel
+ * consumes each valid cached row of (sequence s, KV head g, token t), also
+ *   copies the raw K row to k_rows[((s * num_kv_heads + g) * max_context_len + t) * head_dim]
+ *   copies the raw V row to v_rows[ same ]                      (kv_dtype elements)
+ *   adds 1 to read_counts[(s * num_kv_heads + g) * max_context_len + t]
+ * read_counts must be zeroed by the caller; rows never consumed are left untouched.
+ * max_context_len must be >= every context length. */
+int pa_debug_trace(const void* q, const void* k_pool, const void* v_pool,
+                   const int32_t* block_tables, const int32_t* context_lens,
+                   int num_seqs, int max_blocks_per_seq, int num_blocks,
+                   int num_heads, int num_kv_heads, int head_dim, int block_size,
+                   float scale, int io_dtype, int kv_dtype, float k_scale, float v_scale,
+                   int max_context_len, int partition_size,
+                   void* workspace, size_t workspace_bytes, void* out,
+                   void* k_rows, void* v_rows, int32_t* read_counts, void* stream);
+
+/* Device-side check of the block-table contract. For each sequence s writes
+ * errors[s] = 0 if fine, else a bit set: 1 = context length < 0, 2 = context length
+ * above max_blocks_per_seq * block_size, 4 = some used entry outside [0, num_blocks),
+ * 8 = context length above max_context_len (if max_context_len > 0). */
+int pa_check_tables(const int32_t* block_tables, const int32_t* context_lens,
+                    int num_seqs, int max_blocks_per_seq, int num_blocks, int block_size,
+                    int max_context_len, int32_t* errors, void* stream);
+
+/* Converts n OCP e4m3 codes to fp32 with the same in-register conversion the decode
+ * kernels use (for tests of the fp8 path). */
+int pa_debug_fp8_to_f32(const uint8_t* codes, float* out, int n, void* stream);
+
+/* Static text for a status code. */
+const char* pa_status_str(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

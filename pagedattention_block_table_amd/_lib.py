@@ -1,0 +1,227 @@
+"""ctypes binding of libpa.so (declared in include/pa.h).
+
+Argument marshalling only: torch tensors are checked for device, dtype, shape and
+layout, turned into device pointers, and handed to the C entry points of the same
+names on torch's current HIP stream. Every step of the decode runs in the library's
+kernels; there is no CPU path. If the library is missing the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
+PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_LAUNCH = 0, -1, -2, -3, -4
+DEFAULT_PARTITION = 512
+
+# name -> (restype, argtypes), mirroring include/pa.h
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+_DECODE_ARGS = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _F, _F]
+SIGNATURES = {
+    "pa_decode": (_I, _DECODE_ARGS + [_P, _P]),
+    "pa_partitioned_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "pa_decode_partitioned": (_I, _DECODE_ARGS + [_I, _I, _P, _SZ, _P, _P]),
+    "pa_debug_trace": (_I, _DECODE_ARGS + [_I, _I, _P, _SZ, _P, _P, _P, _P, _P]),
+    "pa_check_tables": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P]),
+    "pa_debug_fp8_to_f32": (_I, [_P, _P, _I, _P]),
+    "pa_status_str": (ctypes.c_char_p, [_I]),
+    "pa_version": (_I, []),
+}
+
+_lib = None
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} returned {status}: {pa_status_str(status)}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpa.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                               "(run `python -m pagedattention_block_table_amd.build`)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def pa_status_str(status: int) -> str:
+    return lib().pa_status_str(int(status)).decode()
+
+
+def pa_version() -> int:
+    return int(lib().pa_version())
+
+
+def pa_partitioned_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int,
+                                   max_context_len: int, partition_size: int = 0) -> int:
+    return int(lib().pa_partitioned_workspace_bytes(num_seqs, num_heads, head_dim,
+                                                    max_context_len, partition_size))
+
+
+# ----------------------------------------------------------------------------------
+# torch-facing wrappers
+# ----------------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
+         torch.uint8: PA_FP8_E4M3}
+    if hasattr(torch, "float8_e4m3fn"):
+        m[torch.float8_e4m3fn] = PA_FP8_E4M3
+    if t.dtype not in m:
+        raise TypeError(f"unsupported tensor dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _check_dev(name, t):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _shapes(q, k_pool, v_pool, block_tables, context_lens):
+    torch = _torch()
+    for n, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool),
+                 ("block_tables", block_tables), ("context_lens", context_lens)):
+        _check_dev(n, t)
+    if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
+        raise ValueError("q must be [S][H][D]; k_pool and v_pool [NB][Hkv][BS][D] of equal shape")
+    if k_pool.dtype != v_pool.dtype:
+        raise ValueError("k_pool and v_pool must share a dtype")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    S, H, D = q.shape
+    NB, Hkv, BS, D2 = k_pool.shape
+    if D2 != D:
+        raise ValueError("head_dim of q and pools differ")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [S][max_blocks] and context_lens [S]")
+    return S, H, D, NB, Hkv, BS, int(block_tables.shape[1])
+
+
+def _common(q, k_pool, v_pool, block_tables, context_lens, scale, k_scale, v_scale, out):
+    torch = _torch()
+    S, H, D, NB, Hkv, BS, MB = _shapes(q, k_pool, v_pool, block_tables, context_lens)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_dev("out", out)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    args = [q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_tables.data_ptr(),
+            context_lens.data_ptr(), S, MB, NB, H, Hkv, D, BS, float(scale), dtype_code(q),
+            dtype_code(k_pool), float(k_scale), float(v_scale)]
+    return args, out, (S, H, D, NB, Hkv, BS, MB)
+
+
+def _raise(fn, rc):
+    if rc != PA_OK:
+        raise PagedAttentionError(fn, rc)
+
+
+def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale: Optional[float] = None,
+              k_scale: float = 1.0, v_scale: float = 1.0, out=None, stream=None):
+    """Single-pass paged decode; returns out [S][H][D] (q's dtype)."""
+    args, out, _ = _common(q, k_pool, v_pool, block_tables, context_lens, scale, k_scale, v_scale, out)
+    _raise("pa_decode", lib().pa_decode(*args, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def pa_decode_partitioned(q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
+                          scale: Optional[float] = None, partition_size: int = 0,
+                          workspace=None, k_scale: float = 1.0, v_scale: float = 1.0,
+                          out=None, stream=None):
+    """Split-context paged decode with log-sum-exp merge; returns out."""
+    torch = _torch()
+    args, out, (S, H, D, *_rest) = _common(q, k_pool, v_pool, block_tables, context_lens, scale,
+                                           k_scale, v_scale, out)
+    need = pa_partitioned_workspace_bytes(S, H, D, int(max_context_len), int(partition_size))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_dev("workspace", workspace)
+    nbytes = workspace.numel() * workspace.element_size()
+    _raise("pa_decode_partitioned",
+           lib().pa_decode_partitioned(*args, int(max_context_len), int(partition_size),
+                                       workspace.data_ptr(), nbytes, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def pa_debug_trace(q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
+                   scale: Optional[float] = None, partition_size: int = 0, k_scale: float = 1.0,
+                   v_scale: float = 1.0, stream=None):
+    """Instrumented decode; returns (out, k_rows, v_rows, read_counts)."""
+    torch = _torch()
+    args, out, (S, H, D, NB, Hkv, BS, MB) = _common(q, k_pool, v_pool, block_tables, context_lens,
+                                                   scale, k_scale, v_scale, None)
+    workspace = None
+    nbytes = 0
+    if partition_size:
+        need = pa_partitioned_workspace_bytes(S, H, D, int(max_context_len), int(partition_size))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        nbytes = need
+    k_rows = torch.zeros((S, Hkv, max_context_len, D), dtype=k_pool.dtype, device=q.device)
+    v_rows = torch.zeros_like(k_rows)
+    counts = torch.zeros((S, Hkv, max_context_len), dtype=torch.int32, device=q.device)
+    _raise("pa_debug_trace",
+           lib().pa_debug_trace(*args, int(max_context_len), int(partition_size),
+                                workspace.data_ptr() if workspace is not None else None, nbytes,
+                                out.data_ptr(), k_rows.data_ptr(), v_rows.data_ptr(),
+                                counts.data_ptr(), _stream(stream)))
+    return out, k_rows, v_rows, counts
+
+
+def pa_check_tables(block_tables, context_lens, num_blocks: int, block_size: int,
+                    max_context_len: int = 0, stream=None):
+    """Per-sequence contract violation bits (see include/pa.h)."""
+    torch = _torch()
+    _check_dev("block_tables", block_tables)
+    _check_dev("context_lens", context_lens)
+    S, MB = block_tables.shape
+    err = torch.empty(S, dtype=torch.int32, device=block_tables.device)
+    _raise("pa_check_tables",
+           lib().pa_check_tables(block_tables.data_ptr(), context_lens.data_ptr(), S, MB,
+                                 int(num_blocks), int(block_size), int(max_context_len),
+                                 err.data_ptr(), _stream(stream)))
+    return err
+
+
+def pa_debug_fp8_to_f32(codes, stream=None):
+    torch = _torch()
+    _check_dev("codes", codes)
+    out = torch.empty(codes.numel(), dtype=torch.float32, device=codes.device)
+    _raise("pa_debug_fp8_to_f32",
+           lib().pa_debug_fp8_to_f32(codes.data_ptr(), out.data_ptr(), codes.numel(), _stream(stream)))
+    return out

@@ -1,0 +1,383 @@
+// C interface of the paged-attention decode library: argument checks, kernel choice,
+// the split-context log-sum-exp merge, the block-table checker and the fp8 probe.
+//
+// Pages cited by title and section:
+//   [P1] "突破GPU内存瓶颈：vLLM与PagedAttention技术深度解析" §2 (block table, shared blocks)
+//   [P2] vLLM architecture deep-dive §1.1 (paged-attention call), §2.2 (metadata),
+//        §3.3 / §4.1 (second, split-context kernel for long text), §4.2 (FP8 KV cache)
+//   [P3] "内存优化：KV Cache管理、PagedAttention原理与内存池配置" (decode over all cached K/V)
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "pa.h"
+#include "pa_decode_impl.h"
+
+namespace pa {
+namespace {
+
+constexpr int kDefaultPartition = 512;
+
+struct MergeArgs {
+  const float* ws;
+  const int32_t* context_lens;
+  void* out;
+  int num_seqs;
+  int num_heads;
+  int num_parts;
+  int part_tokens;
+  int max_ctx;
+};
+
+// Log-sum-exp merge of the partitions of one (sequence, head) per wave ([P2] §3.3 /
+// §4.1 split-context kernel; the merge rule is the exact recombination of softmax
+// partial sums): M = max_p m_p, w_p = exp2(m_p - M), out = sum_p w_p o_p / sum_p w_p l_p.
+// Scores are in log2 units, as the decode kernel wrote them.
+template <int IO, int D>
+__global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a) {
+  constexpr int PER = D / 64;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * 4 + wave;
+  if (pair >= a.num_seqs * a.num_heads) return;
+  const int s = pair / a.num_heads;
+  int L = a.context_lens[s];
+  L = min(max(L, 0), a.max_ctx);
+  const int n = (L + a.part_tokens - 1) / a.part_tokens;
+  if (n <= 1) return;  // written directly by the decode kernel
+  const int64_t NPH = (int64_t)a.num_seqs * a.num_heads * a.num_parts;
+  const float* m = a.ws + (int64_t)pair * a.num_parts;
+  const float* l = a.ws + NPH + (int64_t)pair * a.num_parts;
+  const float* o = a.ws + 2 * NPH + (int64_t)pair * a.num_parts * D;
+
+  float M = -3.0e38f;
+  for (int p = lane; p < n; p += 64) M = fmaxf(M, m[p]);
+  M = rows_max<1>(M);
+
+  float acc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  float den = 0.f;
+#pragma unroll 4
+  for (int p = 0; p < n; ++p) {
+    const float w = __builtin_amdgcn_exp2f(m[p] - M);
+    den = fmaf(w, l[p], den);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] = fmaf(w, o[(int64_t)p * D + lane + 64 * k], acc[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) store_io<IO>(a.out, (int64_t)pair * D + lane + 64 * k, acc[k] / den);
+}
+
+// One thread per sequence checks its used block-table entries.
+__global__ void check_tables_kernel(const int32_t* bt, const int32_t* cl, int S, int MB, int NB,
+                                    int BS, int max_ctx, int32_t* err) {
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= S) return;
+  const int L = cl[s];
+  int e = 0;
+  if (L < 0) e |= 1;
+  if ((int64_t)L > (int64_t)MB * BS) e |= 2;
+  if (max_ctx > 0 && L > max_ctx) e |= 8;
+  const int64_t nb = L > 0 ? min(((int64_t)L + BS - 1) / BS, (int64_t)MB) : 0;
+  for (int64_t j = 0; j < nb; ++j) {
+    const int b = bt[(int64_t)s * MB + j];
+    if (b < 0 || b >= NB) {
+      e |= 4;
+      break;
+    }
+  }
+  err[s] = e;
+}
+
+__global__ void fp8_probe_kernel(const uint8_t* codes, float* out, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int base = i * 16;
+  if (base >= n) return;
+  uint8_t b[16];
+  for (int k = 0; k < 16; ++k) b[k] = base + k < n ? codes[base + k] : 0;
+  uint4 r;
+  r.x = b[0] | (b[1] << 8) | (b[2] << 16) | ((uint32_t)b[3] << 24);
+  r.y = b[4] | (b[5] << 8) | (b[6] << 16) | ((uint32_t)b[7] << 24);
+  r.z = b[8] | (b[9] << 8) | (b[10] << 16) | ((uint32_t)b[11] << 24);
+  r.w = b[12] | (b[13] << 8) | (b[14] << 16) | ((uint32_t)b[15] << 24);
+  float f[16];
+  widen16<kFP8>(r, f);
+  for (int k = 0; k < 16; ++k)
+    if (base + k < n) out[base + k] = f[k];
+}
+
+bool is_pow_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+int elem_bytes(int dt) {
+  switch (dt) {
+    case PA_F32: return 4;
+    case PA_F16: return 2;
+    case PA_BF16: return 2;
+    case PA_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool pos_finite(float x) { return std::isfinite(x) && x > 0.f; }
+
+struct Common {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* bt;
+  const int32_t* cl;
+  int S, MB, NB, H, Hkv, D, BS;
+  float scale;
+  int io, kv;
+  float ks, vs;
+  void* out;
+};
+
+int validate(const Common& c) {
+  if (!c.q || !c.k_pool || !c.v_pool || !c.bt || !c.cl || !c.out) return PA_ERR_INVALID;
+  if (c.S <= 0 || c.MB <= 0 || c.NB <= 0 || c.H <= 0 || c.Hkv <= 0 || c.D <= 0 || c.BS <= 0)
+    return PA_ERR_INVALID;
+  if (c.io != PA_F32 && c.io != PA_F16 && c.io != PA_BF16) return PA_ERR_INVALID;
+  if (elem_bytes(c.kv) == 0) return PA_ERR_INVALID;
+  if (c.H % c.Hkv != 0) return PA_ERR_INVALID;
+  if (!pos_finite(c.scale)) return PA_ERR_INVALID;
+  if (c.kv == PA_FP8_E4M3 && (!pos_finite(c.ks) || !pos_finite(c.vs))) return PA_ERR_INVALID;
+  if (!aligned16(c.q) || !aligned16(c.k_pool) || !aligned16(c.v_pool) || !aligned16(c.out))
+    return PA_ERR_INVALID;
+  if ((int64_t)c.MB * c.BS > INT_MAX / 2) return PA_ERR_INVALID;
+  if (c.kv != c.io && c.kv != PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
+  if (c.D != 64 && c.D != 128) return PA_ERR_UNSUPPORTED;
+  if (c.BS != 8 && c.BS != 16 && c.BS != 32) return PA_ERR_UNSUPPORTED;
+  if (!is_pow_group(c.H / c.Hkv)) return PA_ERR_UNSUPPORTED;
+  const int lpt = c.D * elem_bytes(c.kv) / 16;
+  const int tpl = 64 / lpt;
+  if (c.BS % tpl != 0) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+int launch_pair(int io, int kv, const LaunchSpec& ls) {
+  if (kv == PA_FP8_E4M3) {
+    switch (io) {
+      case PA_F32: return launch_f32_fp8(ls);
+      case PA_F16: return launch_f16_fp8(ls);
+      case PA_BF16: return launch_bf16_fp8(ls);
+    }
+  } else {
+    switch (io) {
+      case PA_F32: return launch_f32_f32(ls);
+      case PA_F16: return launch_f16_f16(ls);
+      case PA_BF16: return launch_bf16_bf16(ls);
+    }
+  }
+  return PA_ERR_UNSUPPORTED;
+}
+
+template <int IO>
+int launch_merge_io(int D, const MergeArgs& m, int grid, hipStream_t st) {
+  if (D == 64) {
+    hipLaunchKernelGGL((merge_kernel<IO, 64>), dim3(grid), dim3(256), 0, st, m);
+  } else {
+    hipLaunchKernelGGL((merge_kernel<IO, 128>), dim3(grid), dim3(256), 0, st, m);
+  }
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int launch_merge(int io, int D, const MergeArgs& m, int grid, hipStream_t st) {
+  switch (io) {
+    case PA_F32: return launch_merge_io<kF32>(D, m, grid, st);
+    case PA_F16: return launch_merge_io<kF16>(D, m, grid, st);
+    case PA_BF16: return launch_merge_io<kBF16>(D, m, grid, st);
+  }
+  return PA_ERR_UNSUPPORTED;
+}
+
+DecodeArgs base_args(const Common& c) {
+  DecodeArgs a{};
+  a.q = c.q;
+  a.k_pool = c.k_pool;
+  a.v_pool = c.v_pool;
+  a.block_tables = c.bt;
+  a.context_lens = c.cl;
+  a.out = c.out;
+  a.num_seqs = c.S;
+  a.max_blocks_per_seq = c.MB;
+  a.num_blocks = c.NB;
+  a.num_heads = c.H;
+  a.num_kv_heads = c.Hkv;
+  const bool fp8 = c.kv == PA_FP8_E4M3;
+  a.q_mul = c.scale * kLog2e * (fp8 ? c.ks : 1.f);
+  a.out_mul = fp8 ? c.vs : 1.f;
+  return a;
+}
+
+int64_t num_parts_for(int max_context_len, int P) {
+  const int64_t n = ((int64_t)max_context_len + P - 1) / P;
+  return n < 1 ? 1 : n;
+}
+
+// Shared body of the partitioned and debug entry points. P == 0 selects single-pass mode.
+int run(const Common& c, int max_context_len, int P, void* workspace, size_t ws_bytes,
+        void* dk, void* dv, int32_t* dcounts, bool debug, hipStream_t st) {
+  int rc = validate(c);
+  if (rc != PA_OK) return rc;
+  LaunchSpec ls{};
+  ls.args = base_args(c);
+  ls.head_dim = c.D;
+  ls.block_size = c.BS;
+  ls.group = c.H / c.Hkv;
+  ls.debug = debug;
+  ls.stream = st;
+  const int cap = c.MB * c.BS;  // a table row covers at most this many tokens
+  int64_t NP = 1;
+  if (P > 0) {
+    if (max_context_len < 0) return PA_ERR_INVALID;
+    if (P % c.BS != 0) return PA_ERR_INVALID;
+    NP = num_parts_for(max_context_len, P);
+    const size_t need = pa_partitioned_workspace_bytes(c.S, c.H, c.D, max_context_len, P);
+    if (need == 0) return PA_ERR_INVALID;
+    if (NP > 1 && (!workspace || ws_bytes < need)) return PA_ERR_WORKSPACE;
+    if (NP > 1 && !aligned16(workspace)) return PA_ERR_INVALID;
+    ls.args.part_tokens = P;
+    ls.args.max_ctx = max_context_len < cap ? max_context_len : cap;
+  } else {
+    ls.args.max_ctx = cap;
+    if (debug && max_context_len >= 0 && max_context_len < cap) ls.args.max_ctx = max_context_len;
+    ls.args.part_tokens = ls.args.max_ctx > 0 ? ls.args.max_ctx : 1;
+  }
+  ls.args.num_parts = (int)NP;
+  ls.args.ws = (float*)workspace;
+  if (debug) {
+    if (!dk || !dv || !dcounts || max_context_len <= 0) return PA_ERR_INVALID;
+    if (!aligned16(dk) || !aligned16(dv)) return PA_ERR_INVALID;
+    ls.args.dbg_k = dk;
+    ls.args.dbg_v = dv;
+    ls.args.dbg_counts = dcounts;
+    ls.args.dbg_max_ctx = max_context_len;
+    if (ls.args.max_ctx > max_context_len) ls.args.max_ctx = max_context_len;
+  }
+  const int64_t grid = (int64_t)c.Hkv * c.S * NP;
+  if (grid > INT_MAX) return PA_ERR_INVALID;
+  ls.grid = (int)grid;
+  rc = launch_pair(c.io, c.kv, ls);
+  if (rc != PA_OK || NP <= 1) return rc;
+  MergeArgs m{};
+  m.ws = (const float*)workspace;
+  m.context_lens = c.cl;
+  m.out = c.out;
+  m.num_seqs = c.S;
+  m.num_heads = c.H;
+  m.num_parts = (int)NP;
+  m.part_tokens = P;
+  m.max_ctx = ls.args.max_ctx;
+  const int64_t pairs = (int64_t)c.S * c.H;
+  return launch_merge(c.io, c.D, m, (int)((pairs + 3) / 4), st);
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" {
+
+int pa_decode(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+              const int32_t* context_lens, int num_seqs, int max_blocks_per_seq, int num_blocks,
+              int num_heads, int num_kv_heads, int head_dim, int block_size, float scale,
+              int io_dtype, int kv_dtype, float k_scale, float v_scale, void* out, void* stream) {
+  try {
+    pa::Common c{q, k_pool, v_pool, block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                 num_blocks, num_heads, num_kv_heads, head_dim, block_size, scale, io_dtype,
+                 kv_dtype, k_scale, v_scale, out};
+    return pa::run(c, -1, 0, nullptr, 0, nullptr, nullptr, nullptr, false, (hipStream_t)stream);
+  } catch (...) {
+    return PA_ERR_LAUNCH;
+  }
+}
+
+size_t pa_partitioned_workspace_bytes(int num_seqs, int num_heads, int head_dim,
+                                      int max_context_len, int partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0 || partition_size < 0)
+    return 0;
+  const int P = partition_size == 0 ? pa::kDefaultPartition : partition_size;
+  const int64_t NP = pa::num_parts_for(max_context_len, P);
+  const int64_t floats = (int64_t)num_seqs * num_heads * NP * (head_dim + 2);
+  return (size_t)(floats * 4);
+}
+
+int pa_decode_partitioned(const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                          int max_blocks_per_seq, int num_blocks, int num_heads, int num_kv_heads,
+                          int head_dim, int block_size, float scale, int io_dtype, int kv_dtype,
+                          float k_scale, float v_scale, int max_context_len, int partition_size,
+                          void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  try {
+    if (partition_size < 0) return PA_ERR_INVALID;
+    const int P = partition_size == 0 ? pa::kDefaultPartition : partition_size;
+    pa::Common c{q, k_pool, v_pool, block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                 num_blocks, num_heads, num_kv_heads, head_dim, block_size, scale, io_dtype,
+                 kv_dtype, k_scale, v_scale, out};
+    return pa::run(c, max_context_len, P, workspace, workspace_bytes, nullptr, nullptr, nullptr,
+                   false, (hipStream_t)stream);
+  } catch (...) {
+    return PA_ERR_LAUNCH;
+  }
+}
+
+int pa_debug_trace(const void* q, const void* k_pool, const void* v_pool,
+                   const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                   int max_blocks_per_seq, int num_blocks, int num_heads, int num_kv_heads,
+                   int head_dim, int block_size, float scale, int io_dtype, int kv_dtype,
+                   float k_scale, float v_scale, int max_context_len, int partition_size,
+                   void* workspace, size_t workspace_bytes, void* out, void* k_rows, void* v_rows,
+                   int32_t* read_counts, void* stream) {
+  try {
+    if (partition_size < 0) return PA_ERR_INVALID;
+    pa::Common c{q, k_pool, v_pool, block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                 num_blocks, num_heads, num_kv_heads, head_dim, block_size, scale, io_dtype,
+                 kv_dtype, k_scale, v_scale, out};
+    return pa::run(c, max_context_len, partition_size, workspace, workspace_bytes, k_rows, v_rows,
+                   read_counts, true, (hipStream_t)stream);
+  } catch (...) {
+    return PA_ERR_LAUNCH;
+  }
+}
+
+int pa_check_tables(const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                    int max_blocks_per_seq, int num_blocks, int block_size, int max_context_len,
+                    int32_t* errors, void* stream) {
+  if (!block_tables || !context_lens || !errors) return PA_ERR_INVALID;
+  if (num_seqs <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || block_size <= 0)
+    return PA_ERR_INVALID;
+  const int threads = 256;
+  const int grid = (num_seqs + threads - 1) / threads;
+  hipLaunchKernelGGL(pa::check_tables_kernel, dim3(grid), dim3(threads), 0, (hipStream_t)stream,
+                     block_tables, context_lens, num_seqs, max_blocks_per_seq, num_blocks,
+                     block_size, max_context_len, errors);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int pa_debug_fp8_to_f32(const uint8_t* codes, float* out, int n, void* stream) {
+  if (!codes || !out || n <= 0) return PA_ERR_INVALID;
+  const int lanes = (n + 15) / 16;
+  const int grid = (lanes + 255) / 256;
+  hipLaunchKernelGGL(pa::fp8_probe_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, codes, out, n);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+const char* pa_status_str(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported shape or dtype combination";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int pa_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,567 @@
+// Paged-attention decode kernels for gfx950 (CDNA4, wave64).
+//
+// What is computed (pages cited by title and section):
+//   [P1] "突破GPU内存瓶颈：vLLM与PagedAttention技术深度解析" §2 — K/V are stored in
+//        fixed-size blocks; a block table maps a sequence's logical blocks to physical
+//        ones; only the last block is partly filled; blocks may be shared.
+//   [P2] vLLM architecture deep-dive §1.1 — scores are q.K^T / sqrt(d); the kernel
+//        loads on demand the blocks named by the table. §3.3 / §4.1 — a split-context
+//        second kernel for long text. §4.2 — FP8 KV cache.
+//   [P3] "内存优化：KV Cache管理、PagedAttention原理与内存池配置" — decode scores the
+//        current query against every cached K/V of the sequence.
+//
+// Work decomposition. A work unit is (KV head g, sequence s, partition p); one
+// workgroup of NW waves runs it. The unit's blocks are dealt to the waves in chunks of
+// U consecutive logical blocks, round robin. Within a wave, lane `lane` owns the 16
+// bytes at column c = lane % LPT of token row r = lane / LPT of each wave load, where
+// LPT = head_dim * elem_bytes / 16 lanes cover one token row. One wave load therefore
+// reads TPL = 64 / LPT consecutive token rows = 1 KiB of contiguous tile memory.
+// A K/V tile (one physical block, one KV head) is BS * D * e contiguous bytes, so the
+// NL = BS / TPL loads of a tile stream one contiguous run.
+//
+// Arithmetic (all fp32): each lane-row group keeps its own online-softmax state
+// (running max m, running sum l, output accumulator) for the G query heads of the
+// group, over the tokens it reads, with scores in log2 units (scale * log2(e) folded
+// into q, and k_scale too for fp8). Every chunk: scores by per-lane dot products reduced
+// across the LPT lanes of the row with DPP; m' = max(m, chunk max); rescale by
+// exp2(m - m'); accumulate exp2(z - m') * V. Tokens past the end are excluded by select
+// (their score is -inf and their rows are never loaded), never by multiplying by zero.
+// At the end the row states of a wave are merged with cross-lane shuffles and the wave
+// states of the workgroup through LDS, with the same max/rescale/sum rule.
+//
+// The order of arithmetic depends only on logical token positions, never on physical
+// block ids, so results are bitwise identical under any physical placement or sharing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+enum : int { kF32 = PA_F32, kF16 = PA_F16, kBF16 = PA_BF16, kFP8 = PA_FP8_E4M3 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int T> struct ElemBytes;
+template <> struct ElemBytes<kF32> { static constexpr int value = 4; };
+template <> struct ElemBytes<kF16> { static constexpr int value = 2; };
+template <> struct ElemBytes<kBF16> { static constexpr int value = 2; };
+template <> struct ElemBytes<kFP8> { static constexpr int value = 1; };
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Arguments shared by every decode kernel instance (passed by value).
+struct DecodeArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  void* out;
+  float* ws;             // partitioned mode: m [S*H*NP], l [S*H*NP], o [S*H*NP*D]
+  void* dbg_k;           // debug: raw K rows [S][Hkv][dbg_max_ctx][D]
+  void* dbg_v;
+  int32_t* dbg_counts;   // debug: [S][Hkv][dbg_max_ctx]
+  int num_seqs;
+  int max_blocks_per_seq;
+  int num_blocks;
+  int num_heads;
+  int num_kv_heads;
+  int part_tokens;       // tokens per partition (multiple of BS)
+  int num_parts;         // partitions per (s, g) in the grid
+  int max_ctx;           // context lengths are clamped to [0, max_ctx]
+  int dbg_max_ctx;
+  float q_mul;           // scale * log2(e) (* k_scale for fp8)
+  float out_mul;         // v_scale for fp8, else 1
+};
+
+// ---------------------------------------------------------------------------------
+// storage conversions
+// ---------------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __builtin_bit_cast(float, bits16 << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// 16 bytes of KV storage -> 16 / elem_bytes fp32 values, in memory order.
+template <int T> __device__ __forceinline__ void widen16(const uint4& r, float* f);
+
+template <> __device__ __forceinline__ void widen16<kF32>(const uint4& r, float* f) {
+  f[0] = __builtin_bit_cast(float, r.x);
+  f[1] = __builtin_bit_cast(float, r.y);
+  f[2] = __builtin_bit_cast(float, r.z);
+  f[3] = __builtin_bit_cast(float, r.w);
+}
+
+template <> __device__ __forceinline__ void widen16<kF16>(const uint4& r, float* f) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f16x2 h = __builtin_bit_cast(f16x2, w[i]);
+    f[2 * i] = (float)h.x;
+    f[2 * i + 1] = (float)h.y;
+  }
+}
+
+template <> __device__ __forceinline__ void widen16<kBF16>(const uint4& r, float* f) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+    f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+  }
+}
+
+// gfx950 converts OCP e4m3 pairs in hardware; word_sel picks bytes {0,1} or {2,3}.
+template <> __device__ __forceinline__ void widen16<kFP8>(const uint4& r, float* f) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+    f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+    f[4 * i + 0] = lo.x;
+    f[4 * i + 1] = lo.y;
+    f[4 * i + 2] = hi.x;
+    f[4 * i + 3] = hi.y;
+  }
+}
+
+template <int IO> __device__ __forceinline__ float load_io(const void* p, int64_t i) {
+  if constexpr (IO == kF32) {
+    return ((const float*)p)[i];
+  } else if constexpr (IO == kF16) {
+    return (float)((const _Float16*)p)[i];
+  } else {
+    return bf16_to_f32(((const uint16_t*)p)[i]);
+  }
+}
+
+template <int IO> __device__ __forceinline__ void store_io(void* p, int64_t i, float v) {
+  if constexpr (IO == kF32) {
+    ((float*)p)[i] = v;
+  } else if constexpr (IO == kF16) {
+    ((_Float16*)p)[i] = (_Float16)v;
+  } else {
+    ((uint16_t*)p)[i] = f32_to_bf16_rne(v);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// cross-lane reductions
+// ---------------------------------------------------------------------------------
+
+template <int CTRL> __device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                                0xF, 0xF, false));
+}
+
+// DPP controls (gfx9): quad_perm = s0 | s1 << 2 | s2 << 4 | s3 << 6; row_ror n = 0x120 + n;
+// row_half_mirror = 0x141.
+constexpr int kQuadXor1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);
+constexpr int kQuadXor2 = 2 | (3 << 2) | (0 << 4) | (1 << 6);
+constexpr int kRowHalfMirror = 0x141;
+
+// Sum over aligned groups of N consecutive lanes; every lane receives its group's sum.
+template <int N> __device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group");
+  if constexpr (N == 1) {
+    return x;
+  } else if constexpr (N == 2) {
+    return x + dpp<kQuadXor1>(x);
+  } else if constexpr (N == 4) {
+    x += dpp<kQuadXor1>(x);
+    return x + dpp<kQuadXor2>(x);
+  } else if constexpr (N == 8) {
+    // lane i (of 8) + lane 7-i, then the quad sum covers all eight.
+    x += dpp<kRowHalfMirror>(x);
+    x += dpp<kQuadXor1>(x);
+    return x + dpp<kQuadXor2>(x);
+  } else if constexpr (N == 16) {
+    x += dpp<0x128>(x);  // row_ror 8
+    x += dpp<0x124>(x);  // row_ror 4
+    x += dpp<0x122>(x);  // row_ror 2
+    return x + dpp<0x121>(x);  // row_ror 1
+  } else if constexpr (N == 32) {
+    x = group_sum<16>(x);
+    return x + __shfl_xor(x, 16);
+  } else {
+    x = group_sum<16>(x);
+    x += __shfl_xor(x, 16);
+    return x + __shfl_xor(x, 32);
+  }
+}
+
+// Reduce across the row groups of a wave: lanes that differ only in bits >= log2(STRIDE).
+template <int STRIDE> __device__ __forceinline__ float rows_max(float x) {
+#pragma unroll
+  for (int k = STRIDE; k < 64; k <<= 1) x = fmaxf(x, __shfl_xor(x, k));
+  return x;
+}
+template <int STRIDE> __device__ __forceinline__ float rows_sum(float x) {
+#pragma unroll
+  for (int k = STRIDE; k < 64; k <<= 1) x += __shfl_xor(x, k);
+  return x;
+}
+
+// ---------------------------------------------------------------------------------
+// XCD-aware unit order
+// ---------------------------------------------------------------------------------
+
+// Workgroups are dispatched round robin over the 8 XCDs (each with its own L2).
+// Map workgroup i to unit v so that each XCD receives one contiguous range of units;
+// units are ordered KV-head-major, so the sequences that share prefix blocks of one KV
+// head read them through the same L2.
+__device__ __forceinline__ int xcd_unit(int i, int n) {
+  constexpr int X = 8;
+  const int xcd = i % X;
+  const int k = i / X;
+  const int per = n / X;
+  const int rem = n % X;
+  return xcd * per + min(xcd, rem) + k;
+}
+
+// ---------------------------------------------------------------------------------
+// the decode kernel
+// ---------------------------------------------------------------------------------
+
+template <int KV, int D, int BS, int G_>
+struct Geometry {
+  static constexpr int E = ElemBytes<KV>::value;
+  static constexpr int VEC = 16 / E;           // elements per lane load
+  static constexpr int LPT = D / VEC;          // lanes per token row
+  static constexpr int TPL = 64 / LPT;         // token rows per wave load
+  static constexpr int NL = BS / TPL;          // wave loads per tile
+  static constexpr int ROW_BYTES = D * E;
+  static constexpr int TILE = BS * D * E;      // bytes of one (block, kv-head) tile
+  static constexpr bool ok = (LPT >= 1) && (LPT <= 64) && (TPL >= 1) && (BS % TPL == 0);
+};
+
+template <int G, int VEC> struct RowState {
+  float m[G];
+  float l[G];
+  float acc[G][VEC];
+};
+
+// One chunk of U consecutive logical blocks starting at j0. TAIL: the chunk reaches past
+// the end of the unit's token range (some rows or whole blocks are invalid).
+template <int IO, int KV, int D, int BS, int G, int U, bool TAIL, bool DBG>
+__device__ __forceinline__ void process_chunk(const DecodeArgs& a, const int32_t* bt,
+                                              const char* kbase, const char* vbase,
+                                              int64_t blk_stride, int j0, int j_end, int t_end,
+                                              int r, int c, int s, int g,
+                                              const float (&qf)[G][16 / ElemBytes<KV>::value],
+                                              RowState<G, 16 / ElemBytes<KV>::value>& st) {
+  using Geo = Geometry<KV, D, BS, G>;
+  constexpr int VEC = Geo::VEC, NL = Geo::NL, TPL = Geo::TPL, LPT = Geo::LPT;
+  const uint32_t lane_off = (uint32_t)(r * Geo::ROW_BYTES + c * 16);
+
+  int bid[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = j0 + u;
+    int b = 0;
+    if (!TAIL || j < j_end) b = bt[j];
+    // contract: 0 <= b < num_blocks; clamp so that a bad table never reads outside the pool
+    b = min(max(b, 0), a.num_blocks - 1);
+    bid[u] = __builtin_amdgcn_readfirstlane(b);
+  }
+
+  uint4 kr[U][NL];
+  uint4 vr[U][NL];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const char* kb = kbase + (int64_t)bid[u] * blk_stride;
+    const char* vb = vbase + (int64_t)bid[u] * blk_stride;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const uint32_t off = lane_off + (uint32_t)(i * TPL * Geo::ROW_BYTES);
+      if (TAIL) {
+        const int t = (j0 + u) * BS + i * TPL + r;
+        if (t < t_end) {
+          kr[u][i] = *(const uint4*)(kb + off);
+          vr[u][i] = *(const uint4*)(vb + off);
+        } else {
+          kr[u][i] = make_uint4(0, 0, 0, 0);
+          vr[u][i] = make_uint4(0, 0, 0, 0);
+        }
+      } else {
+        kr[u][i] = *(const uint4*)(kb + off);
+        vr[u][i] = *(const uint4*)(vb + off);
+      }
+    }
+  }
+
+  if constexpr (DBG) {
+    const int Hkv = a.num_kv_heads;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int t = (j0 + u) * BS + i * TPL + r;
+        if (t < t_end) {
+          const int64_t row = ((int64_t)s * Hkv + g) * a.dbg_max_ctx + t;
+          *(uint4*)((char*)a.dbg_k + row * Geo::ROW_BYTES + c * 16) = kr[u][i];
+          *(uint4*)((char*)a.dbg_v + row * Geo::ROW_BYTES + c * 16) = vr[u][i];
+          if (c == 0) atomicAdd(a.dbg_counts + row, 1);
+        }
+      }
+    }
+  }
+
+  // scores (log2 units)
+  float z[U][NL][G];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      float kf[VEC];
+      widen16<KV>(kr[u][i], kf);
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc = fmaf(qf[gi][e], kf[e], acc);
+        acc = group_sum<LPT>(acc);
+        if (TAIL) {
+          const int t = (j0 + u) * BS + i * TPL + r;
+          acc = (t < t_end) ? acc : -INFINITY;
+        }
+        z[u][i][gi] = acc;
+      }
+    }
+  }
+
+  // online softmax update
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    float mx = st.m[gi];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < NL; ++i) mx = fmaxf(mx, z[u][i][gi]);
+    const float alpha = __builtin_amdgcn_exp2f(st.m[gi] - mx);
+    st.m[gi] = mx;
+    st.l[gi] *= alpha;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) st.acc[gi][e] *= alpha;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      float vf[VEC];
+      widen16<KV>(vr[u][i], vf);
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        const float p = __builtin_amdgcn_exp2f(z[u][i][gi] - st.m[gi]);
+        st.l[gi] += p;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) st.acc[gi][e] = fmaf(p, vf[e], st.acc[gi][e]);
+      }
+    }
+  }
+}
+
+template <int IO, int KV, int D, int BS, int G, int NW, int U, bool DBG>
+__global__ void __launch_bounds__(NW * 64)
+decode_kernel(const DecodeArgs a) {
+  using Geo = Geometry<KV, D, BS, G>;
+  static_assert(Geo::ok, "unsupported geometry");
+  constexpr int VEC = Geo::VEC, LPT = Geo::LPT;
+
+  __shared__ float sm_m[NW][G];
+  __shared__ float sm_l[NW][G];
+  __shared__ float sm_o[NW][G][D];
+
+  const int unit = xcd_unit((int)blockIdx.x, (int)gridDim.x);
+  const int part = unit % a.num_parts;
+  const int sg = unit / a.num_parts;
+  const int s = sg % a.num_seqs;
+  const int g = sg / a.num_seqs;
+
+  int L = a.context_lens[s];
+  L = min(max(L, 0), a.max_ctx);
+  const int t_begin = part * a.part_tokens;
+  if (part > 0 && t_begin >= L) return;  // nothing in this partition (whole workgroup)
+  const int t_end = min(L, t_begin + a.part_tokens);
+  const int j_begin = t_begin / BS;
+  const int j_end = (t_end + BS - 1) / BS;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int r = lane / LPT;
+  const int c = lane % LPT;
+  const int H = a.num_heads;
+
+  // q of the G heads of this group, this lane's VEC columns, pre-scaled to log2 units
+  float qf[G][VEC];
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    const int64_t base = ((int64_t)s * H + (int64_t)g * G + gi) * D + c * VEC;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) qf[gi][e] = load_io<IO>(a.q, base + e) * a.q_mul;
+  }
+
+  RowState<G, VEC> st;
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    st.m[gi] = -3.0e38f;
+    st.l[gi] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) st.acc[gi][e] = 0.f;
+  }
+
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const int64_t blk_stride = (int64_t)a.num_kv_heads * Geo::TILE;
+  const char* kbase = (const char*)a.k_pool + (int64_t)g * Geo::TILE;
+  const char* vbase = (const char*)a.v_pool + (int64_t)g * Geo::TILE;
+
+  for (int j0 = j_begin + wave * U; j0 < j_end; j0 += NW * U) {
+    if ((j0 + U) * BS <= t_end) {
+      process_chunk<IO, KV, D, BS, G, U, false, DBG>(a, bt, kbase, vbase, blk_stride, j0, j_end,
+                                                     t_end, r, c, s, g, qf, st);
+    } else {
+      process_chunk<IO, KV, D, BS, G, U, true, DBG>(a, bt, kbase, vbase, blk_stride, j0, j_end,
+                                                    t_end, r, c, s, g, qf, st);
+    }
+  }
+
+  // merge the row groups of this wave
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    const float M = rows_max<LPT>(st.m[gi]);
+    const float f = __builtin_amdgcn_exp2f(st.m[gi] - M);
+    st.m[gi] = M;
+    st.l[gi] = rows_sum<LPT>(st.l[gi] * f);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) st.acc[gi][e] = rows_sum<LPT>(st.acc[gi][e] * f);
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) sm_o[wave][gi][c * VEC + e] = st.acc[gi][e];
+      if (c == 0) {
+        sm_m[wave][gi] = st.m[gi];
+        sm_l[wave][gi] = st.l[gi];
+      }
+    }
+  }
+  __syncthreads();
+
+  // merge the waves and write
+  const int n_parts_s = (L + a.part_tokens - 1) / a.part_tokens;
+  const bool write_out = n_parts_s <= 1;
+  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
+    const int gi = idx / D;
+    const int d = idx % D;
+    float M = sm_m[0][gi];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][gi]);
+    float o = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = __builtin_amdgcn_exp2f(sm_m[w][gi] - M);
+      o = fmaf(f, sm_o[w][gi][d], o);
+      lsum = fmaf(f, sm_l[w][gi], lsum);
+    }
+    const int h = g * G + gi;
+    if (write_out) {
+      const float v = lsum > 0.f ? (o / lsum) * a.out_mul : 0.f;
+      store_io<IO>(a.out, ((int64_t)s * H + h) * D + d, v);
+    } else {
+      const int64_t NPH = (int64_t)a.num_seqs * H * a.num_parts;
+      const int64_t slot = ((int64_t)s * H + h) * a.num_parts + part;
+      a.ws[2 * NPH + slot * D + d] = o * a.out_mul;
+      if (d == 0) {
+        a.ws[slot] = M;
+        a.ws[NPH + slot] = lsum;
+      }
+    }
+  }
+}
+
+// Per-(io, kv) launcher; defined in one translation unit per dtype pair.
+struct LaunchSpec {
+  DecodeArgs args;
+  int head_dim;
+  int block_size;
+  int group;
+  bool debug;
+  int grid;
+  hipStream_t stream;
+};
+
+template <int IO, int KV, int D, int BS, int G>
+constexpr int pick_unroll() {
+  // Consecutive blocks per wave iteration: about 32 tokens, at least one block.
+  return BS >= 32 ? 1 : 32 / BS;
+}
+
+template <int IO, int KV, int D, int BS, int G>
+int launch_one(const LaunchSpec& ls) {
+  if constexpr (!Geometry<KV, D, BS, G>::ok) {
+    return PA_ERR_UNSUPPORTED;
+  } else {
+    constexpr int NW = 4;
+    constexpr int U = pick_unroll<IO, KV, D, BS, G>();
+    if (ls.debug) {
+      hipLaunchKernelGGL((decode_kernel<IO, KV, D, BS, G, NW, U, true>), dim3(ls.grid), dim3(NW * 64),
+                         0, ls.stream, ls.args);
+    } else {
+      hipLaunchKernelGGL((decode_kernel<IO, KV, D, BS, G, NW, U, false>), dim3(ls.grid), dim3(NW * 64),
+                         0, ls.stream, ls.args);
+    }
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+  }
+}
+
+template <int IO, int KV, int D, int BS>
+int launch_g(const LaunchSpec& ls) {
+  switch (ls.group) {
+    case 1: return launch_one<IO, KV, D, BS, 1>(ls);
+    case 2: return launch_one<IO, KV, D, BS, 2>(ls);
+    case 4: return launch_one<IO, KV, D, BS, 4>(ls);
+    case 8: return launch_one<IO, KV, D, BS, 8>(ls);
+    default: return PA_ERR_UNSUPPORTED;
+  }
+}
+
+template <int IO, int KV, int D>
+int launch_bs(const LaunchSpec& ls) {
+  switch (ls.block_size) {
+    case 8: return launch_g<IO, KV, D, 8>(ls);
+    case 16: return launch_g<IO, KV, D, 16>(ls);
+    case 32: return launch_g<IO, KV, D, 32>(ls);
+    default: return PA_ERR_UNSUPPORTED;
+  }
+}
+
+template <int IO, int KV>
+int launch_decode(const LaunchSpec& ls) {
+  switch (ls.head_dim) {
+    case 64: return launch_bs<IO, KV, 64>(ls);
+    case 128: return launch_bs<IO, KV, 128>(ls);
+    default: return PA_ERR_UNSUPPORTED;
+  }
+}
+
+// Explicit per-pair entry points (one translation unit each, compiled in parallel).
+int launch_f32_f32(const LaunchSpec&);
+int launch_f16_f16(const LaunchSpec&);
+int launch_bf16_bf16(const LaunchSpec&);
+int launch_f32_fp8(const LaunchSpec&);
+int launch_f16_fp8(const LaunchSpec&);
+int launch_bf16_fp8(const LaunchSpec&);
+
+}  // namespace pa

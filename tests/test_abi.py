@@ -1,0 +1,135 @@
+"""The C-ABI library: it loads, exports every symbol include/pa.h declares, and its host
+argument checks return the documented status codes before any HIP call (no GPU needed:
+only invalid calls are made, and they return before touching the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from pagedattention_block_table_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libpa.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(pa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_signatures():
+    names = declared_functions()
+    assert names == sorted(_lib.SIGNATURES), names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_version():
+    assert _lib.pa_status_str(0) == "ok"
+    assert "workspace" in _lib.pa_status_str(-3)
+    assert _lib.pa_status_str(12345) == "unknown status"
+    assert _lib.pa_version() >= 100
+
+
+def test_workspace_bytes_formula():
+    # per (sequence, head, partition): max, sum and head_dim partial outputs, fp32
+    assert _lib.pa_partitioned_workspace_bytes(8, 32, 128, 32768, 512) == 8 * 32 * 64 * 130 * 4
+    assert _lib.pa_partitioned_workspace_bytes(2, 4, 64, 1000, 0) == 2 * 4 * 2 * 66 * 4
+    assert _lib.pa_partitioned_workspace_bytes(2, 4, 64, 0, 0) == 2 * 4 * 1 * 66 * 4
+    assert _lib.pa_partitioned_workspace_bytes(0, 4, 64, 10, 0) == 0
+    assert _lib.pa_partitioned_workspace_bytes(1, 4, 64, -1, 0) == 0
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+def good_args(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, S=4, MB=7, NB=32, H=4, Hkv=4, D=64, BS=16,
+             scale=0.125, io=_lib.PA_F32, kv=_lib.PA_F32, ks=1.0, vs=1.0)
+    a.update(over)
+    return [a[k] for k in ("q", "k", "v", "bt", "cl", "S", "MB", "NB", "H", "Hkv", "D", "BS",
+                           "scale", "io", "kv", "ks", "vs")]
+
+
+BAD = [
+    (dict(q=0), _lib.PA_ERR_INVALID),
+    (dict(bt=0), _lib.PA_ERR_INVALID),
+    (dict(cl=0), _lib.PA_ERR_INVALID),
+    (dict(S=0), _lib.PA_ERR_INVALID),
+    (dict(NB=-1), _lib.PA_ERR_INVALID),
+    (dict(io=3), _lib.PA_ERR_INVALID),
+    (dict(io=7), _lib.PA_ERR_INVALID),
+    (dict(kv=9), _lib.PA_ERR_INVALID),
+    (dict(H=6, Hkv=4), _lib.PA_ERR_INVALID),
+    (dict(scale=0.0), _lib.PA_ERR_INVALID),
+    (dict(scale=float("nan")), _lib.PA_ERR_INVALID),
+    (dict(kv=_lib.PA_FP8_E4M3, ks=0.0), _lib.PA_ERR_INVALID),
+    (dict(kv=_lib.PA_FP8_E4M3, vs=float("inf")), _lib.PA_ERR_INVALID),
+    (dict(q=FAKE + 2), _lib.PA_ERR_INVALID),
+    (dict(k=FAKE + 8), _lib.PA_ERR_INVALID),
+    (dict(kv=_lib.PA_F16), _lib.PA_ERR_UNSUPPORTED),
+    (dict(D=96), _lib.PA_ERR_UNSUPPORTED),
+    (dict(BS=64), _lib.PA_ERR_UNSUPPORTED),
+    (dict(H=48, Hkv=3), _lib.PA_ERR_UNSUPPORTED),
+    (dict(io=_lib.PA_F16, kv=_lib.PA_FP8_E4M3, D=64, BS=8), _lib.PA_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("over,code", BAD, ids=[str(b[0]) for b in BAD])
+def test_decode_rejects(over, code):
+    L = _lib.lib()
+    assert L.pa_decode(*good_args(**over), FAKE, None) == code
+    assert L.pa_decode(*good_args(**over), 0, None) == _lib.PA_ERR_INVALID  # null out first
+
+
+@pytest.mark.parametrize("over,code", BAD[:6], ids=[str(b[0]) for b in BAD[:6]])
+def test_partitioned_rejects(over, code):
+    L = _lib.lib()
+    assert L.pa_decode_partitioned(*good_args(**over), 100, 64, FAKE, 1 << 20, FAKE, None) == code
+
+
+def test_partitioned_workspace_and_partition_checks():
+    L = _lib.lib()
+    a = good_args()
+    # partition not a multiple of block_size
+    assert L.pa_decode_partitioned(*a, 100, 24, FAKE, 1 << 20, FAKE, None) == _lib.PA_ERR_INVALID
+    assert L.pa_decode_partitioned(*a, 100, -16, FAKE, 1 << 20, FAKE, None) == _lib.PA_ERR_INVALID
+    assert L.pa_decode_partitioned(*a, -5, 64, FAKE, 1 << 20, FAKE, None) == _lib.PA_ERR_INVALID
+    need = _lib.pa_partitioned_workspace_bytes(4, 4, 64, 100, 32)
+    assert L.pa_decode_partitioned(*a, 100, 32, FAKE, need - 4, FAKE, None) == _lib.PA_ERR_WORKSPACE
+    assert L.pa_decode_partitioned(*a, 100, 32, 0, need, FAKE, None) == _lib.PA_ERR_WORKSPACE
+    assert L.pa_decode_partitioned(*a, 100, 32, FAKE + 4, need, FAKE, None) == _lib.PA_ERR_INVALID
+
+
+def test_debug_trace_requires_buffers():
+    L = _lib.lib()
+    a = good_args()
+    assert L.pa_debug_trace(*a, 100, 0, None, 0, FAKE, 0, FAKE, FAKE, None) == _lib.PA_ERR_INVALID
+    assert L.pa_debug_trace(*a, 100, 0, None, 0, FAKE, FAKE, FAKE, 0, None) == _lib.PA_ERR_INVALID
+    assert L.pa_debug_trace(*a, 0, 0, None, 0, FAKE, FAKE, FAKE, FAKE, None) == _lib.PA_ERR_INVALID
+
+
+def test_small_entry_points_reject():
+    L = _lib.lib()
+    assert L.pa_check_tables(0, FAKE, 4, 7, 32, 16, 0, FAKE, None) == _lib.PA_ERR_INVALID
+    assert L.pa_check_tables(FAKE, FAKE, 0, 7, 32, 16, 0, FAKE, None) == _lib.PA_ERR_INVALID
+    assert L.pa_debug_fp8_to_f32(FAKE, FAKE, 0, None) == _lib.PA_ERR_INVALID
+    assert L.pa_debug_fp8_to_f32(0, FAKE, 16, None) == _lib.PA_ERR_INVALID
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 4, 64)
+    pool = torch.zeros(2, 4, 16, 64)
+    bt = torch.zeros(1, 1, dtype=torch.int32)
+    cl = torch.ones(1, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        _lib.pa_decode(q, pool, pool, bt, cl)
