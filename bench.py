@@ -173,15 +173,17 @@ def main():
     log(f"[bench] mode={mode} P={P if mode == 'partitioned' else '-'} replicas={R} "
         f"(pool {pool_bytes / 1e6:.1f} MB each), KV unique {kv_unique / 1e6:.2f} MB")
 
+    kw = dict(scale=float(b.scale), k_scale=float(b.k_scale), v_scale=float(b.v_scale),
+              out=out, stream=stream)
+    if mode == "direct":
+        plan = pa.DecodePlan(q, k0, v0, bt, cl, **kw)
+    else:
+        plan = pa.DecodePlan(q, k0, v0, bt, cl, max_context_len=maxL, partition_size=P,
+                             workspace=ws, **kw)
+
     def step(i):
         r = i % R
-        if mode == "direct":
-            pa.pa_decode(q, ks[r], vs[r], bt, cl, scale=float(b.scale), k_scale=float(b.k_scale),
-                         v_scale=float(b.v_scale), out=out, stream=stream)
-        else:
-            pa.pa_decode_partitioned(q, ks[r], vs[r], bt, cl, maxL, scale=float(b.scale),
-                                     partition_size=P, workspace=ws, k_scale=float(b.k_scale),
-                                     v_scale=float(b.v_scale), out=out, stream=stream)
+        plan(ks[r], vs[r])
 
     if args.calibrate_copy:
         src = torch.empty(2**30, dtype=torch.uint8, device="cuda")

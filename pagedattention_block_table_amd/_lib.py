@@ -13,7 +13,8 @@ import os
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpa.so")
+# PA_LIBRARY may name another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpa.so")
 
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_LAUNCH = 0, -1, -2, -3, -4
@@ -201,6 +202,55 @@ def pa_debug_trace(q, k_pool, v_pool, block_tables, context_lens, max_context_le
                                 out.data_ptr(), k_rows.data_ptr(), v_rows.data_ptr(),
                                 counts.data_ptr(), _stream(stream)))
     return out, k_rows, v_rows, counts
+
+
+class DecodePlan:
+    """Arguments of one decode, checked and marshalled once, for calls repeated on the
+    same buffers (a decode loop). Calling the plan enqueues the decode on its stream; the
+    pools may be swapped per call for others of identical shape and dtype (another
+    layer's cache). Marshalling only: the decode itself runs in the library."""
+
+    def __init__(self, q, k_pool, v_pool, block_tables, context_lens, scale=None,
+                 k_scale: float = 1.0, v_scale: float = 1.0, out=None,
+                 max_context_len: Optional[int] = None, partition_size: int = 0,
+                 workspace=None, stream=None):
+        torch = _torch()
+        args, out, (S, H, D, *_r) = _common(q, k_pool, v_pool, block_tables, context_lens,
+                                            scale, k_scale, v_scale, out)
+        self.out = out
+        self._kmeta = (tuple(k_pool.shape), k_pool.dtype, k_pool.device)
+        self._keep = [q, k_pool, v_pool, block_tables, context_lens, out]
+        st = _stream(stream)
+        if max_context_len is None:
+            self._fn = lib().pa_decode
+            tail = [out.data_ptr(), st]
+        else:
+            need = pa_partitioned_workspace_bytes(S, H, D, int(max_context_len), int(partition_size))
+            if workspace is None:
+                workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+            _check_dev("workspace", workspace)
+            self._keep.append(workspace)
+            self._fn = lib().pa_decode_partitioned
+            tail = [int(max_context_len), int(partition_size), workspace.data_ptr(),
+                    workspace.numel() * workspace.element_size(), out.data_ptr(), st]
+        full = args + tail
+        self._args = [t(v) if v is not None else None
+                      for t, v in zip(self._fn.argtypes, full)]
+        self._name = self._fn.__name__
+
+    def __call__(self, k_pool=None, v_pool=None):
+        a = self._args
+        if k_pool is not None:
+            if (tuple(k_pool.shape), k_pool.dtype, k_pool.device) != self._kmeta or \
+               (tuple(v_pool.shape), v_pool.dtype, v_pool.device) != self._kmeta:
+                raise ValueError("replacement pools must match the planned pools")
+            a = list(a)
+            a[1] = k_pool.data_ptr()
+            a[2] = v_pool.data_ptr()
+        rc = self._fn(*a)
+        if rc != PA_OK:
+            raise PagedAttentionError(self._name, rc)
+        return self.out
 
 
 def pa_check_tables(block_tables, context_lens, num_blocks: int, block_size: int,

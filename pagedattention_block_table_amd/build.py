@@ -35,9 +35,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
+def _compile(src: str, verbose: bool, build_dir: str = BUILD, defines=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src).replace(".hip", ".o"))
     cmd = [hipcc(), "-c", "-fPIC", "-O3", "-std=c++17", f"--offload-arch={ARCH}", *DEVICE_FLAGS,
+           *[f"-D{d}" for d in defines],
            "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC, "-o", obj, src]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -51,32 +52,37 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(jobs: int = 0, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int = 0, verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile and link; `defines` (NAME=VALUE) select compile-time tuning knobs and
+    `out` names the library file (the package loads LIB unless told otherwise)."""
+    build_dir = BUILD if out == LIB else os.path.join(BUILD, "v_" + os.path.basename(out).replace(".so", ""))
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not srcs:
         raise RuntimeError("no HIP sources found")
     jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
     t0 = time.time()
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, defines), srcs))
+    tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources in {time.time() - t0:.1f}s", flush=True)
-    return LIB
+        print(f"built {out} from {len(srcs)} sources in {time.time() - t0:.1f}s", flush=True)
+    return out
 
 
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=0)
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--out", default=LIB)
+    ap.add_argument("-D", dest="defines", action="append", default=[])
     a = ap.parse_args()
-    print(build(a.jobs, a.verbose))
+    print(build(a.jobs, a.verbose, os.path.abspath(a.out), a.defines))
 
 
 if __name__ == "__main__":

@@ -252,6 +252,19 @@ template <int G, int VEC> struct RowState {
   float acc[G][VEC];
 };
 
+#ifndef PA_NT_LOADS
+#define PA_NT_LOADS 0
+#endif
+
+// 16-byte K/V load; streamed data is read once per unit.
+__device__ __forceinline__ uint4 load16(const char* p) {
+#if PA_NT_LOADS
+  return __builtin_nontemporal_load((const uint4*)p);
+#else
+  return *(const uint4*)p;
+#endif
+}
+
 // One chunk of U consecutive logical blocks starting at j0. TAIL: the chunk reaches past
 // the end of the unit's token range (some rows or whole blocks are invalid).
 template <int IO, int KV, int D, int BS, int G, int U, bool TAIL, bool DBG>
@@ -288,15 +301,15 @@ __device__ __forceinline__ void process_chunk(const DecodeArgs& a, const int32_t
       if (TAIL) {
         const int t = (j0 + u) * BS + i * TPL + r;
         if (t < t_end) {
-          kr[u][i] = *(const uint4*)(kb + off);
-          vr[u][i] = *(const uint4*)(vb + off);
+          kr[u][i] = load16(kb + off);
+          vr[u][i] = load16(vb + off);
         } else {
           kr[u][i] = make_uint4(0, 0, 0, 0);
           vr[u][i] = make_uint4(0, 0, 0, 0);
         }
       } else {
-        kr[u][i] = *(const uint4*)(kb + off);
-        vr[u][i] = *(const uint4*)(vb + off);
+        kr[u][i] = load16(kb + off);
+        vr[u][i] = load16(vb + off);
       }
     }
   }
@@ -502,10 +515,17 @@ struct LaunchSpec {
   hipStream_t stream;
 };
 
+#ifndef PA_WAVES
+#define PA_WAVES 4
+#endif
+#ifndef PA_CHUNK_TOKENS
+#define PA_CHUNK_TOKENS 32
+#endif
+
 template <int IO, int KV, int D, int BS, int G>
 constexpr int pick_unroll() {
-  // Consecutive blocks per wave iteration: about 32 tokens, at least one block.
-  return BS >= 32 ? 1 : 32 / BS;
+  // Consecutive blocks per wave iteration: about PA_CHUNK_TOKENS tokens, at least one block.
+  return BS >= PA_CHUNK_TOKENS ? 1 : PA_CHUNK_TOKENS / BS;
 }
 
 template <int IO, int KV, int D, int BS, int G>
@@ -513,7 +533,7 @@ int launch_one(const LaunchSpec& ls) {
   if constexpr (!Geometry<KV, D, BS, G>::ok) {
     return PA_ERR_UNSUPPORTED;
   } else {
-    constexpr int NW = 4;
+    constexpr int NW = PA_WAVES;
     constexpr int U = pick_unroll<IO, KV, D, BS, G>();
     if (ls.debug) {
       hipLaunchKernelGGL((decode_kernel<IO, KV, D, BS, G, NW, U, true>), dim3(ls.grid), dim3(NW * 64),

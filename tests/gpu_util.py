@@ -52,8 +52,23 @@ def to_f64(t):
     return t.to(torch.float64).cpu().numpy()
 
 
-def check_against_oracle(b, got, pairs=None, tol=None):
-    """Element-wise comparison of the GPU output with the oracle on (s, h) pairs."""
+# significand bits of each io format, for the half-ulp output-rounding allowance
+IO_PRECISION = {"f32": 24, "f16": 11, "bf16": 8}
+
+
+def half_ulp(io, x):
+    """Half a unit in the last place of the io format at |x| (normal range)."""
+    _, ex = np.frexp(np.abs(x))
+    return np.ldexp(1.0, ex - 1 - IO_PRECISION[io])
+
+
+def check_against_oracle(b, got, pairs=None, tol=None, io_rounding=False):
+    """Element-wise comparison of the GPU output with the oracle on (s, h) pairs.
+
+    The bar is the stated max |delta|. With io_rounding, each element may in addition
+    differ by the half ulp that rounding the exact result to the io format costs: the
+    stated bars are below that half ulp once |out| >= 1 in bf16 (|out| >= 8 in f16),
+    which only the short-context edge cases reach."""
     import oracle
     sp = b.spec
     ref = oracle.decode_batch(b, pairs=pairs)
@@ -64,7 +79,11 @@ def check_against_oracle(b, got, pairs=None, tol=None):
     g = got[idx_s, idx_h]
     r = ref[idx_s, idx_h]
     assert np.isfinite(g).all(), "non-finite GPU output"
-    err = float(np.abs(g - r).max()) if g.size else 0.0
     bar = TOL[sp.kv_dtype] if tol is None else tol
-    assert err <= bar, f"{sp.name}: max |gpu - oracle| = {err:.3e} > {bar:.1e}"
+    d = np.abs(g - r)
+    err = float(d.max()) if g.size else 0.0
+    allow = bar + (half_ulp(sp.io_dtype, r) if io_rounding else 0.0)
+    worst = float((d - allow).max()) if g.size else -1.0
+    assert worst <= 0, f"{sp.name}: max |gpu - oracle| = {err:.3e} exceeds bar {bar:.1e}" + (
+        " + half ulp" if io_rounding else "")
     return err
