@@ -107,8 +107,10 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1)
-    ap.add_argument("--mode", default="auto", choices=["auto", "direct", "partitioned"])
+    ap.add_argument("--mode", default="auto", choices=["auto", "direct", "partitioned", "balanced"])
     ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--workgroups", type=int, default=0,
+                    help="balanced mode: workgroup count (0 = library default)")
     ap.add_argument("--replica-bytes", type=float, default=2 * 2**30)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -177,6 +179,8 @@ def main():
               out=out, stream=stream)
     if mode == "direct":
         plan = pa.DecodePlan(q, k0, v0, bt, cl, **kw)
+    elif mode == "balanced":
+        plan = pa.DecodePlan(q, k0, v0, bt, cl, balanced=True, num_workgroups=args.workgroups, **kw)
     else:
         plan = pa.DecodePlan(q, k0, v0, bt, cl, max_context_len=maxL, partition_size=P,
                              workspace=ws, **kw)
@@ -231,6 +235,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": sp.name, "mode": mode,
                    "partition_size": P if mode == "partitioned" else None,
+                   "workgroups": (args.workgroups or "library default") if mode == "balanced" else None,
                    "num_seqs": sp.num_seqs, "num_heads": sp.num_heads,
                    "num_kv_heads": sp.num_kv_heads, "head_dim": sp.head_dim,
                    "block_size": sp.block_size, "io_dtype": sp.io_dtype, "kv_dtype": sp.kv_dtype,

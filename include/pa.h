@@ -115,10 +115,40 @@ int pa_decode_partitioned(const void* q, const void* k_pool, const void* v_pool,
                           void* workspace, size_t workspace_bytes,
                           void* out, void* stream);
 
+/* Workspace for pa_decode_balanced, in bytes (0 on invalid sizes): one int32 arrival
+ * counter per (KV head, sequence), padded to 256 bytes, then two fp32 partial-state slots
+ * (G running maxima, G exp-sums, G x head_dim partial outputs; G = num_heads /
+ * num_kv_heads) per workgroup. num_workgroups 0 means the library's default (two per
+ * compute unit of the current device). */
+size_t pa_balanced_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                   int num_workgroups);
+
+/* Work-balanced decode. Same result as pa_decode; the schedule differs: the cached tokens
+ * of every (KV head, sequence) are cut into 32-token chunks, and a fixed grid of
+ * num_workgroups workgroups (0 = library default) takes equal shares of all chunks of the
+ * batch, whatever the mix of context lengths. A (KV head, sequence) whose chunks are
+ * shared by several workgroups is finished by the last of them to arrive, which merges
+ * the others' partial states by log-sum-exp weighting (the rule of the split-context
+ * kernel, [P2] §3.3 / §4.1). Everything happens in one kernel launch.
+ * Workspace: pa_balanced_workspace_bytes(...) bytes, 16-byte aligned. Its counter area
+ * must be zero before the first call (e.g. hipMemset once after allocating); every
+ * completed call leaves it zero again. Calls sharing a workspace must be ordered on one
+ * stream. Shapes outside the matrix-core kernels (fp32 io or KV, 8 query heads per KV
+ * head, rows of 64 bytes) and batches of more than 4096 sequences run the single-pass
+ * kernel of pa_decode instead and leave the workspace untouched. */
+int pa_decode_balanced(const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       int num_seqs, int max_blocks_per_seq, int num_blocks,
+                       int num_heads, int num_kv_heads, int head_dim, int block_size,
+                       float scale, int io_dtype, int kv_dtype, float k_scale, float v_scale,
+                       int num_workgroups, void* workspace, size_t workspace_bytes,
+                       void* out, void* stream);
+
 /* Instrumented decode for tests ([P1] §2 block-table reading; every cached position
- * is read exactly once). Runs the same kernels as pa_decode (partition_size == 0) or
- * pa_decode_partitioned (partition_size > 0, workspace required) and, as the kernel
- * consumes each valid cached row of (sequence s, KV head g, token t), also
+ * is read exactly once). Runs the same kernels as pa_decode (partition_size == 0 and
+ * num_workgroups == 0), pa_decode_partitioned (partition_size > 0, workspace required) or
+ * pa_decode_balanced (num_workgroups > 0, workspace required, counters zero) and, as the
+ * kernel consumes each valid cached row of (sequence s, KV head g, token t), also
  *   copies the raw K row to k_rows[((s * num_kv_heads + g) * max_context_len + t) * head_dim]
  *   copies the raw V row to v_rows[ same ]                      (kv_dtype elements)
  *   adds 1 to read_counts[(s * num_kv_heads + g) * max_context_len + t]
@@ -129,7 +159,7 @@ int pa_debug_trace(const void* q, const void* k_pool, const void* v_pool,
                    int num_seqs, int max_blocks_per_seq, int num_blocks,
                    int num_heads, int num_kv_heads, int head_dim, int block_size,
                    float scale, int io_dtype, int kv_dtype, float k_scale, float v_scale,
-                   int max_context_len, int partition_size,
+                   int max_context_len, int partition_size, int num_workgroups,
                    void* workspace, size_t workspace_bytes, void* out,
                    void* k_rows, void* v_rows, int32_t* read_counts, void* stream);
 

@@ -30,7 +30,9 @@ SIGNATURES = {
     "pa_decode": (_I, _DECODE_ARGS + [_P, _P]),
     "pa_partitioned_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "pa_decode_partitioned": (_I, _DECODE_ARGS + [_I, _I, _P, _SZ, _P, _P]),
-    "pa_debug_trace": (_I, _DECODE_ARGS + [_I, _I, _P, _SZ, _P, _P, _P, _P, _P]),
+    "pa_balanced_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "pa_decode_balanced": (_I, _DECODE_ARGS + [_I, _P, _SZ, _P, _P]),
+    "pa_debug_trace": (_I, _DECODE_ARGS + [_I, _I, _I, _P, _SZ, _P, _P, _P, _P, _P]),
     "pa_check_tables": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "pa_debug_fp8_to_f32": (_I, [_P, _P, _I, _P]),
     "pa_status_str": (ctypes.c_char_p, [_I]),
@@ -74,6 +76,12 @@ def pa_partitioned_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int,
                                    max_context_len: int, partition_size: int = 0) -> int:
     return int(lib().pa_partitioned_workspace_bytes(num_seqs, num_heads, head_dim,
                                                     max_context_len, partition_size))
+
+
+def pa_balanced_workspace_bytes(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                                num_workgroups: int = 0) -> int:
+    return int(lib().pa_balanced_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                 num_workgroups))
 
 
 # ----------------------------------------------------------------------------------
@@ -180,16 +188,44 @@ def pa_decode_partitioned(q, k_pool, v_pool, block_tables, context_lens, max_con
     return out
 
 
+def balanced_workspace(q, k_pool, num_workgroups: int = 0):
+    """Zero-filled workspace for pa_decode_balanced (the counters must start at zero;
+    every completed call leaves them zero, so one workspace serves a whole decode loop)."""
+    torch = _torch()
+    S, H, D = q.shape
+    Hkv = k_pool.shape[1]
+    need = pa_balanced_workspace_bytes(S, H, Hkv, D, num_workgroups)
+    return torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
+
+
+def pa_decode_balanced(q, k_pool, v_pool, block_tables, context_lens, scale: Optional[float] = None,
+                       num_workgroups: int = 0, workspace=None, k_scale: float = 1.0,
+                       v_scale: float = 1.0, out=None, stream=None):
+    """Work-balanced paged decode (one launch, any length mix); returns out."""
+    args, out, _ = _common(q, k_pool, v_pool, block_tables, context_lens, scale, k_scale, v_scale, out)
+    if workspace is None:
+        workspace = balanced_workspace(q, k_pool, num_workgroups)
+    _check_dev("workspace", workspace)
+    nbytes = workspace.numel() * workspace.element_size()
+    _raise("pa_decode_balanced",
+           lib().pa_decode_balanced(*args, int(num_workgroups), workspace.data_ptr(), nbytes,
+                                    out.data_ptr(), _stream(stream)))
+    return out
+
+
 def pa_debug_trace(q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
-                   scale: Optional[float] = None, partition_size: int = 0, k_scale: float = 1.0,
-                   v_scale: float = 1.0, stream=None):
+                   scale: Optional[float] = None, partition_size: int = 0, num_workgroups: int = 0,
+                   k_scale: float = 1.0, v_scale: float = 1.0, stream=None):
     """Instrumented decode; returns (out, k_rows, v_rows, read_counts)."""
     torch = _torch()
     args, out, (S, H, D, NB, Hkv, BS, MB) = _common(q, k_pool, v_pool, block_tables, context_lens,
                                                    scale, k_scale, v_scale, None)
     workspace = None
     nbytes = 0
-    if partition_size:
+    if num_workgroups:
+        workspace = balanced_workspace(q, k_pool, num_workgroups)
+        nbytes = workspace.numel()
+    elif partition_size:
         need = pa_partitioned_workspace_bytes(S, H, D, int(max_context_len), int(partition_size))
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
         nbytes = need
@@ -197,7 +233,7 @@ def pa_debug_trace(q, k_pool, v_pool, block_tables, context_lens, max_context_le
     v_rows = torch.zeros_like(k_rows)
     counts = torch.zeros((S, Hkv, max_context_len), dtype=torch.int32, device=q.device)
     _raise("pa_debug_trace",
-           lib().pa_debug_trace(*args, int(max_context_len), int(partition_size),
+           lib().pa_debug_trace(*args, int(max_context_len), int(partition_size), int(num_workgroups),
                                 workspace.data_ptr() if workspace is not None else None, nbytes,
                                 out.data_ptr(), k_rows.data_ptr(), v_rows.data_ptr(),
                                 counts.data_ptr(), _stream(stream)))
@@ -213,7 +249,7 @@ class DecodePlan:
     def __init__(self, q, k_pool, v_pool, block_tables, context_lens, scale=None,
                  k_scale: float = 1.0, v_scale: float = 1.0, out=None,
                  max_context_len: Optional[int] = None, partition_size: int = 0,
-                 workspace=None, stream=None):
+                 workspace=None, stream=None, balanced: bool = False, num_workgroups: int = 0):
         torch = _torch()
         args, out, (S, H, D, *_r) = _common(q, k_pool, v_pool, block_tables, context_lens,
                                             scale, k_scale, v_scale, out)
@@ -221,7 +257,15 @@ class DecodePlan:
         self._kmeta = (tuple(k_pool.shape), k_pool.dtype, k_pool.device)
         self._keep = [q, k_pool, v_pool, block_tables, context_lens, out]
         st = _stream(stream)
-        if max_context_len is None:
+        if balanced:
+            if workspace is None:
+                workspace = balanced_workspace(q, k_pool, num_workgroups)
+            _check_dev("workspace", workspace)
+            self._keep.append(workspace)
+            self._fn = lib().pa_decode_balanced
+            tail = [int(num_workgroups), workspace.data_ptr(),
+                    workspace.numel() * workspace.element_size(), out.data_ptr(), st]
+        elif max_context_len is None:
             self._fn = lib().pa_decode
             tail = [out.data_ptr(), st]
         else:

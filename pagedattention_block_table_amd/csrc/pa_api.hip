@@ -8,6 +8,7 @@
 //   [P3] "内存优化：KV Cache管理、PagedAttention原理与内存池配置" (decode over all cached K/V)
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -220,9 +221,59 @@ int64_t num_parts_for(int max_context_len, int P) {
   return n < 1 ? 1 : n;
 }
 
-// Shared body of the partitioned and debug entry points. P == 0 selects single-pass mode.
-int run(const Common& c, int max_context_len, int P, void* workspace, size_t ws_bytes,
-        void* dk, void* dv, int32_t* dcounts, bool debug, hipStream_t st) {
+// Workgroups the balanced scheduler uses by default: two per compute unit of the current
+// device (queried once per device, thread-safe through the static local).
+int default_balanced_workgroups() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 512;
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];  // zero-initialised; 0 = not yet queried
+  if (dev >= 0 && dev < kMaxDev) {
+    const int known = cache[dev].load(std::memory_order_relaxed);
+    if (known > 0) return known;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const int n = 2 * cus;
+  if (dev >= 0 && dev < kMaxDev) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// The balanced scheduler covers the MFMA shapes: 1, 2 or 4 query heads per KV head,
+// io f16 / bf16, KV = io or fp8, 128 or 256 bytes per token row, at most
+// kMaxBalancedSeqs sequences.
+bool balanced_shape(const Common& c) {
+  const int g = c.H / c.Hkv;
+  if (g != 1 && g != 2 && g != 4) return false;
+  if (c.io != PA_F16 && c.io != PA_BF16) return false;
+  if (c.kv != c.io && c.kv != PA_FP8_E4M3) return false;
+  const int row = c.D * elem_bytes(c.kv);
+  if (row != 128 && row != 256) return false;
+  return c.S <= kMaxBalancedSeqs;
+}
+
+struct BalancedLayout {
+  size_t counter_bytes;  // int32 per (KV head, sequence), padded to 256 bytes
+  size_t slot_bytes;     // fp32 m[G], l[G], o[G][D], two slots per workgroup
+  size_t total;
+};
+
+BalancedLayout balanced_layout(int S, int H, int Hkv, int D, int nwg) {
+  BalancedLayout b{};
+  const int64_t G = H / Hkv;
+  b.counter_bytes = (size_t)((((int64_t)Hkv * S * 4) + 255) / 256 * 256);
+  b.slot_bytes = (size_t)((int64_t)nwg * 2 * G * (D + 2) * 4);
+  b.total = b.counter_bytes + b.slot_bytes;
+  return b;
+}
+
+enum class Mode { kSingle, kPartitioned, kBalanced };
+
+// Shared body of every entry point. P is the partition size (partitioned mode), nwg the
+// workgroup count (balanced mode).
+int run(const Common& c, Mode mode, int max_context_len, int P, int nwg, void* workspace,
+        size_t ws_bytes, void* dk, void* dv, int32_t* dcounts, bool debug, hipStream_t st) {
   int rc = validate(c);
   if (rc != PA_OK) return rc;
   LaunchSpec ls{};
@@ -233,8 +284,9 @@ int run(const Common& c, int max_context_len, int P, void* workspace, size_t ws_
   ls.debug = debug;
   ls.stream = st;
   const int cap = c.MB * c.BS;  // a table row covers at most this many tokens
+  if (mode == Mode::kBalanced && !balanced_shape(c)) mode = Mode::kSingle;  // same result
   int64_t NP = 1;
-  if (P > 0) {
+  if (mode == Mode::kPartitioned) {
     if (max_context_len < 0) return PA_ERR_INVALID;
     if (P % c.BS != 0) return PA_ERR_INVALID;
     NP = num_parts_for(max_context_len, P);
@@ -246,7 +298,7 @@ int run(const Common& c, int max_context_len, int P, void* workspace, size_t ws_
     ls.args.max_ctx = max_context_len < cap ? max_context_len : cap;
   } else {
     ls.args.max_ctx = cap;
-    if (debug && max_context_len >= 0 && max_context_len < cap) ls.args.max_ctx = max_context_len;
+    if (max_context_len >= 0 && max_context_len < cap) ls.args.max_ctx = max_context_len;
     ls.args.part_tokens = ls.args.max_ctx > 0 ? ls.args.max_ctx : 1;
   }
   ls.args.num_parts = (int)NP;
@@ -259,6 +311,19 @@ int run(const Common& c, int max_context_len, int P, void* workspace, size_t ws_
     ls.args.dbg_counts = dcounts;
     ls.args.dbg_max_ctx = max_context_len;
     if (ls.args.max_ctx > max_context_len) ls.args.max_ctx = max_context_len;
+  }
+  if (mode == Mode::kBalanced) {
+    if (nwg < 0) return PA_ERR_INVALID;
+    if (nwg == 0) nwg = default_balanced_workgroups();
+    const BalancedLayout lay = balanced_layout(c.S, c.H, c.Hkv, c.D, nwg);
+    if (!workspace || ws_bytes < lay.total) return PA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PA_ERR_INVALID;
+    ls.args.counters = (int32_t*)workspace;
+    ls.args.ws = (float*)((char*)workspace + lay.counter_bytes);
+    ls.args.nwg = nwg;
+    ls.balanced = true;
+    ls.grid = nwg;
+    return launch_pair(c.io, c.kv, ls);
   }
   const int64_t grid = (int64_t)c.Hkv * c.S * NP;
   if (grid > INT_MAX) return PA_ERR_INVALID;
@@ -291,7 +356,8 @@ int pa_decode(const void* q, const void* k_pool, const void* v_pool, const int32
     pa::Common c{q, k_pool, v_pool, block_tables, context_lens, num_seqs, max_blocks_per_seq,
                  num_blocks, num_heads, num_kv_heads, head_dim, block_size, scale, io_dtype,
                  kv_dtype, k_scale, v_scale, out};
-    return pa::run(c, -1, 0, nullptr, 0, nullptr, nullptr, nullptr, false, (hipStream_t)stream);
+    return pa::run(c, pa::Mode::kSingle, -1, 0, 0, nullptr, 0, nullptr, nullptr, nullptr, false,
+                   (hipStream_t)stream);
   } catch (...) {
     return PA_ERR_LAUNCH;
   }
@@ -319,8 +385,39 @@ int pa_decode_partitioned(const void* q, const void* k_pool, const void* v_pool,
     pa::Common c{q, k_pool, v_pool, block_tables, context_lens, num_seqs, max_blocks_per_seq,
                  num_blocks, num_heads, num_kv_heads, head_dim, block_size, scale, io_dtype,
                  kv_dtype, k_scale, v_scale, out};
-    return pa::run(c, max_context_len, P, workspace, workspace_bytes, nullptr, nullptr, nullptr,
-                   false, (hipStream_t)stream);
+    return pa::run(c, pa::Mode::kPartitioned, max_context_len, P, 0, workspace, workspace_bytes,
+                   nullptr, nullptr, nullptr, false, (hipStream_t)stream);
+  } catch (...) {
+    return PA_ERR_LAUNCH;
+  }
+}
+
+size_t pa_balanced_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                   int num_workgroups) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_workgroups < 0 ||
+      num_heads % num_kv_heads != 0)
+    return 0;
+  try {
+    const int nwg = num_workgroups == 0 ? pa::default_balanced_workgroups() : num_workgroups;
+    return pa::balanced_layout(num_seqs, num_heads, num_kv_heads, head_dim, nwg).total;
+  } catch (...) {
+    return 0;
+  }
+}
+
+int pa_decode_balanced(const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                       int max_blocks_per_seq, int num_blocks, int num_heads, int num_kv_heads,
+                       int head_dim, int block_size, float scale, int io_dtype, int kv_dtype,
+                       float k_scale, float v_scale, int num_workgroups, void* workspace,
+                       size_t workspace_bytes, void* out, void* stream) {
+  try {
+    if (num_workgroups < 0) return PA_ERR_INVALID;
+    pa::Common c{q, k_pool, v_pool, block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                 num_blocks, num_heads, num_kv_heads, head_dim, block_size, scale, io_dtype,
+                 kv_dtype, k_scale, v_scale, out};
+    return pa::run(c, pa::Mode::kBalanced, -1, 0, num_workgroups, workspace, workspace_bytes,
+                   nullptr, nullptr, nullptr, false, (hipStream_t)stream);
   } catch (...) {
     return PA_ERR_LAUNCH;
   }
@@ -331,15 +428,19 @@ int pa_debug_trace(const void* q, const void* k_pool, const void* v_pool,
                    int max_blocks_per_seq, int num_blocks, int num_heads, int num_kv_heads,
                    int head_dim, int block_size, float scale, int io_dtype, int kv_dtype,
                    float k_scale, float v_scale, int max_context_len, int partition_size,
-                   void* workspace, size_t workspace_bytes, void* out, void* k_rows, void* v_rows,
-                   int32_t* read_counts, void* stream) {
+                   int num_workgroups, void* workspace, size_t workspace_bytes, void* out,
+                   void* k_rows, void* v_rows, int32_t* read_counts, void* stream) {
   try {
-    if (partition_size < 0) return PA_ERR_INVALID;
+    if (partition_size < 0 || num_workgroups < 0) return PA_ERR_INVALID;
+    if (partition_size > 0 && num_workgroups > 0) return PA_ERR_INVALID;
     pa::Common c{q, k_pool, v_pool, block_tables, context_lens, num_seqs, max_blocks_per_seq,
                  num_blocks, num_heads, num_kv_heads, head_dim, block_size, scale, io_dtype,
                  kv_dtype, k_scale, v_scale, out};
-    return pa::run(c, max_context_len, partition_size, workspace, workspace_bytes, k_rows, v_rows,
-                   read_counts, true, (hipStream_t)stream);
+    const pa::Mode mode = num_workgroups > 0 ? pa::Mode::kBalanced
+                          : partition_size > 0 ? pa::Mode::kPartitioned
+                                               : pa::Mode::kSingle;
+    return pa::run(c, mode, max_context_len, partition_size, num_workgroups, workspace,
+                   workspace_bytes, k_rows, v_rows, read_counts, true, (hipStream_t)stream);
   } catch (...) {
     return PA_ERR_LAUNCH;
   }
@@ -378,6 +479,6 @@ const char* pa_status_str(int status) {
   }
 }
 
-int pa_version(void) { return 100; }
+int pa_version(void) { return 200; }
 
 }  // extern "C"

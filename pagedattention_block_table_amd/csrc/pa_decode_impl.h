@@ -74,6 +74,8 @@ struct DecodeArgs {
   int num_parts;         // partitions per (s, g) in the grid
   int max_ctx;           // context lengths are clamped to [0, max_ctx]
   int dbg_max_ctx;
+  int32_t* counters;     // balanced mode: arrivals per (KV head, sequence); zero between calls
+  int nwg;               // balanced mode: workgroups sharing the chunks
   float q_mul;           // scale * log2(e) (* k_scale for fp8)
   float out_mul;         // v_scale for fp8, else 1
 };
@@ -256,10 +258,14 @@ template <int G, int VEC> struct RowState {
 #define PA_NT_LOADS 0
 #endif
 
-// 16-byte K/V load; streamed data is read once per unit.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte K/V load. Streamed data is read once per (sequence, KV head), so the loads are
+// marked non-temporal.
 __device__ __forceinline__ uint4 load16(const char* p) {
 #if PA_NT_LOADS
-  return __builtin_nontemporal_load((const uint4*)p);
+  const u32x4_t r = __builtin_nontemporal_load((const u32x4_t*)p);
+  return make_uint4(r.x, r.y, r.z, r.w);
 #else
   return *(const uint4*)p;
 #endif
@@ -504,6 +510,12 @@ decode_kernel(const DecodeArgs a) {
   }
 }
 
+}  // namespace pa
+
+#include "pa_mfma_decode.h"
+
+namespace pa {
+
 // Per-(io, kv) launcher; defined in one translation unit per dtype pair.
 struct LaunchSpec {
   DecodeArgs args;
@@ -511,10 +523,14 @@ struct LaunchSpec {
   int block_size;
   int group;
   bool debug;
+  bool balanced;   // balanced_decode_kernel (MFMA shapes only)
   int grid;
   hipStream_t stream;
 };
 
+#ifndef PA_MFMA
+#define PA_MFMA 1
+#endif
 #ifndef PA_WAVES
 #define PA_WAVES 4
 #endif
@@ -535,6 +551,30 @@ int launch_one(const LaunchSpec& ls) {
   } else {
     constexpr int NW = PA_WAVES;
     constexpr int U = pick_unroll<IO, KV, D, BS, G>();
+    if (ls.balanced) {
+      if constexpr (mfma_supported<IO, KV, D, G>()) {
+        if (ls.debug) {
+          hipLaunchKernelGGL((balanced_decode_kernel<IO, KV, D, BS, G, NW, true>), dim3(ls.grid),
+                             dim3(NW * 64), 0, ls.stream, ls.args);
+        } else {
+          hipLaunchKernelGGL((balanced_decode_kernel<IO, KV, D, BS, G, NW, false>), dim3(ls.grid),
+                             dim3(NW * 64), 0, ls.stream, ls.args);
+        }
+        return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+      } else {
+        return PA_ERR_UNSUPPORTED;
+      }
+    }
+    if constexpr (PA_MFMA && mfma_supported<IO, KV, D, G>()) {
+      if (ls.debug) {
+        hipLaunchKernelGGL((mfma_decode_kernel<IO, KV, D, BS, G, NW, true>), dim3(ls.grid),
+                           dim3(NW * 64), 0, ls.stream, ls.args);
+      } else {
+        hipLaunchKernelGGL((mfma_decode_kernel<IO, KV, D, BS, G, NW, false>), dim3(ls.grid),
+                           dim3(NW * 64), 0, ls.stream, ls.args);
+      }
+      return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+    }
     if (ls.debug) {
       hipLaunchKernelGGL((decode_kernel<IO, KV, D, BS, G, NW, U, true>), dim3(ls.grid), dim3(NW * 64),
                          0, ls.stream, ls.args);

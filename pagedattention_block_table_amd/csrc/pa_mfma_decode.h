@@ -1,0 +1,704 @@
+// Decode kernels for gfx950 with the score product on the matrix cores.
+//
+// Same computation as decode_kernel (pages cited there): for a KV head g and the G query
+// heads that share it (G = 1, 2 or 4), scores z = scale * q.K^T over the cached tokens,
+// online softmax, and the softmax-weighted sum of V rows, in fp32. The score product
+// [G x D] x [D x tokens] runs as v_mfma_f32_16x16x32_{f16,bf16}; the V product runs on
+// the vector ALUs.
+//
+// MFMA operand layout (16x16x32, wave64): lane l supplies row l%16 of A and column
+// l%16 of B, each as the 8 consecutive k values 8*(l/16) .. 8*(l/16)+7; lane l receives
+// D[4*(l/16) + r][l%16] in result register r. Here A = the query heads (row m holds
+// head m % G, so the G heads repeat down the 16 rows), B = K^T (column n = token n of a
+// 16-token tile) and k runs over head_dim. The k order inside the product is free, so
+// each lane feeds the MFMA straight from its own 16-byte K loads: lane (n = l%16,
+// lg = l/16) loads the 16-byte chunks 4i + lg of token n's row. Result register r of
+// every lane then holds the score of head r % G for token n.
+//
+// V product: lane (n, lg) with half h = n/8 loads, for token n and its partner n^8, the
+// chunks 4*(VPL*h + k) + lg (k < VPL = chunks-per-lane / 2), so each V row of the tile
+// is read exactly once per wave. The partner's probabilities come from lane n^8 with
+// one DPP rotate. Each lane accumulates G heads x VPL chunks; at the end the 8 lanes of
+// a half-row that hold the same columns are summed with DPP.
+//
+// Softmax: the running max of each head is uniform over the wave. It is only raised
+// when a chunk's max exceeds it by more than kLazyRescale (log2 units); in between the
+// probabilities exp2(z - m) stay <= 2^kLazyRescale, and the final normalisation by the
+// running sum makes the result independent of which m was used.
+//
+// Work is cut into chunks of CT = 16 * NT tokens (NT tiles). Chunks are dealt round
+// robin to the waves of a workgroup, so the order of arithmetic depends only on logical
+// token positions: results are bitwise identical under any block size, physical
+// placement or sharing. Each wave fetches the table entries of its chunks ahead, 64 at a
+// time, and keeps the next chunk's K/V loads in flight while it computes the current one.
+//
+// Two schedulers use the same chunk engine:
+//   mfma_decode_kernel      one workgroup per (KV head, sequence, partition);
+//   balanced_decode_kernel  a fixed grid of workgroups splits the total chunk count of
+//                           the batch evenly; a (KV head, sequence) whose chunks span
+//                           several workgroups is merged by the last one to finish it.
+#pragma once
+
+namespace pa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// log2-unit headroom of the lazy running-max update (probabilities stay <= 2^8)
+constexpr float kLazyRescale = 8.0f;
+
+#ifndef PA_STAGGER
+#define PA_STAGGER 1
+#endif
+#ifndef PA_MFMA_TILES
+#define PA_MFMA_TILES 1
+#endif
+
+// Largest batch the balanced scheduler takes (its chunk prefix sums live in LDS).
+constexpr int kMaxBalancedSeqs = 4096;
+
+template <int MT> struct Mma;
+template <> struct Mma<kF16> {
+  typedef f16x8_t vec;
+  static __device__ __forceinline__ f32x4_t mma(const vec& a, const vec& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  // two fp32 values that are exactly representable -> packed pair (exact)
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+};
+template <> struct Mma<kBF16> {
+  typedef bf16x8_t vec;
+  static __device__ __forceinline__ f32x4_t mma(const vec& a, const vec& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // fp32 values with at most 8 significant bits: the upper halves are the bf16 codes
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo),
+                                 0x07060302u);
+  }
+};
+
+// Eight e4m3 codes (two dwords) -> eight MFMA operands of type MT, exactly: every e4m3
+// value has at most 4 significant bits and fits both f16 and bf16.
+template <int MT>
+__device__ __forceinline__ typename Mma<MT>::vec fp8x8_operand(uint32_t w0, uint32_t w1) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
+  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+  uint4 r;
+  r.x = Mma<MT>::pack2(a.x, a.y);
+  r.y = Mma<MT>::pack2(b.x, b.y);
+  r.z = Mma<MT>::pack2(c.x, c.y);
+  r.w = Mma<MT>::pack2(d.x, d.y);
+  return __builtin_bit_cast(typename Mma<MT>::vec, r);
+}
+
+template <int MT, int KV>
+__device__ __forceinline__ typename Mma<MT>::vec k_operand(const uint4& r, int half) {
+  if constexpr (KV == kFP8) {
+    return half == 0 ? fp8x8_operand<MT>(r.x, r.y) : fp8x8_operand<MT>(r.z, r.w);
+  } else {
+    return __builtin_bit_cast(typename Mma<MT>::vec, r);
+  }
+}
+
+template <int KV, int D>
+struct MfmaGeo {
+  static constexpr int E = ElemBytes<KV>::value;
+  static constexpr int VEC = 16 / E;         // values per 16-byte chunk
+  static constexpr int RB = D * E;           // bytes of one token row
+  static constexpr int CPR = RB / 16;        // chunks per row
+  static constexpr int CPL = CPR / 4;        // K chunks per lane per row
+  static constexpr int VPL = CPL / 2;        // V chunks per lane per token (two tokens)
+  static constexpr int NST = D / 32;         // MFMA steps over head_dim
+  static constexpr bool ok = (KV != kF32) && (CPR % 4 == 0) && (CPL >= 2) && (CPL % 2 == 0);
+};
+
+// Shapes the MFMA kernels take: 1, 2 or 4 query heads per KV head, io f16/bf16, KV = io
+// or fp8, and at least 128 bytes per token row.
+template <int IO, int KV, int D, int G>
+constexpr bool mfma_supported() {
+  return (G == 1 || G == 2 || G == 4) && (IO == kF16 || IO == kBF16) && (KV == IO || KV == kFP8) &&
+         MfmaGeo<KV, D>::ok;
+}
+
+// Order in which a wave visits the `len` chunks of a segment: from a per-sequence
+// rotation, so that workgroups that share prefix blocks do not all start on the same
+// block at the same time.
+__device__ __forceinline__ int rotated(int idx, int rot, int len) {
+  const int c = idx + rot;
+  return c >= len ? c - len : c;
+}
+
+// K/V registers of one chunk in flight: K rows of the own token of each tile, V rows of
+// the own token and of its partner n^8.
+template <int KV, int D, int NT>
+struct ChunkBuf {
+  using Geo = MfmaGeo<KV, D>;
+  uint4 kr[NT][Geo::CPL];
+  uint4 vo[NT][Geo::VPL];
+  uint4 vp[NT][Geo::VPL];
+};
+
+// Per-wave state and chunk processing for one (sequence s, KV head g) at a time.
+//
+// A wave takes the chunks k0 + rotated(wave + k*NW, rot, len), k = 0, 1, ... of a
+// segment. Their block-table entries are fetched ahead by one vector load per 64 chunks
+// (lane l holds the entries of the wave's chunk 64*w + l; the next window is loaded while
+// the current one is used), and the K/V loads of chunk k+1 are in flight while chunk k is
+// computed, so a wave never waits on a table entry and always has a chunk outstanding.
+template <int IO, int KV, int D, int BS, int G, int NT, bool DBG>
+struct MfmaEngine {
+  using Geo = MfmaGeo<KV, D>;
+  static constexpr int VEC = Geo::VEC, RB = Geo::RB, CPL = Geo::CPL, VPL = Geo::VPL,
+                       NST = Geo::NST;
+  static constexpr int CT = 16 * NT;                 // tokens per chunk
+  static constexpr int NBC = CT >= BS ? CT / BS : 1; // blocks per chunk
+  static constexpr int TILE_BYTES = BS * RB;
+  using M = Mma<IO>;
+  using vec = typename M::vec;
+  using Buf = ChunkBuf<KV, D, NT>;
+  static_assert(mfma_supported<IO, KV, D, G>(), "unsupported MFMA decode geometry");
+  static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+  static_assert(CT % BS == 0 || BS % CT == 0, "chunks and blocks nest");
+
+  int lane, n, lg, hh;
+  int s, g, t_end, j_end;
+  int base, k0, len, rot, wave, nw;
+  const int32_t* bt;
+  const char* kbase;
+  const char* vbase;
+  int64_t blk_stride;
+  int win[2][NBC];  // block ids of this wave's chunks, windows w and w + 1
+  vec qa[NST];
+  float m_run[G], l_run[G];
+  float acc[G][VPL][VEC];
+
+  __device__ __forceinline__ explicit MfmaEngine(int lane_) {
+    lane = lane_;
+    n = lane & 15;
+    lg = lane >> 4;
+    hh = n >> 3;
+  }
+
+  // first token of this wave's k-th chunk
+  __device__ __forceinline__ int chunk_token(int k) const {
+    return base + CT * (k0 + rotated(wave + k * nw, rot, len));
+  }
+
+  // table entries of this wave's chunks 64*w .. 64*w+63 (lane l: chunk 64*w + l)
+  __device__ __forceinline__ void load_window(const DecodeArgs& a, int w, int (&dst)[NBC]) {
+    const int k = 64 * w + lane;
+    const bool live = wave + k * nw < len;
+    const int j = live ? chunk_token(k) / BS : 0;
+#pragma unroll
+    for (int u = 0; u < NBC; ++u) {
+      int b = 0;
+      if (live && j + u < j_end) b = bt[j + u];
+      // contract: 0 <= b < num_blocks; clamp so that a bad table never reads outside the pool
+      dst[u] = min(max(b, 0), a.num_blocks - 1);
+    }
+  }
+
+  // Start (sequence s_, KV head g_) whose valid tokens end at t_end_, for this wave's
+  // chunks of the segment of chunks k0_ .. k0_ + len_ - 1 counted from token base_ (a
+  // multiple of the block size): load the query operands and the first table windows,
+  // and clear the softmax state.
+  __device__ __forceinline__ void begin(const DecodeArgs& a, int s_, int g_, int t_end_, int base_,
+                                        int k0_, int len_, int rot_, int wave_, int nw_) {
+    s = s_;
+    g = g_;
+    t_end = t_end_;
+    j_end = (t_end + BS - 1) / BS;
+    base = base_;
+    k0 = k0_;
+    len = len_;
+    rot = rot_;
+    wave = wave_;
+    nw = nw_;
+    bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    blk_stride = (int64_t)a.num_kv_heads * TILE_BYTES;
+    kbase = (const char*)a.k_pool + (int64_t)g * TILE_BYTES;
+    vbase = (const char*)a.v_pool + (int64_t)g * TILE_BYTES;
+    load_window(a, 0, win[0]);
+    load_window(a, 1, win[1]);
+    // row n of A is head g*G + n%G; k index (lg, e) <-> column VEC*(4i+lg)+e
+    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)s * a.num_heads + g * G + (n % G)) * D;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int col = VEC * (4 * i + lg);
+#pragma unroll
+      for (int hf = 0; hf < VEC / 8; ++hf) {
+        const uint4 w = *(const uint4*)(qrow + col + 8 * hf);
+        qa[i * (VEC / 8) + hf] = __builtin_bit_cast(vec, w);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      m_run[r] = -3.0e38f;
+      l_run[r] = 0.f;
+#pragma unroll
+      for (int k = 0; k < VPL; ++k)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[r][k][e] = 0.f;
+    }
+  }
+
+  // Issue the K/V loads of this wave's k-th chunk (chunks are issued in order k = 0, 1, ...).
+  __device__ __forceinline__ void issue(const DecodeArgs& a, Buf& b, int k) {
+    if ((k & 63) == 0 && k > 0) {
+      // entering window k/64: it was loaded 64 chunks ago; fetch the one after it
+#pragma unroll
+      for (int u = 0; u < NBC; ++u) win[0][u] = win[1][u];
+      load_window(a, (k >> 6) + 1, win[1]);
+    }
+    const int c0 = chunk_token(k);
+    int64_t off[NBC];
+#pragma unroll
+    for (int u = 0; u < NBC; ++u)
+      off[u] = (int64_t)__builtin_amdgcn_readlane(win[0][u], k & 63) * blk_stride;
+    const int jb = c0 / BS;  // first block of the chunk
+    const bool tail = c0 + CT > t_end;
+#pragma unroll
+    for (int tau = 0; tau < NT; ++tau) {
+      const int to = c0 + 16 * tau + n;          // own token
+      const int tp = c0 + 16 * tau + (n ^ 8);    // partner token
+      const int uo = NBC > 1 ? to / BS - jb : 0;
+      const int up = NBC > 1 ? tp / BS - jb : 0;
+      int64_t bo = off[0], bp = off[0];
+#pragma unroll
+      for (int u = 1; u < NBC; ++u) {
+        bo = uo == u ? off[u] : bo;
+        bp = up == u ? off[u] : bp;
+      }
+      const char* krow = kbase + bo + (to % BS) * RB;
+      const char* vrow_o = vbase + bo + (to % BS) * RB;
+      const char* vrow_p = vbase + bp + (tp % BS) * RB;
+      if (!tail) {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) b.kr[tau][i] = load16(krow + 16 * (4 * i + lg));
+#pragma unroll
+        for (int q = 0; q < VPL; ++q) {
+          const int vc = 4 * (VPL * hh + q) + lg;
+          b.vo[tau][q] = load16(vrow_o + 16 * vc);
+          b.vp[tau][q] = load16(vrow_p + 16 * vc);
+        }
+      } else {
+        const bool ok_o = to < t_end;
+        const bool ok_p = tp < t_end;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+          b.kr[tau][i] = ok_o ? load16(krow + 16 * (4 * i + lg)) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < VPL; ++q) {
+          const int vc = 4 * (VPL * hh + q) + lg;
+          b.vo[tau][q] = ok_o ? load16(vrow_o + 16 * vc) : make_uint4(0, 0, 0, 0);
+          b.vp[tau][q] = ok_p ? load16(vrow_p + 16 * vc) : make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // Scores, online softmax and V accumulation of this wave's k-th chunk, loaded in b.
+  __device__ __forceinline__ void consume(const DecodeArgs& a, const Buf& b, int k) {
+    const int c0 = chunk_token(k);
+    if constexpr (DBG) {
+      const int Hkv = a.num_kv_heads;
+#pragma unroll
+      for (int tau = 0; tau < NT; ++tau) {
+        const int to = c0 + 16 * tau + n;
+        const int tp = c0 + 16 * tau + (n ^ 8);
+        const int64_t ro = ((int64_t)s * Hkv + g) * a.dbg_max_ctx + to;
+        const int64_t rp = ((int64_t)s * Hkv + g) * a.dbg_max_ctx + tp;
+        if (to < t_end) {
+#pragma unroll
+          for (int i = 0; i < CPL; ++i)
+            *(uint4*)((char*)a.dbg_k + ro * RB + 16 * (4 * i + lg)) = b.kr[tau][i];
+#pragma unroll
+          for (int q = 0; q < VPL; ++q)
+            *(uint4*)((char*)a.dbg_v + ro * RB + 16 * (4 * (VPL * hh + q) + lg)) = b.vo[tau][q];
+          if (lg == 0) atomicAdd(a.dbg_counts + ro, 1);
+        }
+        if (tp < t_end) {
+#pragma unroll
+          for (int q = 0; q < VPL; ++q)
+            *(uint4*)((char*)a.dbg_v + rp * RB + 16 * (4 * (VPL * hh + q) + lg)) = b.vp[tau][q];
+        }
+      }
+    }
+
+    // scores of the G heads for the own token of each tile (log2 units)
+    float z[NT][G];
+#pragma unroll
+    for (int tau = 0; tau < NT; ++tau) {
+      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < CPL; ++i)
+#pragma unroll
+        for (int hf = 0; hf < VEC / 8; ++hf)
+          c = M::mma(qa[i * (VEC / 8) + hf], k_operand<IO, KV>(b.kr[tau][i], hf), c);
+      const bool ok = c0 + 16 * tau + n < t_end;
+#pragma unroll
+      for (int r = 0; r < G; ++r) z[tau][r] = ok ? c[r] * a.q_mul : -INFINITY;
+    }
+
+    // chunk max per head (all four 16-lane rows hold the same values)
+    float mx[G];
+    bool raise = false;
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      float x = z[0][r];
+#pragma unroll
+      for (int tau = 1; tau < NT; ++tau) x = fmaxf(x, z[tau][r]);
+      x = fmaxf(x, dpp<0x128>(x));  // row_ror 8
+      x = fmaxf(x, dpp<0x124>(x));  // row_ror 4
+      x = fmaxf(x, dpp<0x122>(x));  // row_ror 2
+      x = fmaxf(x, dpp<0x121>(x));  // row_ror 1
+      // keep the running max wave-uniform (scalar) even if rows differ in the last bit
+      mx[r] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+      raise |= mx[r] > m_run[r] + kLazyRescale;
+    }
+    if (raise) {
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        const float mn = fmaxf(m_run[r], mx[r]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[r] - mn);
+        m_run[r] = mn;
+        l_run[r] *= alpha;
+#pragma unroll
+        for (int q = 0; q < VPL; ++q)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[r][q][e] *= alpha;
+      }
+    }
+
+#pragma unroll
+    for (int tau = 0; tau < NT; ++tau) {
+      float po[G], pp[G];
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        po[r] = __builtin_amdgcn_exp2f(z[tau][r] - m_run[r]);
+        l_run[r] += po[r];
+        pp[r] = dpp<0x128>(po[r]);  // lane n^8 holds the partner token
+      }
+#pragma unroll
+      for (int q = 0; q < VPL; ++q) {
+        float fo[VEC], fq[VEC];
+        widen16<KV>(b.vo[tau][q], fo);
+        widen16<KV>(b.vp[tau][q], fq);
+#pragma unroll
+        for (int r = 0; r < G; ++r)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            acc[r][q][e] = fmaf(po[r], fo[e], acc[r][q][e]);
+            acc[r][q][e] = fmaf(pp[r], fq[e], acc[r][q][e]);
+          }
+      }
+    }
+  }
+
+  // This wave's chunks of the segment, two in flight.
+  __device__ __forceinline__ void run(const DecodeArgs& a) {
+    const int nwc = wave < len ? (len - wave + nw - 1) / nw : 0;
+    Buf A, B;
+    if (nwc > 0) issue(a, A, 0);
+    if (nwc > 1) issue(a, B, 1);
+    for (int k = 0; k < nwc; k += 2) {
+      consume(a, A, k);
+      if (k + 2 < nwc) issue(a, A, k + 2);
+      if (k + 1 < nwc) {
+        consume(a, B, k + 1);
+        if (k + 3 < nwc) issue(a, B, k + 3);
+      }
+    }
+  }
+
+  // Reduce the wave's state (l over the 16 token lanes of a row, acc over the 8 lanes of
+  // a half-row) and store it as wave `wave` of the workgroup's LDS arrays.
+  template <int NW>
+  __device__ __forceinline__ void finish(float (&sm_m)[NW][G], float (&sm_l)[NW][G],
+                                         float (&sm_o)[NW][G][D]) {
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      l_run[r] = group_sum<16>(l_run[r]);
+#pragma unroll
+      for (int q = 0; q < VPL; ++q)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          float x = acc[r][q][e];
+          x += dpp<kRowHalfMirror>(x);
+          x += dpp<kQuadXor2>(x);
+          x += dpp<kQuadXor1>(x);
+          acc[r][q][e] = x;
+        }
+    }
+    if ((n & 7) == 0) {
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+#pragma unroll
+        for (int q = 0; q < VPL; ++q)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) sm_o[wave][r][VEC * (4 * (VPL * hh + q) + lg) + e] = acc[r][q][e];
+        if (lane == 0) {
+          sm_m[wave][r] = m_run[r];
+          sm_l[wave][r] = l_run[r];
+        }
+      }
+    }
+  }
+};
+
+// Merge of the NW wave states in LDS for element (head gi, column d): running max M,
+// sum of exp2(m - M) * l and of exp2(m - M) * o.
+template <int NW, int G, int D>
+__device__ __forceinline__ void merge_waves(const float (&sm_m)[NW][G], const float (&sm_l)[NW][G],
+                                            const float (&sm_o)[NW][G][D], int gi, int d, float& Mx,
+                                            float& lsum, float& o) {
+  Mx = sm_m[0][gi];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) Mx = fmaxf(Mx, sm_m[w][gi]);
+  o = 0.f;
+  lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const float f = __builtin_amdgcn_exp2f(sm_m[w][gi] - Mx);
+    o = fmaf(f, sm_o[w][gi][d], o);
+    lsum = fmaf(f, sm_l[w][gi], lsum);
+  }
+}
+
+template <int IO, int KV, int D, int BS, int G, int NW, bool DBG>
+__global__ void __launch_bounds__(NW * 64)
+mfma_decode_kernel(const DecodeArgs a) {
+  using Eng = MfmaEngine<IO, KV, D, BS, G, PA_MFMA_TILES, DBG>;
+  constexpr int CT = Eng::CT;
+
+  __shared__ float sm_m[NW][G];
+  __shared__ float sm_l[NW][G];
+  __shared__ float sm_o[NW][G][D];
+
+  const int unit = xcd_unit((int)blockIdx.x, (int)gridDim.x);
+  const int part = unit % a.num_parts;
+  const int sg = unit / a.num_parts;
+  const int s = sg % a.num_seqs;
+  const int g = sg / a.num_seqs;
+
+  int L = a.context_lens[s];
+  L = min(max(L, 0), a.max_ctx);
+  const int t_begin = part * a.part_tokens;
+  if (part > 0 && t_begin >= L) return;  // nothing in this partition (whole workgroup)
+  const int t_end = min(L, t_begin + a.part_tokens);
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  Eng eng(threadIdx.x & 63);
+  const int nch = (t_end - t_begin + CT - 1) / CT;
+  const int rot = PA_STAGGER ? (s * 5) % max(nch, 1) : 0;
+  eng.begin(a, s, g, t_end, t_begin, 0, nch, rot, wave, NW);
+  eng.run(a);
+  eng.template finish<NW>(sm_m, sm_l, sm_o);
+  __syncthreads();
+
+  // merge the waves and write
+  const int H = a.num_heads;
+  const int n_parts_s = (L + a.part_tokens - 1) / a.part_tokens;
+  const bool write_out = n_parts_s <= 1;
+  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
+    const int gi = idx / D;
+    const int d = idx % D;
+    float Mx, lsum, o;
+    merge_waves<NW, G, D>(sm_m, sm_l, sm_o, gi, d, Mx, lsum, o);
+    const int h = g * G + gi;
+    if (write_out) {
+      const float v = lsum > 0.f ? (o / lsum) * a.out_mul : 0.f;
+      store_io<IO>(a.out, ((int64_t)s * H + h) * D + d, v);
+    } else {
+      const int64_t NPH = (int64_t)a.num_seqs * H * a.num_parts;
+      const int64_t slot = ((int64_t)s * H + h) * a.num_parts + part;
+      a.ws[2 * NPH + slot * D + d] = o * a.out_mul;
+      if (d == 0) {
+        a.ws[slot] = Mx;
+        a.ws[NPH + slot] = lsum;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// balanced scheduler
+// ---------------------------------------------------------------------------------
+
+// First chunk of logical workgroup w when C chunks are shared by nwg workgroups.
+__device__ __forceinline__ int64_t chunk_begin(int64_t w, int64_t C, int64_t nwg) {
+  return w * C / nwg;
+}
+// Logical workgroup whose range holds chunk x (every range is non-empty when nwg <= C).
+__device__ __forceinline__ int64_t chunk_owner(int64_t x, int64_t C, int64_t nwg) {
+  return ((x + 1) * nwg - 1) / C;
+}
+
+// Floats per partial-state slot: m[G], l[G], o[G][D].
+template <int G, int D> constexpr int slot_floats() { return G * (D + 2); }
+
+template <int IO, int KV, int D, int BS, int G, int NW, bool DBG>
+__global__ void __launch_bounds__(NW * 64)
+balanced_decode_kernel(const DecodeArgs a) {
+  using Eng = MfmaEngine<IO, KV, D, BS, G, PA_MFMA_TILES, DBG>;
+  constexpr int CT = Eng::CT;
+  constexpr int NTH = NW * 64;
+  constexpr int SLOT = slot_floats<G, D>();
+
+  __shared__ float sm_m[NW][G];
+  __shared__ float sm_l[NW][G];
+  __shared__ float sm_o[NW][G][D];
+  __shared__ int sm_pref[kMaxBalancedSeqs + 1];  // exclusive prefix sums of chunk counts
+  __shared__ int sm_wsum[NW];
+  __shared__ int sm_last;
+
+  const int S = a.num_seqs;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+
+  // 1. chunks per sequence (at least one, so that empty sequences get their zero output
+  //    written) and their exclusive prefix sums, thread t owning a contiguous run of S/NTH
+  const int per = (S + NTH - 1) / NTH;
+  const int i0 = min(S, tid * per);
+  const int i1 = min(S, i0 + per);
+  int local = 0;
+  for (int i = i0; i < i1; ++i) {
+    const int L = min(max(a.context_lens[i], 0), a.max_ctx);
+    local += max(1, (L + CT - 1) / CT);
+  }
+  int incl = local;  // inclusive scan over the wave
+#pragma unroll
+  for (int k = 1; k < 64; k <<= 1) {
+    const int y = __shfl_up(incl, k);
+    if (lane >= k) incl += y;
+  }
+  if (lane == 63) sm_wsum[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += sm_wsum[w];
+  int run = base + incl - local;
+  for (int i = i0; i < i1; ++i) {
+    sm_pref[i] = run;
+    const int L = min(max(a.context_lens[i], 0), a.max_ctx);
+    run += max(1, (L + CT - 1) / CT);
+  }
+  if (tid == NTH - 1) {
+    int tot = 0;
+    for (int w = 0; w < NW; ++w) tot += sm_wsum[w];
+    sm_pref[S] = tot;
+  }
+  __syncthreads();
+
+  // 2. this workgroup's chunk range [cb, ce) of the C = Hkv * Cg chunks (KV-head major)
+  const int Cg = sm_pref[S];
+  const int64_t C = (int64_t)a.num_kv_heads * Cg;
+  const int64_t nwg = min((int64_t)a.nwg, C);
+  const int64_t v = xcd_unit((int)blockIdx.x, (int)gridDim.x);
+  if (v >= nwg) return;  // more workgroups than chunks (whole workgroup)
+  const int64_t cb = chunk_begin(v, C, nwg);
+  const int64_t ce = chunk_begin(v + 1, C, nwg);
+
+  Eng eng(lane);
+  const int H = a.num_heads;
+  int64_t c = cb;
+  bool first_seg = true;
+  while (c < ce) {
+    const int g = (int)(c / Cg);
+    const int r = (int)(c - (int64_t)g * Cg);
+    // sequence s with sm_pref[s] <= r < sm_pref[s + 1] (prefix sums strictly increase)
+    int lo = 0, hi = S;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (sm_pref[mid] <= r) lo = mid; else hi = mid;
+    }
+    const int s = lo;
+    const int nch = sm_pref[s + 1] - sm_pref[s];
+    const int k0 = r - sm_pref[s];
+    const int len = (int)min((int64_t)(nch - k0), ce - c);
+    const int k1 = k0 + len;
+    const int L = min(max(a.context_lens[s], 0), a.max_ctx);
+
+    const int rot = PA_STAGGER ? (s * 5) % len : 0;
+    eng.begin(a, s, g, L, 0, k0, len, rot, wave, NW);
+    eng.run(a);
+    eng.template finish<NW>(sm_m, sm_l, sm_o);
+    __syncthreads();
+
+    if (k0 == 0 && k1 == nch) {
+      // the whole (sequence, KV head) is here: normalise and write
+      for (int idx = tid; idx < G * D; idx += NTH) {
+        const int gi = idx / D;
+        const int d = idx % D;
+        float Mx, lsum, o;
+        merge_waves<NW, G, D>(sm_m, sm_l, sm_o, gi, d, Mx, lsum, o);
+        const float val = lsum > 0.f ? (o / lsum) * a.out_mul : 0.f;
+        store_io<IO>(a.out, ((int64_t)s * H + g * G + gi) * D + d, val);
+      }
+    } else {
+      // a piece: store (m, l, o) in this workgroup's slot (0 = its first segment, 1 = its
+      // last) with device-coherent stores, then count the arrival
+      float* slot = a.ws + ((int64_t)v * 2 + (first_seg ? 0 : 1)) * SLOT;
+      for (int idx = tid; idx < G * D; idx += NTH) {
+        const int gi = idx / D;
+        const int d = idx % D;
+        float Mx, lsum, o;
+        merge_waves<NW, G, D>(sm_m, sm_l, sm_o, gi, d, Mx, lsum, o);
+        __hip_atomic_store(slot + 2 * G + gi * D + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0) {
+          __hip_atomic_store(slot + gi, Mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(slot + G + gi, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      // every store of this workgroup has completed before the arrival is counted
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      const int64_t ub = (int64_t)g * Cg + sm_pref[s];  // first chunk of this (s, g)
+      const int64_t w0 = chunk_owner(ub, C, nwg);
+      const int64_t w1 = chunk_owner(ub + nch - 1, C, nwg);
+      int32_t* counter = a.counters + (int64_t)g * S + s;
+      if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm_last = old == (int)(w1 - w0);
+      }
+      __syncthreads();
+      if (sm_last) {
+        // last piece to arrive: merge all pieces of (s, g) and write the output
+        for (int idx = tid; idx < G * D; idx += NTH) {
+          const int gi = idx / D;
+          const int d = idx % D;
+          float Mx = -3.0e38f;
+          for (int64_t w = w0; w <= w1; ++w) {
+            const int pos = chunk_begin(w, C, nwg) >= ub ? 0 : 1;
+            const float* ps = a.ws + (w * 2 + pos) * SLOT;
+            Mx = fmaxf(Mx, __hip_atomic_load(ps + gi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          }
+          float o = 0.f, lsum = 0.f;
+          for (int64_t w = w0; w <= w1; ++w) {
+            const int pos = chunk_begin(w, C, nwg) >= ub ? 0 : 1;
+            const float* ps = a.ws + (w * 2 + pos) * SLOT;
+            const float m = __hip_atomic_load(ps + gi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float f = __builtin_amdgcn_exp2f(m - Mx);
+            lsum = fmaf(f, __hip_atomic_load(ps + G + gi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), lsum);
+            o = fmaf(f, __hip_atomic_load(ps + 2 * G + gi * D + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), o);
+          }
+          const float val = lsum > 0.f ? (o / lsum) * a.out_mul : 0.f;
+          store_io<IO>(a.out, ((int64_t)s * H + g * G + gi) * D + d, val);
+        }
+        // leave the counter at zero for the next call
+        if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();  // LDS is reused by the next segment
+    c += len;
+    first_seg = false;
+  }
+}
+
+}  // namespace pa

@@ -35,12 +35,18 @@ def to_device(b, device="cuda"):
                 context_lens=torch.from_numpy(b.context_lens).to(device))
 
 
-def run(b, dev, mode="direct", partition_size=None, stream=None):
-    """HIP decode of a batch; returns the output tensor (io dtype, on the device)."""
+def run(b, dev, mode="direct", partition_size=None, stream=None, num_workgroups=0, workspace=None):
+    """HIP decode of a batch; returns the output tensor (io dtype, on the device).
+    mode: "direct" (pa_decode), "partitioned" (partition_size) or "balanced"
+    (num_workgroups, 0 = library default)."""
     kw = dict(scale=float(b.scale), k_scale=float(b.k_scale), v_scale=float(b.v_scale), stream=stream)
     if mode == "direct":
         return pa.pa_decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"],
                             dev["context_lens"], **kw)
+    if mode == "balanced":
+        return pa.pa_decode_balanced(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"],
+                                     dev["context_lens"], num_workgroups=num_workgroups,
+                                     workspace=workspace, **kw)
     P = partition_size if partition_size is not None else (b.spec.partition_size or 512)
     return pa.pa_decode_partitioned(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"],
                                     dev["context_lens"], max(b.max_context_len, 1),

@@ -112,9 +112,39 @@ def test_partitioned_workspace_and_partition_checks():
 def test_debug_trace_requires_buffers():
     L = _lib.lib()
     a = good_args()
-    assert L.pa_debug_trace(*a, 100, 0, None, 0, FAKE, 0, FAKE, FAKE, None) == _lib.PA_ERR_INVALID
-    assert L.pa_debug_trace(*a, 100, 0, None, 0, FAKE, FAKE, FAKE, 0, None) == _lib.PA_ERR_INVALID
-    assert L.pa_debug_trace(*a, 0, 0, None, 0, FAKE, FAKE, FAKE, FAKE, None) == _lib.PA_ERR_INVALID
+    assert L.pa_debug_trace(*a, 100, 0, 0, None, 0, FAKE, 0, FAKE, FAKE, None) == _lib.PA_ERR_INVALID
+    assert L.pa_debug_trace(*a, 100, 0, 0, None, 0, FAKE, FAKE, FAKE, 0, None) == _lib.PA_ERR_INVALID
+    assert L.pa_debug_trace(*a, 0, 0, 0, None, 0, FAKE, FAKE, FAKE, FAKE, None) == _lib.PA_ERR_INVALID
+    # a partition size and a workgroup count at once, or negative values
+    assert L.pa_debug_trace(*a, 100, 16, 8, FAKE, 1 << 20, FAKE, FAKE, FAKE, FAKE, None) == _lib.PA_ERR_INVALID
+    assert L.pa_debug_trace(*a, 100, 0, -1, FAKE, 1 << 20, FAKE, FAKE, FAKE, FAKE, None) == _lib.PA_ERR_INVALID
+
+
+@pytest.mark.parametrize("over,code", BAD[:15], ids=[str(b[0]) for b in BAD[:15]])
+def test_balanced_rejects(over, code):
+    L = _lib.lib()
+    assert L.pa_decode_balanced(*good_args(**over), 64, FAKE, 1 << 20, FAKE, None) == code
+
+
+def test_balanced_workspace_checks():
+    L = _lib.lib()
+    # a shape the balanced kernel takes: f16, 8 query heads over 2 KV heads, head_dim 128
+    a = good_args(io=_lib.PA_F16, kv=_lib.PA_F16, H=8, Hkv=2, D=128)
+    need = _lib.pa_balanced_workspace_bytes(4, 8, 2, 128, 64)
+    assert L.pa_decode_balanced(*a, 64, FAKE, need - 16, FAKE, None) == _lib.PA_ERR_WORKSPACE
+    assert L.pa_decode_balanced(*a, 64, 0, need, FAKE, None) == _lib.PA_ERR_WORKSPACE
+    assert L.pa_decode_balanced(*a, 64, FAKE + 4, need, FAKE, None) == _lib.PA_ERR_INVALID
+    assert L.pa_decode_balanced(*a, -2, FAKE, need, FAKE, None) == _lib.PA_ERR_INVALID
+
+
+def test_balanced_workspace_formula():
+    # counters: one int32 per (KV head, sequence), padded to 256 bytes; then per workgroup
+    # two slots of G maxima, G sums and G x head_dim partial outputs, fp32
+    assert _lib.pa_balanced_workspace_bytes(64, 32, 8, 128, 512) == 2048 + 512 * 2 * 4 * 130 * 4
+    assert _lib.pa_balanced_workspace_bytes(3, 4, 4, 64, 10) == 256 + 10 * 2 * 1 * 66 * 4
+    assert _lib.pa_balanced_workspace_bytes(0, 4, 4, 64, 10) == 0
+    assert _lib.pa_balanced_workspace_bytes(2, 6, 4, 64, 10) == 0
+    assert _lib.pa_balanced_workspace_bytes(2, 4, 4, 64, -1) == 0
 
 
 def test_small_entry_points_reject():

@@ -23,16 +23,21 @@ def _native_library():
     pa._lib.lib()
 
 
-MODES = [("direct", None), ("partitioned", 64), ("partitioned", 512)]
+MODES = [("direct", None), ("partitioned", 64), ("partitioned", 512), ("balanced", 1),
+         ("balanced", 3), ("balanced", 7), ("balanced", 64), ("balanced", 0)]
 
 
-@pytest.mark.parametrize("mode,P", MODES, ids=["direct", "part64", "part512"])
+@pytest.mark.parametrize("mode,P", MODES, ids=["direct", "part64", "part512", "bal1", "bal3",
+                                               "bal7", "bal64", "bal_default"])
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 def test_small_parity(cfg, mode, P):
     b = W.make_batch(W.small_variant(cfg))
     log(f"[small] cfg={cfg} {b.spec.name} mode={mode} P={P} lens={b.context_lens.tolist()[:8]}")
     dev = to_device(b)
-    got = to_f64(run(b, dev, mode, P))
+    if mode == "balanced":
+        got = to_f64(run(b, dev, mode, num_workgroups=P))
+    else:
+        got = to_f64(run(b, dev, mode, P))
     err = check_against_oracle(b, got)
     if b.spec.kv_dtype == "f32":
         assert err <= F32_DERIVED, err
@@ -53,23 +58,28 @@ def _raw_u8(a):
     return np.ascontiguousarray(a).view(np.uint8)
 
 
-@pytest.mark.parametrize("P", [0, 64], ids=["direct", "part64"])
+@pytest.mark.parametrize("P,NWG", [(0, 0), (64, 0), (0, 5), (0, 13)],
+                         ids=["direct", "part64", "bal5", "bal13"])
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
-def test_trace_every_position_read_once_bit_exact(cfg, P):
+def test_trace_every_position_read_once_bit_exact(cfg, P, NWG):
     """The instrumented kernels copy each K/V row they consume and count the reads:
     every (sequence, KV head, position < L) is read exactly once, nothing else is read,
     and the bytes equal the oracle's block-table gather."""
     import torch
     b = W.make_batch(W.small_variant(cfg))
     sp = b.spec
-    log(f"[trace] cfg={cfg} P={P}")
+    log(f"[trace] cfg={cfg} P={P} NWG={NWG}")
     dev = to_device(b)
     maxL = b.max_context_len
     out, kr, vr, counts = pa.pa_debug_trace(dev["q"], dev["k_pool"], dev["v_pool"],
                                             dev["block_tables"], dev["context_lens"], maxL,
                                             scale=float(b.scale), partition_size=P,
+                                            num_workgroups=NWG,
                                             k_scale=float(b.k_scale), v_scale=float(b.v_scale))
-    plain = run(b, dev, "direct" if P == 0 else "partitioned", P or None)
+    if NWG:
+        plain = run(b, dev, "balanced", num_workgroups=NWG)
+    else:
+        plain = run(b, dev, "direct" if P == 0 else "partitioned", P or None)
     torch.cuda.synchronize()
     assert torch.equal(out, plain)
     counts = counts.cpu().numpy()
@@ -90,14 +100,15 @@ def test_trace_every_position_read_once_bit_exact(cfg, P):
             np.testing.assert_array_equal(_raw_u8(vr[s, g, :L]), _raw_u8(ev))
 
 
+@pytest.mark.parametrize("mode,NWG", [("direct", 0), ("balanced", 6)], ids=["direct", "bal6"])
 @pytest.mark.parametrize("cfg", [0, 2, 4])
-def test_placement_blocksize_sharing_bitwise(cfg):
+def test_placement_blocksize_sharing_bitwise(cfg, mode, NWG):
     """Outputs depend only on logical positions: the same bits under a new physical
     placement, under private copies of shared prefix blocks, and under another block size."""
     import torch
     b = W.make_batch(W.small_variant(cfg), keep_logical=True)
-    log(f"[invariance] cfg={cfg}")
-    base = run(b, to_device(b))
+    log(f"[invariance] cfg={cfg} mode={mode}")
+    base = run(b, to_device(b), mode, num_workgroups=NWG)
     variants = [W.repage(b, seed=5), W.repage(b, seed=6)]
     if b.spec.shared_prefix:
         variants.append(W.repage(b, unshare=True, seed=7))
@@ -106,7 +117,7 @@ def test_placement_blocksize_sharing_bitwise(cfg):
             continue
         variants.append(W.repage(b, block_size=bs, seed=bs))
     for v in variants:
-        got = run(v, to_device(v))
+        got = run(v, to_device(v), mode, num_workgroups=NWG)
         torch.cuda.synchronize()
         assert torch.equal(got, base), (v.spec.block_size, v.num_blocks)
 
@@ -139,8 +150,12 @@ def test_edge_shapes(io, kv, D, BS, G):
                   ("fixed", EDGE_LENS), seed=3000 + D + BS + G)
     b = W.make_batch(spec)
     dev = to_device(b)
-    for mode, P in (("direct", None), ("partitioned", BS), ("partitioned", 2 * BS)):
-        got = to_f64(run(b, dev, mode, P))
+    for mode, P in (("direct", None), ("partitioned", BS), ("partitioned", 2 * BS), ("balanced", 1),
+                    ("balanced", 4), ("balanced", 9)):
+        if mode == "balanced":
+            got = to_f64(run(b, dev, mode, num_workgroups=P))
+        else:
+            got = to_f64(run(b, dev, mode, P))
         check_against_oracle(b, got, io_rounding=True)
         zero = b.context_lens == 0
         assert (got[zero] == 0).all()
@@ -163,6 +178,27 @@ def test_all_empty_batch():
     for mode in ("direct", "partitioned"):
         got = to_f64(run(b, dev, mode, 16))
         assert (got == 0).all()
+    for nwg in (1, 3, 40):
+        got = to_f64(run(b, dev, "balanced", num_workgroups=nwg))
+        assert (got == 0).all()
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+def test_balanced_workspace_reuse(cfg):
+    """One workspace serves repeated calls: each call leaves the arrival counters at zero
+    and gives the same bits (pieces are always merged in the same order)."""
+    import torch
+    b = W.make_batch(W.small_variant(cfg))
+    dev = to_device(b)
+    ws = pa.balanced_workspace(dev["q"], dev["k_pool"], 7)
+    outs = [run(b, dev, "balanced", num_workgroups=7, workspace=ws).clone() for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    sp = b.spec
+    ncount = sp.num_kv_heads * sp.num_seqs
+    assert int(ws[:4 * ncount].view(torch.int32).abs().sum()) == 0
+    check_against_oracle(b, to_f64(outs[0]))
 
 
 def test_many_partitions_merge():
@@ -223,8 +259,9 @@ def _sample_pairs(b, cfg):
     return [(int(s), int(h)) for s in seqs for h in (0, 5, 18, 31)]
 
 
-FULL = [(0, "direct"), (1, "direct"), (1, "partitioned"), (2, "direct"), (2, "partitioned"),
-        (4, "partitioned"), (4, "direct"), (3, "partitioned"), (3, "direct")]
+FULL = [(0, "direct"), (1, "direct"), (1, "partitioned"), (1, "balanced"), (2, "direct"),
+        (2, "partitioned"), (2, "balanced"), (4, "partitioned"), (4, "direct"), (4, "balanced"),
+        (3, "partitioned"), (3, "direct"), (3, "balanced")]
 
 
 @pytest.mark.slow
