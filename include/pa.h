@@ -124,7 +124,7 @@ size_t pa_balanced_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads
                                    int num_workgroups);
 
 /* Work-balanced decode. Same result as pa_decode; the schedule differs: the cached tokens
- * of every (KV head, sequence) are cut into 32-token chunks, and a fixed grid of
+ * of every (KV head, sequence) are cut into 16-token chunks, and a fixed grid of
  * num_workgroups workgroups (0 = library default) takes equal shares of all chunks of the
  * batch, whatever the mix of context lengths. A (KV head, sequence) whose chunks are
  * shared by several workgroups is finished by the last of them to arrive, which merges

@@ -8,6 +8,7 @@ kernels; there is no CPU path. If the library is missing the first call raises.
 from __future__ import annotations
 
 import ctypes
+import functools
 import math
 import os
 from typing import Optional
@@ -285,9 +286,7 @@ class DecodePlan:
     def __call__(self, k_pool=None, v_pool=None):
         a = self._args
         if k_pool is not None:
-            if (tuple(k_pool.shape), k_pool.dtype, k_pool.device) != self._kmeta or \
-               (tuple(v_pool.shape), v_pool.dtype, v_pool.device) != self._kmeta:
-                raise ValueError("replacement pools must match the planned pools")
+            self._check_pools(k_pool, v_pool)
             a = list(a)
             a[1] = k_pool.data_ptr()
             a[2] = v_pool.data_ptr()
@@ -295,6 +294,21 @@ class DecodePlan:
         if rc != PA_OK:
             raise PagedAttentionError(self._name, rc)
         return self.out
+
+    def _check_pools(self, k_pool, v_pool):
+        if (tuple(k_pool.shape), k_pool.dtype, k_pool.device) != self._kmeta or \
+           (tuple(v_pool.shape), v_pool.dtype, v_pool.device) != self._kmeta:
+            raise ValueError("replacement pools must match the planned pools")
+
+    def bound(self, k_pool, v_pool):
+        """A zero-argument callable that enqueues this decode on the given pools (another
+        layer's cache of identical shape) with every argument already marshalled; it
+        returns the library's status code. The pools must outlive the callable."""
+        self._check_pools(k_pool, v_pool)
+        a = list(self._args)
+        a[1] = ctypes.c_void_p(k_pool.data_ptr())
+        a[2] = ctypes.c_void_p(v_pool.data_ptr())
+        return functools.partial(self._fn, *a)
 
 
 def pa_check_tables(block_tables, context_lens, num_blocks: int, block_size: int,

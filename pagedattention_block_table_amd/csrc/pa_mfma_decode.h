@@ -32,8 +32,9 @@
 // placement or sharing. Each wave fetches the table entries of its chunks ahead, 64 at a
 // time, and keeps the next chunk's K/V loads in flight while it computes the current one.
 //
-// Two schedulers use the same chunk engine:
-//   mfma_decode_kernel      one workgroup per (KV head, sequence, partition);
+// Two schedulers use the same chunk math:
+//   mfma_decode_kernel      one workgroup per (KV head, sequence, partition), its waves
+//                           taking the chunks round robin and merging through LDS;
 //   balanced_decode_kernel  a fixed grid of workgroups splits the total chunk count of
 //                           the batch evenly; a (KV head, sequence) whose chunks span
 //                           several workgroups is merged by the last one to finish it.
@@ -134,6 +135,13 @@ __device__ __forceinline__ int rotated(int idx, int rot, int len) {
   return c >= len ? c - len : c;
 }
 
+// Lane roles inside a wave: n = token of a 16-token tile, lg = lane group (which
+// 16-byte chunks of a row), hh = half of the tile the lane pairs with for V.
+struct LaneIds {
+  int lane, n, lg, hh;
+  __device__ __forceinline__ explicit LaneIds(int l) : lane(l), n(l & 15), lg(l >> 4), hh((l & 15) >> 3) {}
+};
+
 // K/V registers of one chunk in flight: K rows of the own token of each tile, V rows of
 // the own token and of its partner n^8.
 template <int KV, int D, int NT>
@@ -144,29 +152,251 @@ struct ChunkBuf {
   uint4 vp[NT][Geo::VPL];
 };
 
-// Per-wave state and chunk processing for one (sequence s, KV head g) at a time.
-//
-// A wave takes the chunks k0 + rotated(wave + k*NW, rot, len), k = 0, 1, ... of a
-// segment. Their block-table entries are fetched ahead by one vector load per 64 chunks
-// (lane l holds the entries of the wave's chunk 64*w + l; the next window is loaded while
-// the current one is used), and the K/V loads of chunk k+1 are in flight while chunk k is
-// computed, so a wave never waits on a table entry and always has a chunk outstanding.
+// Online-softmax state of one wave for one (sequence, KV head): per head the running max
+// (log2 units, wave-uniform), the lane's partial exp-sum and its partial outputs.
+template <int KV, int D, int G>
+struct WaveState {
+  using Geo = MfmaGeo<KV, D>;
+  float m[G], l[G];
+  float acc[G][Geo::VPL][Geo::VEC];
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      m[r] = -3.0e38f;
+      l[r] = 0.f;
+#pragma unroll
+      for (int q = 0; q < Geo::VPL; ++q)
+#pragma unroll
+        for (int e = 0; e < Geo::VEC; ++e) acc[r][q][e] = 0.f;
+    }
+  }
+};
+
+// Query operands of (sequence s, KV head g): row n of A is head g*G + n%G, and the k
+// index (lg, e) of step i*VEC/8 + hf is column VEC*(4i+lg) + 8*hf + e.
+template <int IO, int KV, int D, int G>
+__device__ __forceinline__ void load_q(const DecodeArgs& a, int s, int g, const LaneIds& li,
+                                       typename Mma<IO>::vec (&qa)[MfmaGeo<KV, D>::NST]) {
+  using Geo = MfmaGeo<KV, D>;
+  const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)s * a.num_heads + g * G + (li.n % G)) * D;
+#pragma unroll
+  for (int i = 0; i < Geo::CPL; ++i) {
+    const int col = Geo::VEC * (4 * i + li.lg);
+#pragma unroll
+    for (int hf = 0; hf < Geo::VEC / 8; ++hf) {
+      const uint4 w = *(const uint4*)(qrow + col + 8 * hf);
+      qa[i * (Geo::VEC / 8) + hf] = __builtin_bit_cast(typename Mma<IO>::vec, w);
+    }
+  }
+}
+
+// Issue the K/V loads of the chunk whose first token is c0 (a multiple of the block size
+// or of 16), with off[u] = byte offset of the chunk's u-th block and kbase / vbase
+// pointing at the KV head's tile of block 0. Rows at or past t_end are not loaded.
+template <int KV, int D, int BS, int NT>
+__device__ __forceinline__ void issue_chunk(ChunkBuf<KV, D, NT>& b, const char* kbase, const char* vbase,
+                                            const int64_t* off, int c0, int t_end, const LaneIds& li) {
+  using Geo = MfmaGeo<KV, D>;
+  constexpr int CT = 16 * NT, RB = Geo::RB, CPL = Geo::CPL, VPL = Geo::VPL;
+  constexpr int NBC = CT >= BS ? CT / BS : 1;
+  const int jb = c0 / BS;
+  const bool tail = c0 + CT > t_end;
+#pragma unroll
+  for (int tau = 0; tau < NT; ++tau) {
+    const int to = c0 + 16 * tau + li.n;          // own token
+    const int tp = c0 + 16 * tau + (li.n ^ 8);    // partner token
+    int64_t bo = off[0], bp = off[0];
+#pragma unroll
+    for (int u = 1; u < NBC; ++u) {
+      bo = to / BS - jb == u ? off[u] : bo;
+      bp = tp / BS - jb == u ? off[u] : bp;
+    }
+    const char* krow = kbase + bo + (to % BS) * RB;
+    const char* vrow_o = vbase + bo + (to % BS) * RB;
+    const char* vrow_p = vbase + bp + (tp % BS) * RB;
+    if (!tail) {
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) b.kr[tau][i] = load16(krow + 16 * (4 * i + li.lg));
+#pragma unroll
+      for (int q = 0; q < VPL; ++q) {
+        const int vc = 4 * (VPL * li.hh + q) + li.lg;
+        b.vo[tau][q] = load16(vrow_o + 16 * vc);
+        b.vp[tau][q] = load16(vrow_p + 16 * vc);
+      }
+    } else {
+      const bool ok_o = to < t_end;
+      const bool ok_p = tp < t_end;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i)
+        b.kr[tau][i] = ok_o ? load16(krow + 16 * (4 * i + li.lg)) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < VPL; ++q) {
+        const int vc = 4 * (VPL * li.hh + q) + li.lg;
+        b.vo[tau][q] = ok_o ? load16(vrow_o + 16 * vc) : make_uint4(0, 0, 0, 0);
+        b.vp[tau][q] = ok_p ? load16(vrow_p + 16 * vc) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Test builds: copy the raw K/V rows the wave consumes and count the reads of each
+// (sequence s, KV head g, token).
+template <int KV, int D, int NT>
+__device__ __forceinline__ void trace_chunk(const DecodeArgs& a, const ChunkBuf<KV, D, NT>& b, int s, int g,
+                                            int c0, int t_end, const LaneIds& li) {
+  using Geo = MfmaGeo<KV, D>;
+  constexpr int RB = Geo::RB, CPL = Geo::CPL, VPL = Geo::VPL;
+  const int Hkv = a.num_kv_heads;
+#pragma unroll
+  for (int tau = 0; tau < NT; ++tau) {
+    const int to = c0 + 16 * tau + li.n;
+    const int tp = c0 + 16 * tau + (li.n ^ 8);
+    const int64_t ro = ((int64_t)s * Hkv + g) * a.dbg_max_ctx + to;
+    const int64_t rp = ((int64_t)s * Hkv + g) * a.dbg_max_ctx + tp;
+    if (to < t_end) {
+#pragma unroll
+      for (int i = 0; i < CPL; ++i)
+        *(uint4*)((char*)a.dbg_k + ro * RB + 16 * (4 * i + li.lg)) = b.kr[tau][i];
+#pragma unroll
+      for (int q = 0; q < VPL; ++q)
+        *(uint4*)((char*)a.dbg_v + ro * RB + 16 * (4 * (VPL * li.hh + q) + li.lg)) = b.vo[tau][q];
+      if (li.lg == 0) atomicAdd(a.dbg_counts + ro, 1);
+    }
+    if (tp < t_end) {
+#pragma unroll
+      for (int q = 0; q < VPL; ++q)
+        *(uint4*)((char*)a.dbg_v + rp * RB + 16 * (4 * (VPL * li.hh + q) + li.lg)) = b.vp[tau][q];
+    }
+  }
+}
+
+// Scores, online softmax and V accumulation of one loaded chunk (first token c0).
+template <int IO, int KV, int D, int G, int NT>
+__device__ __forceinline__ void consume_chunk(const DecodeArgs& a, const ChunkBuf<KV, D, NT>& b,
+                                              const typename Mma<IO>::vec (&qa)[MfmaGeo<KV, D>::NST],
+                                              int c0, int t_end, WaveState<KV, D, G>& st,
+                                              const LaneIds& li) {
+  using Geo = MfmaGeo<KV, D>;
+  using M = Mma<IO>;
+  constexpr int VEC = Geo::VEC, CPL = Geo::CPL, VPL = Geo::VPL;
+  // scores of the G heads for the own token of each tile (log2 units)
+  float z[NT][G];
+#pragma unroll
+  for (int tau = 0; tau < NT; ++tau) {
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+#pragma unroll
+      for (int hf = 0; hf < VEC / 8; ++hf)
+        c = M::mma(qa[i * (VEC / 8) + hf], k_operand<IO, KV>(b.kr[tau][i], hf), c);
+    const bool ok = c0 + 16 * tau + li.n < t_end;
+#pragma unroll
+    for (int r = 0; r < G; ++r) z[tau][r] = ok ? c[r] * a.q_mul : -INFINITY;
+  }
+
+  // chunk max per head (all four 16-lane rows hold the same values)
+  float mx[G];
+  bool raise = false;
+#pragma unroll
+  for (int r = 0; r < G; ++r) {
+    float x = z[0][r];
+#pragma unroll
+    for (int tau = 1; tau < NT; ++tau) x = fmaxf(x, z[tau][r]);
+    x = fmaxf(x, dpp<0x128>(x));  // row_ror 8
+    x = fmaxf(x, dpp<0x124>(x));  // row_ror 4
+    x = fmaxf(x, dpp<0x122>(x));  // row_ror 2
+    x = fmaxf(x, dpp<0x121>(x));  // row_ror 1
+    // keep the running max wave-uniform (scalar) even if rows differ in the last bit
+    mx[r] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+    raise |= mx[r] > st.m[r] + kLazyRescale;
+  }
+  if (raise) {
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      const float mn = fmaxf(st.m[r], mx[r]);
+      const float alpha = __builtin_amdgcn_exp2f(st.m[r] - mn);
+      st.m[r] = mn;
+      st.l[r] *= alpha;
+#pragma unroll
+      for (int q = 0; q < VPL; ++q)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) st.acc[r][q][e] *= alpha;
+    }
+  }
+
+#pragma unroll
+  for (int tau = 0; tau < NT; ++tau) {
+    float po[G], pp[G];
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      po[r] = __builtin_amdgcn_exp2f(z[tau][r] - st.m[r]);
+      st.l[r] += po[r];
+      pp[r] = dpp<0x128>(po[r]);  // lane n^8 holds the partner token
+    }
+#pragma unroll
+    for (int q = 0; q < VPL; ++q) {
+      float fo[VEC], fq[VEC];
+      widen16<KV>(b.vo[tau][q], fo);
+      widen16<KV>(b.vp[tau][q], fq);
+#pragma unroll
+      for (int r = 0; r < G; ++r)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          st.acc[r][q][e] = fmaf(po[r], fo[e], st.acc[r][q][e]);
+          st.acc[r][q][e] = fmaf(pp[r], fq[e], st.acc[r][q][e]);
+        }
+    }
+  }
+}
+
+// Reduce a wave's state: l over the 16 token lanes of a row (every lane gets the total),
+// acc over the 8 lanes of a half-row (lanes with n % 8 == 0 hold the totals for the
+// columns VEC*(4*(VPL*hh + q) + lg) + e).
+template <int KV, int D, int G>
+__device__ __forceinline__ void reduce_state(WaveState<KV, D, G>& st) {
+  using Geo = MfmaGeo<KV, D>;
+#pragma unroll
+  for (int r = 0; r < G; ++r) {
+    st.l[r] = group_sum<16>(st.l[r]);
+#pragma unroll
+    for (int q = 0; q < Geo::VPL; ++q)
+#pragma unroll
+      for (int e = 0; e < Geo::VEC; ++e) {
+        float x = st.acc[r][q][e];
+        x += dpp<kRowHalfMirror>(x);
+        x += dpp<kQuadXor2>(x);
+        x += dpp<kQuadXor1>(x);
+        st.acc[r][q][e] = x;
+      }
+  }
+}
+
+// Column of head_dim held in a reduced state's acc[r][q][e] by a lane with n % 8 == 0.
+template <int KV, int D>
+__device__ __forceinline__ int acc_column(const LaneIds& li, int q, int e) {
+  using Geo = MfmaGeo<KV, D>;
+  return Geo::VEC * (4 * (Geo::VPL * li.hh + q) + li.lg) + e;
+}
+
+// Per-wave processing of one segment of one (sequence s, KV head g): the wave takes the
+// chunks k0 + rotated(wave + k*NW, rot, len), k = 0, 1, ..., counted in CT-token chunks
+// from token `base`. Their block-table entries are fetched ahead by one vector load per
+// 64 chunks (lane l holds the entries of the wave's chunk 64*w + l; the next window is
+// loaded while the current one is used), and the K/V loads of chunk k+1 are in flight
+// while chunk k is computed.
 template <int IO, int KV, int D, int BS, int G, int NT, bool DBG>
 struct MfmaEngine {
   using Geo = MfmaGeo<KV, D>;
-  static constexpr int VEC = Geo::VEC, RB = Geo::RB, CPL = Geo::CPL, VPL = Geo::VPL,
-                       NST = Geo::NST;
   static constexpr int CT = 16 * NT;                 // tokens per chunk
   static constexpr int NBC = CT >= BS ? CT / BS : 1; // blocks per chunk
-  static constexpr int TILE_BYTES = BS * RB;
-  using M = Mma<IO>;
-  using vec = typename M::vec;
+  static constexpr int TILE_BYTES = BS * Geo::RB;
+  using vec = typename Mma<IO>::vec;
   using Buf = ChunkBuf<KV, D, NT>;
   static_assert(mfma_supported<IO, KV, D, G>(), "unsupported MFMA decode geometry");
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
   static_assert(CT % BS == 0 || BS % CT == 0, "chunks and blocks nest");
 
-  int lane, n, lg, hh;
+  LaneIds li;
   int s, g, t_end, j_end;
   int base, k0, len, rot, wave, nw;
   const int32_t* bt;
@@ -174,25 +404,17 @@ struct MfmaEngine {
   const char* vbase;
   int64_t blk_stride;
   int win[2][NBC];  // block ids of this wave's chunks, windows w and w + 1
-  vec qa[NST];
-  float m_run[G], l_run[G];
-  float acc[G][VPL][VEC];
+  vec qa[Geo::NST];
+  WaveState<KV, D, G> st;
 
-  __device__ __forceinline__ explicit MfmaEngine(int lane_) {
-    lane = lane_;
-    n = lane & 15;
-    lg = lane >> 4;
-    hh = n >> 3;
-  }
+  __device__ __forceinline__ explicit MfmaEngine(int lane) : li(lane) {}
 
-  // first token of this wave's k-th chunk
   __device__ __forceinline__ int chunk_token(int k) const {
     return base + CT * (k0 + rotated(wave + k * nw, rot, len));
   }
 
-  // table entries of this wave's chunks 64*w .. 64*w+63 (lane l: chunk 64*w + l)
   __device__ __forceinline__ void load_window(const DecodeArgs& a, int w, int (&dst)[NBC]) {
-    const int k = 64 * w + lane;
+    const int k = 64 * w + li.lane;
     const bool live = wave + k * nw < len;
     const int j = live ? chunk_token(k) / BS : 0;
 #pragma unroll
@@ -204,10 +426,6 @@ struct MfmaEngine {
     }
   }
 
-  // Start (sequence s_, KV head g_) whose valid tokens end at t_end_, for this wave's
-  // chunks of the segment of chunks k0_ .. k0_ + len_ - 1 counted from token base_ (a
-  // multiple of the block size): load the query operands and the first table windows,
-  // and clear the softmax state.
   __device__ __forceinline__ void begin(const DecodeArgs& a, int s_, int g_, int t_end_, int base_,
                                         int k0_, int len_, int rot_, int wave_, int nw_) {
     s = s_;
@@ -226,29 +444,10 @@ struct MfmaEngine {
     vbase = (const char*)a.v_pool + (int64_t)g * TILE_BYTES;
     load_window(a, 0, win[0]);
     load_window(a, 1, win[1]);
-    // row n of A is head g*G + n%G; k index (lg, e) <-> column VEC*(4i+lg)+e
-    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)s * a.num_heads + g * G + (n % G)) * D;
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const int col = VEC * (4 * i + lg);
-#pragma unroll
-      for (int hf = 0; hf < VEC / 8; ++hf) {
-        const uint4 w = *(const uint4*)(qrow + col + 8 * hf);
-        qa[i * (VEC / 8) + hf] = __builtin_bit_cast(vec, w);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < G; ++r) {
-      m_run[r] = -3.0e38f;
-      l_run[r] = 0.f;
-#pragma unroll
-      for (int k = 0; k < VPL; ++k)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[r][k][e] = 0.f;
-    }
+    load_q<IO, KV, D, G>(a, s, g, li, qa);
+    st.reset();
   }
 
-  // Issue the K/V loads of this wave's k-th chunk (chunks are issued in order k = 0, 1, ...).
   __device__ __forceinline__ void issue(const DecodeArgs& a, Buf& b, int k) {
     if ((k & 63) == 0 && k > 0) {
       // entering window k/64: it was loaded 64 chunks ago; fetch the one after it
@@ -256,149 +455,17 @@ struct MfmaEngine {
       for (int u = 0; u < NBC; ++u) win[0][u] = win[1][u];
       load_window(a, (k >> 6) + 1, win[1]);
     }
-    const int c0 = chunk_token(k);
     int64_t off[NBC];
 #pragma unroll
     for (int u = 0; u < NBC; ++u)
       off[u] = (int64_t)__builtin_amdgcn_readlane(win[0][u], k & 63) * blk_stride;
-    const int jb = c0 / BS;  // first block of the chunk
-    const bool tail = c0 + CT > t_end;
-#pragma unroll
-    for (int tau = 0; tau < NT; ++tau) {
-      const int to = c0 + 16 * tau + n;          // own token
-      const int tp = c0 + 16 * tau + (n ^ 8);    // partner token
-      const int uo = NBC > 1 ? to / BS - jb : 0;
-      const int up = NBC > 1 ? tp / BS - jb : 0;
-      int64_t bo = off[0], bp = off[0];
-#pragma unroll
-      for (int u = 1; u < NBC; ++u) {
-        bo = uo == u ? off[u] : bo;
-        bp = up == u ? off[u] : bp;
-      }
-      const char* krow = kbase + bo + (to % BS) * RB;
-      const char* vrow_o = vbase + bo + (to % BS) * RB;
-      const char* vrow_p = vbase + bp + (tp % BS) * RB;
-      if (!tail) {
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) b.kr[tau][i] = load16(krow + 16 * (4 * i + lg));
-#pragma unroll
-        for (int q = 0; q < VPL; ++q) {
-          const int vc = 4 * (VPL * hh + q) + lg;
-          b.vo[tau][q] = load16(vrow_o + 16 * vc);
-          b.vp[tau][q] = load16(vrow_p + 16 * vc);
-        }
-      } else {
-        const bool ok_o = to < t_end;
-        const bool ok_p = tp < t_end;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i)
-          b.kr[tau][i] = ok_o ? load16(krow + 16 * (4 * i + lg)) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int q = 0; q < VPL; ++q) {
-          const int vc = 4 * (VPL * hh + q) + lg;
-          b.vo[tau][q] = ok_o ? load16(vrow_o + 16 * vc) : make_uint4(0, 0, 0, 0);
-          b.vp[tau][q] = ok_p ? load16(vrow_p + 16 * vc) : make_uint4(0, 0, 0, 0);
-        }
-      }
-    }
+    issue_chunk<KV, D, BS, NT>(b, kbase, vbase, off, chunk_token(k), t_end, li);
   }
 
-  // Scores, online softmax and V accumulation of this wave's k-th chunk, loaded in b.
   __device__ __forceinline__ void consume(const DecodeArgs& a, const Buf& b, int k) {
     const int c0 = chunk_token(k);
-    if constexpr (DBG) {
-      const int Hkv = a.num_kv_heads;
-#pragma unroll
-      for (int tau = 0; tau < NT; ++tau) {
-        const int to = c0 + 16 * tau + n;
-        const int tp = c0 + 16 * tau + (n ^ 8);
-        const int64_t ro = ((int64_t)s * Hkv + g) * a.dbg_max_ctx + to;
-        const int64_t rp = ((int64_t)s * Hkv + g) * a.dbg_max_ctx + tp;
-        if (to < t_end) {
-#pragma unroll
-          for (int i = 0; i < CPL; ++i)
-            *(uint4*)((char*)a.dbg_k + ro * RB + 16 * (4 * i + lg)) = b.kr[tau][i];
-#pragma unroll
-          for (int q = 0; q < VPL; ++q)
-            *(uint4*)((char*)a.dbg_v + ro * RB + 16 * (4 * (VPL * hh + q) + lg)) = b.vo[tau][q];
-          if (lg == 0) atomicAdd(a.dbg_counts + ro, 1);
-        }
-        if (tp < t_end) {
-#pragma unroll
-          for (int q = 0; q < VPL; ++q)
-            *(uint4*)((char*)a.dbg_v + rp * RB + 16 * (4 * (VPL * hh + q) + lg)) = b.vp[tau][q];
-        }
-      }
-    }
-
-    // scores of the G heads for the own token of each tile (log2 units)
-    float z[NT][G];
-#pragma unroll
-    for (int tau = 0; tau < NT; ++tau) {
-      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < CPL; ++i)
-#pragma unroll
-        for (int hf = 0; hf < VEC / 8; ++hf)
-          c = M::mma(qa[i * (VEC / 8) + hf], k_operand<IO, KV>(b.kr[tau][i], hf), c);
-      const bool ok = c0 + 16 * tau + n < t_end;
-#pragma unroll
-      for (int r = 0; r < G; ++r) z[tau][r] = ok ? c[r] * a.q_mul : -INFINITY;
-    }
-
-    // chunk max per head (all four 16-lane rows hold the same values)
-    float mx[G];
-    bool raise = false;
-#pragma unroll
-    for (int r = 0; r < G; ++r) {
-      float x = z[0][r];
-#pragma unroll
-      for (int tau = 1; tau < NT; ++tau) x = fmaxf(x, z[tau][r]);
-      x = fmaxf(x, dpp<0x128>(x));  // row_ror 8
-      x = fmaxf(x, dpp<0x124>(x));  // row_ror 4
-      x = fmaxf(x, dpp<0x122>(x));  // row_ror 2
-      x = fmaxf(x, dpp<0x121>(x));  // row_ror 1
-      // keep the running max wave-uniform (scalar) even if rows differ in the last bit
-      mx[r] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
-      raise |= mx[r] > m_run[r] + kLazyRescale;
-    }
-    if (raise) {
-#pragma unroll
-      for (int r = 0; r < G; ++r) {
-        const float mn = fmaxf(m_run[r], mx[r]);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[r] - mn);
-        m_run[r] = mn;
-        l_run[r] *= alpha;
-#pragma unroll
-        for (int q = 0; q < VPL; ++q)
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[r][q][e] *= alpha;
-      }
-    }
-
-#pragma unroll
-    for (int tau = 0; tau < NT; ++tau) {
-      float po[G], pp[G];
-#pragma unroll
-      for (int r = 0; r < G; ++r) {
-        po[r] = __builtin_amdgcn_exp2f(z[tau][r] - m_run[r]);
-        l_run[r] += po[r];
-        pp[r] = dpp<0x128>(po[r]);  // lane n^8 holds the partner token
-      }
-#pragma unroll
-      for (int q = 0; q < VPL; ++q) {
-        float fo[VEC], fq[VEC];
-        widen16<KV>(b.vo[tau][q], fo);
-        widen16<KV>(b.vp[tau][q], fq);
-#pragma unroll
-        for (int r = 0; r < G; ++r)
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            acc[r][q][e] = fmaf(po[r], fo[e], acc[r][q][e]);
-            acc[r][q][e] = fmaf(pp[r], fq[e], acc[r][q][e]);
-          }
-      }
-    }
+    if constexpr (DBG) trace_chunk<KV, D, NT>(a, b, s, g, c0, t_end, li);
+    consume_chunk<IO, KV, D, G, NT>(a, b, qa, c0, t_end, st, li);
   }
 
   // This wave's chunks of the segment, two in flight.
@@ -417,35 +484,21 @@ struct MfmaEngine {
     }
   }
 
-  // Reduce the wave's state (l over the 16 token lanes of a row, acc over the 8 lanes of
-  // a half-row) and store it as wave `wave` of the workgroup's LDS arrays.
+  // Reduce the wave's state and store it as wave `wave` of the workgroup's LDS arrays.
   template <int NW>
   __device__ __forceinline__ void finish(float (&sm_m)[NW][G], float (&sm_l)[NW][G],
                                          float (&sm_o)[NW][G][D]) {
-#pragma unroll
-    for (int r = 0; r < G; ++r) {
-      l_run[r] = group_sum<16>(l_run[r]);
-#pragma unroll
-      for (int q = 0; q < VPL; ++q)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          float x = acc[r][q][e];
-          x += dpp<kRowHalfMirror>(x);
-          x += dpp<kQuadXor2>(x);
-          x += dpp<kQuadXor1>(x);
-          acc[r][q][e] = x;
-        }
-    }
-    if ((n & 7) == 0) {
+    reduce_state<KV, D, G>(st);
+    if ((li.n & 7) == 0) {
 #pragma unroll
       for (int r = 0; r < G; ++r) {
 #pragma unroll
-        for (int q = 0; q < VPL; ++q)
+        for (int q = 0; q < Geo::VPL; ++q)
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) sm_o[wave][r][VEC * (4 * (VPL * hh + q) + lg) + e] = acc[r][q][e];
-        if (lane == 0) {
-          sm_m[wave][r] = m_run[r];
-          sm_l[wave][r] = l_run[r];
+          for (int e = 0; e < Geo::VEC; ++e) sm_o[wave][r][acc_column<KV, D>(li, q, e)] = st.acc[r][q][e];
+        if (li.lane == 0) {
+          sm_m[wave][r] = st.m[r];
+          sm_l[wave][r] = st.l[r];
         }
       }
     }
