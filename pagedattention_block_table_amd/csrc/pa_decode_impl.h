@@ -565,7 +565,9 @@ int launch_one(const LaunchSpec& ls) {
         return PA_ERR_UNSUPPORTED;
       }
     }
-    if constexpr (PA_MFMA && mfma_supported<IO, KV, D, G>()) {
+    // one workgroup per unit: the matrix-core kernel when query heads share a KV head; for
+    // one query head per KV head the vector kernel (whole 1 KiB rows per wave load) is faster
+    if constexpr (PA_MFMA && G >= 2 && mfma_supported<IO, KV, D, G>()) {
       if (ls.debug) {
         hipLaunchKernelGGL((mfma_decode_kernel<IO, KV, D, BS, G, NW, true>), dim3(ls.grid),
                            dim3(NW * 64), 0, ls.stream, ls.args);

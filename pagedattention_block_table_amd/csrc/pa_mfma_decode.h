@@ -40,11 +40,14 @@
 //                           several workgroups is merged by the last one to finish it.
 #pragma once
 
+#include <type_traits>
+
 namespace pa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 // log2-unit headroom of the lazy running-max update (probabilities stay <= 2^8)
 constexpr float kLazyRescale = 8.0f;
@@ -505,6 +508,379 @@ struct MfmaEngine {
   }
 };
 
+// 16x16x16 products for the V side: A = probabilities, B = V^T tile read transposed
+// from LDS. Operands are four 16-bit values per lane: lane l supplies row l%16 of A and
+// column l%16 of B for k = 4*(l/16) .. 4*(l/16)+3; the result layout is that of the
+// 16x16x32 product.
+template <int MT> struct Mma16;
+template <> struct Mma16<kF16> {
+  typedef _Float16 v4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ f32x4_t mma(const v4& a, const v4& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
+  // p = hi + lo + (error <= 2^-22 |p|): both halves as f16 codes
+  static __device__ __forceinline__ void split(float p, uint16_t& hi, uint16_t& lo) {
+    const _Float16 h = (_Float16)p;
+    hi = __builtin_bit_cast(uint16_t, h);
+    lo = __builtin_bit_cast(uint16_t, (_Float16)(p - (float)h));
+  }
+};
+template <> struct Mma16<kBF16> {
+  typedef short v4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ f32x4_t mma(const v4& a, const v4& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+  // p = hi + lo + (error <= 2^-16 |p|): hi is p truncated to bf16, lo the truncated rest
+  static __device__ __forceinline__ void split(float p, uint16_t& hi, uint16_t& lo) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, p);
+    hi = (uint16_t)(u >> 16);
+    const float rest = p - __builtin_bit_cast(float, u & 0xffff0000u);
+    lo = (uint16_t)(__builtin_bit_cast(uint32_t, rest) >> 16);
+  }
+};
+
+// V registers of one 16-token chunk in flight, in memory order: instruction i of lane l
+// holds bytes 1024*i + 16*l .. +15 of the chunk's 16 V rows.
+template <int KV, int D>
+struct VTileRegs {
+  static constexpr int NV = 16 * D * ElemBytes<KV>::value / 1024;
+  uint4 v[NV > 0 ? NV : 1];
+};
+
+// Per-wave engine for G = 2 or 4 query heads per KV head with both products on the
+// matrix cores. Scores as in MfmaEngine (16x16x32, K^T straight from the lanes' loads).
+// The V product O[h][d] += sum_t P[h][t] V[t][d] runs as 16x16x16 MFMAs: each chunk's V
+// rows are loaded with contiguous 1 KiB wave loads, written to a per-wave LDS tile in the
+// MFMA type (fp8 widened exactly), and read back transposed (ds_read_b64_tr_b16: lane i
+// of a 16-lane group gets column i of four rows) as the B operand; the probabilities go
+// through LDS as the A operand (row h = head h % G, four tokens per lane), split into a
+// high and a low 16-bit part so that the product keeps fp32 accuracy. The accumulators
+// hold the complete sums over the wave's tokens: lane l, register r of d-tile dt holds
+// head (4*(l/16) + r) % G, column 16*dt + l%16.
+template <int IO, int KV, int D, int BS, int G, bool DBG>
+struct MfmaPvEngine {
+  using Geo = MfmaGeo<KV, D>;
+  static constexpr int NT = 1;
+  static constexpr int CT = 16;
+  static constexpr int NBC = CT >= BS ? CT / BS : 1;
+  static constexpr int RB = Geo::RB;
+  static constexpr int TILE_BYTES = BS * RB;
+  static constexpr int NDT = D / 16;           // 16-column tiles of head_dim
+  static constexpr int NV = VTileRegs<KV, D>::NV;
+  // LDS V tile in the MFMA type, rows padded by 32 bytes: the transposed reads of 16
+  // rows then spread over the 64 banks (two-way at most) instead of sharing 8 banks
+  static constexpr int VT_ROW = D + 16;        // 16-bit elements per tile row
+  static constexpr int VT_BYTES = 16 * VT_ROW * 2;
+  static constexpr int P_BYTES = 2 * G * 16 * 2;
+  static constexpr int kLdsBytes = VT_BYTES + P_BYTES;
+  using vec = typename Mma<IO>::vec;
+  using M16 = Mma16<IO>;
+  using v4 = typename M16::v4;
+  static_assert(G == 2 || G == 4, "group");
+  static_assert(mfma_supported<IO, KV, D, G>(), "unsupported MFMA decode geometry");
+  static_assert(NV >= 1 && 16 * RB % 1024 == 0, "V tile of whole wave loads");
+
+  struct Buf {
+    uint4 kr[Geo::CPL];
+    VTileRegs<KV, D> vt;
+  };
+
+  LaneIds li;
+  int s, g, t_end, j_end;
+  int base, k0, len, rot, wave, nw;
+  const int32_t* bt;
+  const char* kbase;
+  const char* vbase;
+  int64_t blk_stride;
+  int win[2][NBC];
+  vec qa[Geo::NST];
+  float m[G], l[G];
+  f32x4_t o[NDT];
+  char* lds;  // this wave's V tile and probability tiles
+
+  __device__ __forceinline__ MfmaPvEngine(int lane, char* wave_lds) : li(lane), lds(wave_lds) {}
+
+  __device__ __forceinline__ int chunk_token(int k) const {
+    return base + CT * (k0 + rotated(wave + k * nw, rot, len));
+  }
+
+  __device__ __forceinline__ void load_window(const DecodeArgs& a, int w, int (&dst)[NBC]) {
+    const int k = 64 * w + li.lane;
+    const bool live = wave + k * nw < len;
+    const int j = live ? chunk_token(k) / BS : 0;
+#pragma unroll
+    for (int u = 0; u < NBC; ++u) {
+      int b = 0;
+      if (live && j + u < j_end) b = bt[j + u];
+      // contract: 0 <= b < num_blocks; clamp so that a bad table never reads outside the pool
+      dst[u] = min(max(b, 0), a.num_blocks - 1);
+    }
+  }
+
+  __device__ __forceinline__ void begin(const DecodeArgs& a, int s_, int g_, int t_end_, int base_,
+                                        int k0_, int len_, int rot_, int wave_, int nw_) {
+    s = s_;
+    g = g_;
+    t_end = t_end_;
+    j_end = (t_end + BS - 1) / BS;
+    base = base_;
+    k0 = k0_;
+    len = len_;
+    rot = rot_;
+    wave = wave_;
+    nw = nw_;
+    bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    blk_stride = (int64_t)a.num_kv_heads * TILE_BYTES;
+    kbase = (const char*)a.k_pool + (int64_t)g * TILE_BYTES;
+    vbase = (const char*)a.v_pool + (int64_t)g * TILE_BYTES;
+    load_window(a, 0, win[0]);
+    load_window(a, 1, win[1]);
+    load_q<IO, KV, D, G>(a, s, g, li, qa);
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      m[r] = -3.0e38f;
+      l[r] = 0.f;
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  __device__ __forceinline__ void issue(const DecodeArgs& a, Buf& b, int k) {
+    if ((k & 63) == 0 && k > 0) {
+#pragma unroll
+      for (int u = 0; u < NBC; ++u) win[0][u] = win[1][u];
+      load_window(a, (k >> 6) + 1, win[1]);
+    }
+    int64_t off[NBC];
+#pragma unroll
+    for (int u = 0; u < NBC; ++u)
+      off[u] = (int64_t)__builtin_amdgcn_readlane(win[0][u], k & 63) * blk_stride;
+    const int c0 = chunk_token(k);
+    const int jb = c0 / BS;
+    const bool tail = c0 + CT > t_end;
+    // K: lane (n, lg) loads chunks 4i + lg of token n
+    {
+      const int to = c0 + li.n;
+      int64_t bo = off[0];
+#pragma unroll
+      for (int u = 1; u < NBC; ++u) bo = to / BS - jb == u ? off[u] : bo;
+      const char* krow = kbase + bo + (to % BS) * RB;
+      const bool ok = !tail || to < t_end;
+#pragma unroll
+      for (int i = 0; i < Geo::CPL; ++i)
+        b.kr[i] = ok ? load16(krow + 16 * (4 * i + li.lg)) : make_uint4(0, 0, 0, 0);
+    }
+    // V: instruction i covers bytes 1024*i .. of the 16 rows, in memory order
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int byte = 1024 * i + 16 * li.lane;
+      const int t = c0 + byte / RB;
+      int64_t bo = off[0];
+#pragma unroll
+      for (int u = 1; u < NBC; ++u) bo = t / BS - jb == u ? off[u] : bo;
+      const char* p = vbase + bo + (t % BS) * RB + byte % RB;
+      const bool ok = !tail || t < t_end;
+      b.vt.v[i] = ok ? load16(p) : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  __device__ __forceinline__ void trace(const DecodeArgs& a, const Buf& b, int c0) {
+    const int Hkv = a.num_kv_heads;
+    const int64_t row0 = ((int64_t)s * Hkv + g) * a.dbg_max_ctx;
+    const int to = c0 + li.n;
+    if (to < t_end) {
+#pragma unroll
+      for (int i = 0; i < Geo::CPL; ++i)
+        *(uint4*)((char*)a.dbg_k + (row0 + to) * RB + 16 * (4 * i + li.lg)) = b.kr[i];
+      if (li.lg == 0) atomicAdd(a.dbg_counts + row0 + to, 1);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int byte = 1024 * i + 16 * li.lane;
+      const int t = c0 + byte / RB;
+      if (t < t_end) *(uint4*)((char*)a.dbg_v + (row0 + t) * RB + byte % RB) = b.vt.v[i];
+    }
+  }
+
+  // Lanes of one wave exchange data through LDS: a wave-scope fence keeps the compiler
+  // from moving a lane's LDS reads above other lanes' writes (the hardware executes one
+  // wave's LDS instructions in order).
+  static __device__ __forceinline__ void lds_exchange() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  __device__ __forceinline__ void consume(const DecodeArgs& a, const Buf& b, int k) {
+    const int c0 = chunk_token(k);
+    if constexpr (DBG) trace(a, b, c0);
+
+    // the previous chunk's transposed reads of the tile come before these writes
+    lds_exchange();
+
+    // V rows -> LDS tile [16][D] in the MFMA type
+    uint16_t* vt = (uint16_t*)lds;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int byte = 1024 * i + 16 * li.lane;
+      const int t = byte / RB;
+      const int col = (byte % RB) / ElemBytes<KV>::value;
+      if constexpr (KV == kFP8) {
+        const uint4 r = b.vt.v[i];
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+        uint32_t packed[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], false);
+          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], true);
+          packed[2 * q] = Mma<IO>::pack2(lo.x, lo.y);
+          packed[2 * q + 1] = Mma<IO>::pack2(hi.x, hi.y);
+        }
+        *(uint4*)(vt + t * VT_ROW + col) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        *(uint4*)(vt + t * VT_ROW + col + 8) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+      } else {
+        *(uint4*)(vt + t * VT_ROW + col) = b.vt.v[i];
+      }
+    }
+
+    // the tile is read back by other lanes of the wave (transposed): order the writes
+    // before those reads
+    lds_exchange();
+
+    // scores of the G heads for token n (log2 units); register r holds head r % G
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < Geo::CPL; ++i)
+#pragma unroll
+      for (int hf = 0; hf < Geo::VEC / 8; ++hf)
+        c = Mma<IO>::mma(qa[i * (Geo::VEC / 8) + hf], k_operand<IO, KV>(b.kr[i], hf), c);
+    const bool ok = c0 + li.n < t_end;
+    float z[G];
+#pragma unroll
+    for (int r = 0; r < G; ++r) z[r] = ok ? c[r] * a.q_mul : -INFINITY;
+
+    float mx[G];
+    bool raise = false;
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      float x = z[r];
+      x = fmaxf(x, dpp<0x128>(x));  // row_ror 8
+      x = fmaxf(x, dpp<0x124>(x));  // row_ror 4
+      x = fmaxf(x, dpp<0x122>(x));  // row_ror 2
+      x = fmaxf(x, dpp<0x121>(x));  // row_ror 1
+      mx[r] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+      raise |= mx[r] > m[r] + kLazyRescale;
+    }
+    if (raise) {
+      float alpha[G];
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        const float mn = fmaxf(m[r], mx[r]);
+        alpha[r] = __builtin_amdgcn_exp2f(m[r] - mn);
+        m[r] = mn;
+        l[r] *= alpha[r];
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[dt][r] *= alpha[r % G];
+    }
+
+    // probabilities -> LDS as A operands [hi/lo][head][token]
+    uint16_t* pt = (uint16_t*)(lds + VT_BYTES);
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      const float p = __builtin_amdgcn_exp2f(z[r] - m[r]);
+      l[r] += p;
+      uint16_t hi, lo;
+      M16::split(p, hi, lo);
+      if (li.lg == 0) {
+        pt[r * 16 + li.n] = hi;
+        pt[G * 16 + r * 16 + li.n] = lo;
+      }
+    }
+    lds_exchange();
+    const int h = li.n % G;
+    const v4 ahi = *(const v4*)(pt + h * 16 + 4 * li.lg);
+    const v4 alo = *(const v4*)(pt + G * 16 + h * 16 + 4 * li.lg);
+
+    // O[h][16dt + i] += sum_t P[h][t] V[t][16dt + i]
+    const int vrow = 4 * li.lg + (li.n >> 2);
+    const int vcol = 4 * (li.n & 3);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const v4 bv = __builtin_bit_cast(
+          v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) i16x4_t*)(vt + vrow * VT_ROW + 16 * dt + vcol)));
+      o[dt] = M16::mma(ahi, bv, o[dt]);
+      o[dt] = M16::mma(alo, bv, o[dt]);
+    }
+  }
+
+  __device__ __forceinline__ void run(const DecodeArgs& a) {
+    const int nwc = wave < len ? (len - wave + nw - 1) / nw : 0;
+    Buf A, B;
+    if (nwc > 0) issue(a, A, 0);
+    if (nwc > 1) issue(a, B, 1);
+    for (int k = 0; k < nwc; k += 2) {
+      consume(a, A, k);
+      if (k + 2 < nwc) issue(a, A, k + 2);
+      if (k + 1 < nwc) {
+        consume(a, B, k + 1);
+        if (k + 3 < nwc) issue(a, B, k + 3);
+      }
+    }
+  }
+
+  template <int NW>
+  __device__ __forceinline__ void finish(float (&sm_m)[NW][G], float (&sm_l)[NW][G],
+                                         float (&sm_o)[NW][G][D]) {
+#pragma unroll
+    for (int r = 0; r < G; ++r) l[r] = group_sum<16>(l[r]);
+    if (li.lg == 0) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < G; ++r) sm_o[wave][r][16 * dt + li.n] = o[dt][r];
+    }
+    if (li.lane == 0) {
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        sm_m[wave][r] = m[r];
+        sm_l[wave][r] = l[r];
+      }
+    }
+  }
+};
+
+// Engine used for a shape: the V product on the matrix cores when 2 or 4 query heads
+// share a 16-bit KV head; on the vector ALUs for one query head per KV head (one FMA
+// per V element) and for fp8 KV, where widening the tile for the matrix cores costs
+// more vector work than the FMAs it replaces (measured on the mixed-length fp8 batch).
+#ifndef PA_MFMA_PV
+#define PA_MFMA_PV 1
+#endif
+template <int IO, int KV, int D, int BS, int G, bool DBG>
+struct EngineFor {
+  static constexpr bool pv = PA_MFMA_PV && (G == 2 || G == 4) && KV != kFP8;
+  using type = typename std::conditional<pv, MfmaPvEngine<IO, KV, D, BS, G, DBG>,
+                                         MfmaEngine<IO, KV, D, BS, G, PA_MFMA_TILES, DBG>>::type;
+  static constexpr int lds_bytes = pv ? MfmaPvEngine<IO, KV, D, BS, (pv ? G : 4), DBG>::kLdsBytes : 16;
+};
+
+template <class Eng> struct EngineMaker;  // builds an engine with or without its LDS tile
+template <int IO, int KV, int D, int BS, int G, int NT, bool DBG>
+struct EngineMaker<MfmaEngine<IO, KV, D, BS, G, NT, DBG>> {
+  static __device__ __forceinline__ MfmaEngine<IO, KV, D, BS, G, NT, DBG> make(int lane, char*) {
+    return MfmaEngine<IO, KV, D, BS, G, NT, DBG>(lane);
+  }
+};
+template <int IO, int KV, int D, int BS, int G, bool DBG>
+struct EngineMaker<MfmaPvEngine<IO, KV, D, BS, G, DBG>> {
+  static __device__ __forceinline__ MfmaPvEngine<IO, KV, D, BS, G, DBG> make(int lane, char* lds) {
+    return MfmaPvEngine<IO, KV, D, BS, G, DBG>(lane, lds);
+  }
+};
+
 // Merge of the NW wave states in LDS for element (head gi, column d): running max M,
 // sum of exp2(m - M) * l and of exp2(m - M) * o.
 template <int NW, int G, int D>
@@ -527,9 +903,11 @@ __device__ __forceinline__ void merge_waves(const float (&sm_m)[NW][G], const fl
 template <int IO, int KV, int D, int BS, int G, int NW, bool DBG>
 __global__ void __launch_bounds__(NW * 64)
 mfma_decode_kernel(const DecodeArgs a) {
-  using Eng = MfmaEngine<IO, KV, D, BS, G, PA_MFMA_TILES, DBG>;
+  using Sel = EngineFor<IO, KV, D, BS, G, DBG>;
+  using Eng = typename Sel::type;
   constexpr int CT = Eng::CT;
 
+  __shared__ __align__(16) char sm_eng[NW][Sel::lds_bytes];
   __shared__ float sm_m[NW][G];
   __shared__ float sm_l[NW][G];
   __shared__ float sm_o[NW][G][D];
@@ -547,7 +925,7 @@ mfma_decode_kernel(const DecodeArgs a) {
   const int t_end = min(L, t_begin + a.part_tokens);
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  Eng eng(threadIdx.x & 63);
+  Eng eng = EngineMaker<Eng>::make(threadIdx.x & 63, sm_eng[wave]);
   const int nch = (t_end - t_begin + CT - 1) / CT;
   const int rot = PA_STAGGER ? (s * 5) % max(nch, 1) : 0;
   eng.begin(a, s, g, t_end, t_begin, 0, nch, rot, wave, NW);
@@ -599,7 +977,8 @@ template <int G, int D> constexpr int slot_floats() { return G * (D + 2); }
 template <int IO, int KV, int D, int BS, int G, int NW, bool DBG>
 __global__ void __launch_bounds__(NW * 64)
 balanced_decode_kernel(const DecodeArgs a) {
-  using Eng = MfmaEngine<IO, KV, D, BS, G, PA_MFMA_TILES, DBG>;
+  using Sel = EngineFor<IO, KV, D, BS, G, DBG>;
+  using Eng = typename Sel::type;
   constexpr int CT = Eng::CT;
   constexpr int NTH = NW * 64;
   constexpr int SLOT = slot_floats<G, D>();
@@ -610,6 +989,7 @@ balanced_decode_kernel(const DecodeArgs a) {
   __shared__ int sm_pref[kMaxBalancedSeqs + 1];  // exclusive prefix sums of chunk counts
   __shared__ int sm_wsum[NW];
   __shared__ int sm_last;
+  __shared__ __align__(16) char sm_eng[NW][Sel::lds_bytes];
 
   const int S = a.num_seqs;
   const int tid = threadIdx.x;
@@ -658,7 +1038,7 @@ balanced_decode_kernel(const DecodeArgs a) {
   const int64_t cb = chunk_begin(v, C, nwg);
   const int64_t ce = chunk_begin(v + 1, C, nwg);
 
-  Eng eng(lane);
+  Eng eng = EngineMaker<Eng>::make(lane, sm_eng[wave]);
   const int H = a.num_heads;
   int64_t c = cb;
   bool first_seg = true;
