@@ -31,6 +31,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 METRIC = "paged-attn decode KV GB/s read and % of MI355X HBM peak; seqs·tokens/s"
 DEFAULT_MODE = {0: "direct", 1: "direct", 2: "direct", 3: "balanced", 4: "balanced"}
 KERNEL_SOURCES = ["pagedattention_block_table_amd/csrc/pa_decode_impl.h",
+                  "pagedattention_block_table_amd/csrc/pa_mfma_decode.h",
                   "pagedattention_block_table_amd/csrc/pa_api.hip"]
 
 
