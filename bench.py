@@ -230,6 +230,32 @@ def main():
     durs_ms = [s.elapsed_time(e_) for s, e_ in zip(starts, ends)]
     kern_ms = float(np.mean(durs_ms))
 
+    # the write that precedes each decode step: one new token's K/V per sequence, stored
+    # (quantised for fp8) into its block. Timed on its own; the appended rows go to the slot
+    # of each sequence's last cached token, so the pool keeps its shape and cost is the same.
+    app = None
+    if sp.io_dtype in ("f32", "f16", "bf16"):
+        gen = torch.Generator(device="cuda").manual_seed(7)
+        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[sp.io_dtype]
+        kn = torch.randn((sp.num_seqs, sp.num_kv_heads, sp.head_dim), generator=gen, device="cuda").to(tdt)
+        vn = torch.randn((sp.num_seqs, sp.num_kv_heads, sp.head_dim), generator=gen, device="cuda").to(tdt)
+        sid = torch.arange(sp.num_seqs, dtype=torch.int32, device="cuda")
+        pos = torch.clamp(cl - 1, min=0)
+        appk = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K)]
+        for i in range(3):
+            pa.pa_append_kv(kn, vn, sid, pos, bt, k0, v0, k_scale=float(b.k_scale), v_scale=float(b.v_scale))
+        torch.cuda.synchronize()
+        for i in range(K):
+            appk[2 * i].record(stream)
+            pa.pa_append_kv(kn, vn, sid, pos, bt, k0, v0, k_scale=float(b.k_scale), v_scale=float(b.v_scale))
+            appk[2 * i + 1].record(stream)
+        torch.cuda.synchronize()
+        app_ms = float(np.mean([appk[2 * i].elapsed_time(appk[2 * i + 1]) for i in range(K)]))
+        io_b = {"f32": 4, "f16": 2, "bf16": 2}[sp.io_dtype]
+        app_bytes = sp.num_seqs * (sp.num_kv_heads * sp.head_dim * 2 * (io_b + e) + 12)
+        app = {"us_per_launch": round(app_ms * 1e3, 3), "bytes_per_launch": app_bytes,
+               "GB_per_s": round(app_bytes / (app_ms * 1e-3) / 1e9, 2)}
+
     value = kv_unique / (ms_per_step * 1e-3) / 1e9
     achieved = algo_bytes / (kern_ms * 1e-3) / 1e9
     traffic = read_traffic(sp.name, mode)
@@ -268,6 +294,7 @@ def main():
                      "p10_p90_ms": [round(float(np.percentile(durs_ms, 10)), 6),
                                     round(float(np.percentile(durs_ms, 90)), 6)]},
         "cpu_baseline": None,
+        "append_kv": app,
     }
     log(f"[bench] {ms_per_step * 1e3:.2f} us/step wall, {kern_ms * 1e3:.2f} us/launch (events): "
         f"{value:.1f} GB/s KV, roofline frac {achieved / HBM_PEAK_GBS:.3f}")

@@ -163,6 +163,26 @@ int pa_debug_trace(const void* q, const void* k_pool, const void* v_pool,
                    void* workspace, size_t workspace_bytes, void* out,
                    void* k_rows, void* v_rows, int32_t* read_counts, void* stream);
 
+/* Appends new tokens' keys and values to the paged cache ([P1] §2 block table; [P3]
+ * paged pool: a growing request writes into its last block and gets blocks appended;
+ * [P2] §2.1 decode mode). Token t (of num_tokens) belongs to sequence seq_ids[t] at
+ * logical position positions[t]; its rows
+ *   k_new[t][g][:], v_new[t][g][:]   (layout [num_tokens][num_kv_heads][head_dim], src_dtype)
+ * are stored, for every KV head g, at
+ *   k_pool[ block_tables[s][p / block_size] ][g][p % block_size][:]   (and v_pool)
+ * src_dtype is F32, F16 or BF16; kv_dtype equals it (the bits are copied) or is
+ * PA_FP8_E4M3, which stores e4m3(x / k_scale) (v_scale for V): the quotient rounded to
+ * fp32, then to the nearest e4m3 value (ties to even), magnitudes above 448 saturated to
+ * +-448, NaN kept as NaN. The caller allocates the blocks (the table entries must exist);
+ * a token whose sequence, position or block lies outside the tables or the pool is
+ * skipped. Pointers to k_new, v_new and the pools must be 16-byte aligned; head_dim in
+ * {64, 128}, block_size in {8, 16, 32}. Asynchronous on `stream`; allocates nothing. */
+int pa_append_kv(const void* k_new, const void* v_new, const int32_t* seq_ids,
+                 const int32_t* positions, int num_tokens, const int32_t* block_tables,
+                 int num_seqs, int max_blocks_per_seq, void* k_pool, void* v_pool,
+                 int num_blocks, int num_kv_heads, int head_dim, int block_size,
+                 int src_dtype, int kv_dtype, float k_scale, float v_scale, void* stream);
+
 /* Device-side check of the block-table contract. For each sequence s writes
  * errors[s] = 0 if fine, else a bit set: 1 = context length < 0, 2 = context length
  * above max_blocks_per_seq * block_size, 4 = some used entry outside [0, num_blocks),

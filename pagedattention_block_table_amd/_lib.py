@@ -35,6 +35,7 @@ SIGNATURES = {
     "pa_decode_balanced": (_I, _DECODE_ARGS + [_I, _P, _SZ, _P, _P]),
     "pa_debug_trace": (_I, _DECODE_ARGS + [_I, _I, _I, _P, _SZ, _P, _P, _P, _P, _P]),
     "pa_check_tables": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P]),
+    "pa_append_kv": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _P]),
     "pa_debug_fp8_to_f32": (_I, [_P, _P, _I, _P]),
     "pa_status_str": (ctypes.c_char_p, [_I]),
     "pa_version": (_I, []),
@@ -309,6 +310,31 @@ class DecodePlan:
         a[1] = ctypes.c_void_p(k_pool.data_ptr())
         a[2] = ctypes.c_void_p(v_pool.data_ptr())
         return functools.partial(self._fn, *a)
+
+
+def pa_append_kv(k_new, v_new, seq_ids, positions, block_tables, k_pool, v_pool,
+                 k_scale: float = 1.0, v_scale: float = 1.0, stream=None):
+    """Write new tokens' K/V rows ([T][Hkv][D], io dtype) into the paged pools in place."""
+    torch = _torch()
+    for n, t in (("k_new", k_new), ("v_new", v_new), ("seq_ids", seq_ids), ("positions", positions),
+                 ("block_tables", block_tables), ("k_pool", k_pool), ("v_pool", v_pool)):
+        _check_dev(n, t)
+    if k_new.dim() != 3 or v_new.shape != k_new.shape or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
+        raise ValueError("k_new/v_new must be [T][Hkv][D] and the pools [NB][Hkv][BS][D]")
+    if seq_ids.dtype != torch.int32 or positions.dtype != torch.int32 or block_tables.dtype != torch.int32:
+        raise ValueError("seq_ids, positions and block_tables must be int32")
+    T, Hkv, D = k_new.shape
+    NB, Hkv2, BS, D2 = k_pool.shape
+    if Hkv2 != Hkv or D2 != D or seq_ids.shape != (T,) or positions.shape != (T,):
+        raise ValueError("shapes of the new rows, ids and pools disagree")
+    S, MB = block_tables.shape
+    _raise("pa_append_kv",
+           lib().pa_append_kv(k_new.data_ptr(), v_new.data_ptr(), seq_ids.data_ptr(),
+                              positions.data_ptr(), T, block_tables.data_ptr(), S, MB,
+                              k_pool.data_ptr(), v_pool.data_ptr(), NB, Hkv, D, BS,
+                              dtype_code(k_new), dtype_code(k_pool), float(k_scale), float(v_scale),
+                              _stream(stream)))
+    return k_pool, v_pool
 
 
 def pa_check_tables(block_tables, context_lens, num_blocks: int, block_size: int,

@@ -163,3 +163,30 @@ def test_binding_refuses_cpu_tensors():
     cl = torch.ones(1, dtype=torch.int32)
     with pytest.raises(ValueError, match="GPU tensor"):
         _lib.pa_decode(q, pool, pool, bt, cl)
+
+
+def test_append_rejects():
+    L = _lib.lib()
+    good = dict(kn=FAKE, vn=FAKE, seq=FAKE, pos=FAKE, T=4, bt=FAKE, S=2, MB=3, kp=FAKE, vp=FAKE, NB=8,
+                Hkv=2, D=128, BS=16, src=_lib.PA_F16, kv=_lib.PA_F16, ks=1.0, vs=1.0)
+
+    def call(**over):
+        a = dict(good)
+        a.update(over)
+        return L.pa_append_kv(a["kn"], a["vn"], a["seq"], a["pos"], a["T"], a["bt"], a["S"], a["MB"],
+                              a["kp"], a["vp"], a["NB"], a["Hkv"], a["D"], a["BS"], a["src"], a["kv"],
+                              a["ks"], a["vs"], None)
+
+    assert call(kn=0) == _lib.PA_ERR_INVALID
+    assert call(bt=0) == _lib.PA_ERR_INVALID
+    assert call(T=-1) == _lib.PA_ERR_INVALID
+    assert call(S=0) == _lib.PA_ERR_INVALID
+    assert call(src=_lib.PA_FP8_E4M3) == _lib.PA_ERR_INVALID      # new rows come in an io dtype
+    assert call(kv=7) == _lib.PA_ERR_INVALID
+    assert call(kv=_lib.PA_BF16) == _lib.PA_ERR_UNSUPPORTED       # only copy or fp8 quantise
+    assert call(kv=_lib.PA_FP8_E4M3, ks=0.0) == _lib.PA_ERR_INVALID
+    assert call(kv=_lib.PA_FP8_E4M3, vs=float("nan")) == _lib.PA_ERR_INVALID
+    assert call(kp=FAKE + 4) == _lib.PA_ERR_INVALID
+    assert call(D=96) == _lib.PA_ERR_UNSUPPORTED
+    assert call(BS=64) == _lib.PA_ERR_UNSUPPORTED
+    assert call(T=0) == _lib.PA_OK                                 # nothing to write, nothing enqueued
