@@ -195,6 +195,55 @@ int pa_check_tables(const int32_t* block_tables, const int32_t* context_lens,
  * kernels use (for tests of the fp8 path). */
 int pa_debug_fp8_to_f32(const uint8_t* codes, float* out, int n, void* stream);
 
+/* ---------------------------------------------------------------------------------
+ * Host block manager ([P1] §2 and §5; [P3] paged-pool and prefix-caching sections): owns
+ * the physical block pool of one paged KV cache on the host and produces the block tables
+ * and slots that the kernels above consume. Host memory only, no HIP calls; one manager
+ * must not be used from several threads at once.
+ *   - Free blocks form a stack (allocation and release are O(1)); a sequence holds only
+ *     the blocks its tokens use and gets a new block when its last one is full.
+ *   - Blocks are shared by reference count (forked sequences, prefix cache hits).
+ *   - With prefix caching, every full block is indexed under (parent block, parent's
+ *     generation, its token ids); a new sequence reuses the longest chain of indexed
+ *     blocks that matches its prompt exactly. Indexed blocks whose count drops to zero
+ *     stay reusable until the free stack runs out, then the least recently released one
+ *     is evicted.
+ *   - Appending to a partly filled block that is shared copies it first: the manager
+ *     allocates the new block and reports (copy_src, copy_dst); the caller copies the
+ *     block's K/V on the device before writing the new token.
+ * Status codes as above; PA_ERR_WORKSPACE means the pool has no block to give (the
+ * manager is then unchanged). Sequence handles are small integers that are never reused.
+ * --------------------------------------------------------------------------------- */
+typedef struct pa_block_manager pa_block_manager;
+
+/* New manager over num_blocks blocks of block_size tokens; NULL on invalid sizes. */
+pa_block_manager* pa_bm_create(int num_blocks, int block_size, int enable_prefix_caching);
+void pa_bm_destroy(pa_block_manager* bm);
+/* Blocks that can still be allocated (free plus evictable cached blocks). */
+int pa_bm_num_free(const pa_block_manager* bm);
+/* Adds a sequence holding the num_tokens prompt tokens; returns its handle (>= 0).
+ * *num_cached_tokens (may be NULL) receives how many leading tokens were found in the
+ * prefix cache (their K/V need not be computed again). */
+int pa_bm_add_sequence(pa_block_manager* bm, const int32_t* token_ids, int num_tokens,
+                       int* num_cached_tokens);
+/* Appends one token; *slot = block * block_size + offset of its K/V. *copy_src and
+ * *copy_dst are -1, or the blocks to copy before writing (copy on write). */
+int pa_bm_append_token(pa_block_manager* bm, int seq, int32_t token_id, int32_t* slot,
+                       int32_t* copy_src, int32_t* copy_dst);
+/* A new sequence sharing every block of `parent` (beam search, parallel sampling). */
+int pa_bm_fork(pa_block_manager* bm, int parent);
+/* Releases a sequence's blocks. */
+int pa_bm_free_sequence(pa_block_manager* bm, int seq);
+int pa_bm_context_len(const pa_block_manager* bm, int seq);
+/* Writes the sequence's table into out[0 .. max_blocks) padded with -1; returns the number
+ * of blocks (PA_ERR_WORKSPACE if more than max_blocks). */
+int pa_bm_block_table(const pa_block_manager* bm, int seq, int32_t* out, int max_blocks);
+int pa_bm_ref_count(const pa_block_manager* bm, int block);
+/* Block tables [n][max_blocks] (-1 padded) and context lengths of n sequences, in host
+ * arrays ready to copy to the device. */
+int pa_bm_export(const pa_block_manager* bm, const int32_t* seqs, int n, int max_blocks,
+                 int32_t* block_tables, int32_t* context_lens);
+
 /* Static text for a status code. */
 const char* pa_status_str(int status);
 

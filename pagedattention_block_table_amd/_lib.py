@@ -37,6 +37,17 @@ SIGNATURES = {
     "pa_check_tables": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "pa_append_kv": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _P]),
     "pa_debug_fp8_to_f32": (_I, [_P, _P, _I, _P]),
+    "pa_bm_create": (_P, [_I, _I, _I]),
+    "pa_bm_destroy": (None, [_P]),
+    "pa_bm_num_free": (_I, [_P]),
+    "pa_bm_add_sequence": (_I, [_P, _P, _I, _P]),
+    "pa_bm_append_token": (_I, [_P, _I, ctypes.c_int32, _P, _P, _P]),
+    "pa_bm_fork": (_I, [_P, _I]),
+    "pa_bm_free_sequence": (_I, [_P, _I]),
+    "pa_bm_context_len": (_I, [_P, _I]),
+    "pa_bm_block_table": (_I, [_P, _I, _P, _I]),
+    "pa_bm_ref_count": (_I, [_P, _I]),
+    "pa_bm_export": (_I, [_P, _P, _I, _I, _P, _P]),
     "pa_status_str": (ctypes.c_char_p, [_I]),
     "pa_version": (_I, []),
 }
@@ -359,3 +370,89 @@ def pa_debug_fp8_to_f32(codes, stream=None):
     _raise("pa_debug_fp8_to_f32",
            lib().pa_debug_fp8_to_f32(codes.data_ptr(), out.data_ptr(), codes.numel(), _stream(stream)))
     return out
+
+
+class BlockManager:
+    """Host block manager of the library (pa_bm_* in include/pa.h): the physical block pool
+    of one paged cache, reference-counted sharing, optional prefix caching and copy on
+    write. Methods raise PagedAttentionError on a failing status (PA_ERR_WORKSPACE when the
+    pool has no block to give)."""
+
+    def __init__(self, num_blocks: int, block_size: int, prefix_caching: bool = False):
+        self._L = lib()
+        self._h = self._L.pa_bm_create(int(num_blocks), int(block_size), int(bool(prefix_caching)))
+        if not self._h:
+            raise ValueError("invalid block manager sizes")
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._L.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    @property
+    def num_free(self) -> int:
+        return int(self._L.pa_bm_num_free(self._h))
+
+    def add_sequence(self, token_ids):
+        """Returns (handle, number of prompt tokens found in the prefix cache)."""
+        import numpy as np
+        toks = np.ascontiguousarray(token_ids, dtype=np.int32)
+        cached = ctypes.c_int(0)
+        rc = self._L.pa_bm_add_sequence(self._h, toks.ctypes.data if toks.size else None, toks.size,
+                                        ctypes.byref(cached))
+        if rc < 0:
+            raise PagedAttentionError("pa_bm_add_sequence", rc)
+        return rc, cached.value
+
+    def append_token(self, seq: int, token_id: int):
+        """Returns (slot, copy_src, copy_dst); copy_* are -1 unless a shared block was copied."""
+        slot, src, dst = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _raise("pa_bm_append_token", self._L.pa_bm_append_token(self._h, int(seq), int(token_id),
+                                                                 ctypes.byref(slot), ctypes.byref(src),
+                                                                 ctypes.byref(dst)))
+        return slot.value, src.value, dst.value
+
+    def fork(self, seq: int) -> int:
+        rc = self._L.pa_bm_fork(self._h, int(seq))
+        if rc < 0:
+            raise PagedAttentionError("pa_bm_fork", rc)
+        return rc
+
+    def free_sequence(self, seq: int):
+        _raise("pa_bm_free_sequence", self._L.pa_bm_free_sequence(self._h, int(seq)))
+
+    def context_len(self, seq: int) -> int:
+        rc = self._L.pa_bm_context_len(self._h, int(seq))
+        if rc < 0:
+            raise PagedAttentionError("pa_bm_context_len", rc)
+        return rc
+
+    def block_table(self, seq: int):
+        n = self.context_len(seq)
+        cap = max(1, (n + self.block_size - 1) // self.block_size)
+        out = (ctypes.c_int32 * cap)()
+        rc = self._L.pa_bm_block_table(self._h, int(seq), out, cap)
+        if rc < 0:
+            raise PagedAttentionError("pa_bm_block_table", rc)
+        return list(out[:rc])
+
+    def ref_count(self, block: int) -> int:
+        rc = self._L.pa_bm_ref_count(self._h, int(block))
+        if rc < 0:
+            raise PagedAttentionError("pa_bm_ref_count", rc)
+        return rc
+
+    def export(self, seqs, max_blocks: int):
+        """(block_tables int32 [n][max_blocks] padded with -1, context_lens int32 [n])."""
+        import numpy as np
+        ids = np.ascontiguousarray(seqs, dtype=np.int32)
+        tables = np.empty((ids.size, max_blocks), dtype=np.int32)
+        lens = np.empty(ids.size, dtype=np.int32)
+        _raise("pa_bm_export", self._L.pa_bm_export(self._h, ids.ctypes.data, ids.size, int(max_blocks),
+                                                     tables.ctypes.data, lens.ctypes.data))
+        return tables, lens

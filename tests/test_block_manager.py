@@ -1,0 +1,258 @@
+"""The host block manager (C++, pa_bm_* in include/pa.h) against its plain Python model
+(oracle/block_manager_model.py) and against the behaviour the pages describe. CPU only."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+from oracle.block_manager_model import ERR_INVALID, ERR_NO_BLOCK, OK, BlockManagerModel
+from pagedattention_block_table_amd import _lib
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libpa.so not built")
+
+
+class Lib:
+    """The C++ manager with the model's return conventions (status codes, no exceptions)."""
+
+    def __init__(self, nb, bs, pc=False):
+        self.L = _lib.lib()
+        self.h = self.L.pa_bm_create(nb, bs, int(pc))
+        self.nb, self.bs = nb, bs
+
+    def __del__(self):
+        self.L.pa_bm_destroy(self.h)
+
+    def available(self):
+        return self.L.pa_bm_num_free(self.h)
+
+    def add_sequence(self, tokens):
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        c = ctypes.c_int(0)
+        rc = self.L.pa_bm_add_sequence(self.h, t.ctypes.data if t.size else None, t.size, ctypes.byref(c))
+        return rc, (c.value if rc >= 0 else 0)
+
+    def append_token(self, s, token):
+        slot, src, dst = ctypes.c_int32(-1), ctypes.c_int32(-1), ctypes.c_int32(-1)
+        rc = self.L.pa_bm_append_token(self.h, s, token, ctypes.byref(slot), ctypes.byref(src), ctypes.byref(dst))
+        return (rc, slot.value, src.value, dst.value) if rc == 0 else (rc, -1, -1, -1)
+
+    def fork(self, s):
+        return self.L.pa_bm_fork(self.h, s)
+
+    def free_sequence(self, s):
+        return self.L.pa_bm_free_sequence(self.h, s)
+
+    def block_table(self, s):
+        n = self.L.pa_bm_context_len(self.h, s)
+        cap = max(1, (n + self.bs - 1) // self.bs)
+        out = (ctypes.c_int32 * cap)()
+        k = self.L.pa_bm_block_table(self.h, s, out, cap)
+        return list(out[:k])
+
+    def context_len(self, s):
+        return self.L.pa_bm_context_len(self.h, s)
+
+    def ref_count(self, b):
+        return self.L.pa_bm_ref_count(self.h, b)
+
+
+IMPLS = {"cpp": lambda nb, bs, pc: Lib(nb, bs, pc), "model": lambda nb, bs, pc: BlockManagerModel(nb, bs, pc)}
+
+
+def _ref(impl, b):
+    return impl.ref_count(b) if isinstance(impl, Lib) else impl.ref[b]
+
+
+def _live(impl, handles):
+    return [h for h in handles if impl.context_len(h) >= 0] if isinstance(impl, Lib) else \
+        [h for h in handles if impl.seqs[h] is not None]
+
+
+def check_invariants(impl, handles, nb, bs):
+    """Reference count = number of live tables holding the block; every block is either
+    referenced or allocatable; tables cover exactly ceil(len / bs) blocks, no duplicates."""
+    live = _live(impl, handles)
+    count = [0] * nb
+    for h in live:
+        t = impl.block_table(h)
+        n = impl.context_len(h)
+        assert len(t) == (n + bs - 1) // bs
+        assert len(set(t)) == len(t)
+        for b in t:
+            count[b] += 1
+    for b in range(nb):
+        assert _ref(impl, b) == count[b], (b, _ref(impl, b), count[b])
+    referenced = sum(1 for c in count if c > 0)
+    assert referenced + impl.available() == nb
+
+
+# ----------------------------------------------------------------------------------
+# the pages' behaviour, pinned on both implementations
+# ----------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("impl", sorted(IMPLS))
+def test_on_demand_allocation_and_release(impl):
+    """[P3]: a request holds only the blocks it uses, gets a new block when its last one is
+    full, and returns them to the pool when it ends; the freed block is handed out next."""
+    m = IMPLS[impl](8, 4, False)
+    s, _ = m.add_sequence(list(range(5)))          # 5 tokens -> 2 blocks
+    assert m.block_table(s) == [0, 1] and m.available() == 6
+    for t in range(3):                              # fill block 1
+        rc, slot, src, dst = m.append_token(s, 100 + t)
+        assert rc == OK and slot == 1 * 4 + 1 + t and (src, dst) == (-1, -1)
+    rc, slot, _, _ = m.append_token(s, 200)         # position 8 starts block 2
+    assert rc == OK and m.block_table(s) == [0, 1, 2] and slot == 8
+    s2, _ = m.add_sequence([7])
+    assert m.block_table(s2) == [3]
+    assert m.free_sequence(s) == OK and m.available() == 7
+    s3, _ = m.add_sequence([1, 2])                  # most recently freed block first
+    assert m.block_table(s3) == [0]
+    check_invariants(m, [s, s2, s3], 8, 4)
+
+
+@pytest.mark.parametrize("impl", sorted(IMPLS))
+def test_shared_system_prompt_prefix(impl):
+    """[P3] prefix caching: 64 requests with the same 500-token system prompt, block size
+    16, share its 31 full blocks; the partial 32nd block and the rest are private."""
+    m = IMPLS[impl](64 * 40, 16, True)
+    rng = np.random.default_rng(0)
+    prompt = rng.integers(0, 32000, 500).tolist()
+    handles, cached = [], []
+    for r in range(64):
+        history = rng.integers(0, 32000, 500).tolist()
+        h, c = m.add_sequence(prompt + history)
+        handles.append(h)
+        cached.append(c)
+    assert cached == [0] + [496] * 63
+    t0 = m.block_table(handles[0])
+    for h in handles[1:]:
+        t = m.block_table(h)
+        assert t[:31] == t0[:31] and len(set(t[31:]) & set(t0)) == 0
+    assert [_ref(m, b) for b in t0[:31]] == [64] * 31
+    assert _ref(m, t0[31]) == 1
+    check_invariants(m, handles, 64 * 40, 16)
+
+
+@pytest.mark.parametrize("impl", sorted(IMPLS))
+def test_prefix_must_match_exactly(impl):
+    """[P3]: the cache hits only for an identical prefix; one different token in a block
+    stops the reuse from that block on."""
+    m = IMPLS[impl](64, 4, True)
+    a, _ = m.add_sequence(list(range(12)))
+    b, cb = m.add_sequence([0, 1, 2, 3, 4, 5, 99, 7, 8, 9, 10, 11])
+    assert cb == 4
+    assert m.block_table(b)[0] == m.block_table(a)[0]
+    assert m.block_table(b)[1] != m.block_table(a)[1]
+    assert m.block_table(b)[2] != m.block_table(a)[2]
+
+
+@pytest.mark.parametrize("impl", sorted(IMPLS))
+def test_beam_fork_copy_on_write(impl):
+    """[P1] §5: beam candidates share the parent's blocks; writing into the shared, partly
+    filled last block first gives the writer its own copy, full blocks stay shared."""
+    m = IMPLS[impl](16, 4, False)
+    p, _ = m.add_sequence(list(range(6)))           # blocks [0, 1], block 1 half full
+    c = m.fork(p)
+    assert m.block_table(c) == [0, 1] and _ref(m, 0) == 2 and _ref(m, 1) == 2
+    rc, slot, src, dst = m.append_token(c, 42)
+    assert rc == OK and (src, dst) == (1, 2) and slot == 2 * 4 + 2
+    assert m.block_table(c) == [0, 2] and m.block_table(p) == [0, 1]
+    assert _ref(m, 1) == 1 and _ref(m, 2) == 1 and _ref(m, 0) == 2
+    rc, slot, src, dst = m.append_token(p, 43)     # the parent's block is no longer shared
+    assert rc == OK and (src, dst) == (-1, -1) and slot == 1 * 4 + 2
+    check_invariants(m, [p, c], 16, 4)
+
+
+@pytest.mark.parametrize("impl", sorted(IMPLS))
+def test_eviction_of_cached_blocks(impl):
+    """Released prefix blocks stay reusable until the pool runs out; then the least
+    recently released one is reused for new data and no longer matches its old prefix."""
+    m = IMPLS[impl](6, 2, True)
+    a, _ = m.add_sequence([1, 2, 3, 4, 5, 6])      # blocks 0, 1, 2, all full and indexed
+    assert m.free_sequence(a) == OK and m.available() == 6
+    b, cb = m.add_sequence([1, 2, 3, 4])           # hits blocks 0 and 1
+    assert cb == 4 and m.block_table(b) == [0, 1]
+    m.free_sequence(b)                              # released child first: queue 2, 1, 0
+    c, cc = m.add_sequence([9, 9, 8, 8, 7, 7, 6, 6, 5, 5])
+    assert cc == 0 and m.block_table(c) == [3, 4, 5, 2, 1] and m.available() == 1
+    d, cd = m.add_sequence([1, 2])                 # block 0 survived the eviction
+    assert cd == 2 and m.block_table(d) == [0] and m.available() == 0
+    assert m.add_sequence([1, 2, 3, 4])[0] == ERR_NO_BLOCK   # block 1 now holds other data
+    m.free_sequence(c)
+    e, ce = m.add_sequence([1, 2, 3, 4])
+    assert ce == 2 and m.block_table(e) == [0, 1]
+    check_invariants(m, [a, b, c, d, e], 6, 2)
+
+
+@pytest.mark.parametrize("impl", sorted(IMPLS))
+def test_out_of_blocks_leaves_state_unchanged(impl):
+    m = IMPLS[impl](3, 4, False)
+    a, _ = m.add_sequence(list(range(8)))
+    rc, _ = m.add_sequence(list(range(9)))
+    assert rc == ERR_NO_BLOCK and m.available() == 1
+    b, _ = m.add_sequence([1])
+    for t in range(3):
+        assert m.append_token(b, t)[0] == OK
+    assert m.append_token(b, 9)[0] == ERR_NO_BLOCK
+    assert m.context_len(b) == 4 and m.block_table(b) == [2]
+    assert m.append_token(1234, 0)[0] == ERR_INVALID
+    check_invariants(m, [a, b], 3, 4)
+
+
+# ----------------------------------------------------------------------------------
+# differential: random operation sequences on the C++ manager and the model
+# ----------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed,nb,bs,pc", [(1, 64, 4, False), (2, 64, 4, True), (3, 20, 2, True),
+                                           (4, 200, 16, True), (5, 12, 8, False), (6, 30, 4, True)])
+def test_random_operations_match_model(seed, nb, bs, pc):
+    rng = np.random.default_rng(seed)
+    cpp, mod = Lib(nb, bs, pc), BlockManagerModel(nb, bs, pc)
+    handles = []
+    prompts = [rng.integers(0, 5, rng.integers(0, 3 * bs)).tolist() for _ in range(4)]
+    for step in range(600):
+        op = rng.choice(["add", "append", "append", "append", "fork", "free"], p=[0.15, 0.2, 0.2, 0.2, 0.1, 0.15])
+        live = _live(mod, handles)
+        if op == "add" or not live:
+            base = prompts[rng.integers(0, len(prompts))]
+            toks = base + rng.integers(0, 5, rng.integers(0, 2 * bs)).tolist()
+            r1, r2 = cpp.add_sequence(toks), mod.add_sequence(toks)
+            assert r1 == r2, (step, op, r1, r2)
+            if r1[0] >= 0:
+                handles.append(r1[0])
+        elif op == "append":
+            s = int(rng.choice(live))
+            tok = int(rng.integers(0, 5))
+            assert cpp.append_token(s, tok) == mod.append_token(s, tok), (step, op)
+        elif op == "fork":
+            s = int(rng.choice(live))
+            r1, r2 = cpp.fork(s), mod.fork(s)
+            assert r1 == r2
+            handles.append(r1)
+        else:
+            s = int(rng.choice(live))
+            assert cpp.free_sequence(s) == mod.free_sequence(s) == OK
+        assert cpp.available() == mod.available()
+        if step % 25 == 0:
+            for h in _live(mod, handles):
+                assert cpp.block_table(h) == mod.block_table(h)
+                assert cpp.context_len(h) == mod.context_len(h)
+            check_invariants(cpp, handles, nb, bs)
+            check_invariants(mod, handles, nb, bs)
+
+
+def test_binding_export_and_errors():
+    bm = _lib.BlockManager(10, 4, prefix_caching=True)
+    a, _ = bm.add_sequence(list(range(9)))
+    b, cached = bm.add_sequence(list(range(8)) + [50])
+    assert cached == 8
+    tables, lens = bm.export([a, b], 4)
+    assert tables.tolist() == [[0, 1, 2, -1], [0, 1, 3, -1]] and lens.tolist() == [9, 9]
+    with pytest.raises(_lib.PagedAttentionError):
+        bm.export([a, b], 2)
+    with pytest.raises(_lib.PagedAttentionError):
+        bm.append_token(77, 1)
+    with pytest.raises(ValueError):
+        _lib.BlockManager(0, 16)
+    bm.close()
