@@ -183,6 +183,22 @@ int pa_append_kv(const void* k_new, const void* v_new, const int32_t* seq_ids,
                  int num_blocks, int num_kv_heads, int head_dim, int block_size,
                  int src_dtype, int kv_dtype, float k_scale, float v_scale, void* stream);
 
+/* Copies whole physical blocks for copy-on-write ([P3] paged pool: sequences of a parallel
+ * sample or a beam share physical blocks by reference count; [P1] §5 beam search). The
+ * pages share blocks but do not say what happens when one sharer writes into a shared,
+ * partly filled block; the plainest reading, and what pa_bm_append_token reports, is
+ * that the writer first gets a private copy. For each i < num_pairs, with
+ * src = block_pairs[2i] and dst = block_pairs[2i + 1] (device int32 array):
+ *   k_pool[dst][:][:][:] = k_pool[src][:][:][:]   and the same for v_pool
+ * (layout [num_blocks][num_kv_heads][block_size][head_dim], kv_dtype elements; every byte
+ * of the block is copied, whatever its fill). Pairs run in parallel: no dst may be the src
+ * or the dst of another pair. Pairs with an id outside [0, num_blocks) or src == dst are
+ * skipped. Pools must be 16-byte aligned and a block's bytes a multiple of 16.
+ * num_pairs == 0 is a no-op. Asynchronous on `stream`; allocates nothing. */
+int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_pairs, int num_pairs,
+                   int num_blocks, int num_kv_heads, int head_dim, int block_size,
+                   int kv_dtype, void* stream);
+
 /* Device-side check of the block-table contract. For each sequence s writes
  * errors[s] = 0 if fine, else a bit set: 1 = context length < 0, 2 = context length
  * above max_blocks_per_seq * block_size, 4 = some used entry outside [0, num_blocks),
@@ -206,8 +222,12 @@ int pa_debug_fp8_to_f32(const uint8_t* codes, float* out, int n, void* stream);
  *   - With prefix caching, every full block is indexed under (parent block, parent's
  *     generation, its token ids); a new sequence reuses the longest chain of indexed
  *     blocks that matches its prompt exactly. Indexed blocks whose count drops to zero
- *     stay reusable until the free stack runs out, then the least recently released one
- *     is evicted.
+ *     stay reusable until the free stack runs out; then one is evicted by LRU-K ([P2]
+ *     §2.3): a logical clock advances once per add, append or fork; a block is accessed
+ *     when a sequence gains a reference to it or writes into it (once per operation); the
+ *     victim is the block whose K-th most recent access is oldest (fewer than K accesses
+ *     count as oldest), ties to the older last access, then to the block deeper in its
+ *     prefix chain, then to the lower id.
  *   - Appending to a partly filled block that is shared copies it first: the manager
  *     allocates the new block and reports (copy_src, copy_dst); the caller copies the
  *     block's K/V on the device before writing the new token.
@@ -216,8 +236,9 @@ int pa_debug_fp8_to_f32(const uint8_t* codes, float* out, int n, void* stream);
  * --------------------------------------------------------------------------------- */
 typedef struct pa_block_manager pa_block_manager;
 
-/* New manager over num_blocks blocks of block_size tokens; NULL on invalid sizes. */
-pa_block_manager* pa_bm_create(int num_blocks, int block_size, int enable_prefix_caching);
+/* New manager over num_blocks blocks of block_size tokens; lru_k in 1..4 is K of the
+ * eviction policy (0 means 2, LRU-2). NULL on invalid arguments. */
+pa_block_manager* pa_bm_create(int num_blocks, int block_size, int enable_prefix_caching, int lru_k);
 void pa_bm_destroy(pa_block_manager* bm);
 /* Blocks that can still be allocated (free plus evictable cached blocks). */
 int pa_bm_num_free(const pa_block_manager* bm);

@@ -11,11 +11,16 @@ the C++ manager and compare every result.
        identical prefix.
   [P1] "突破GPU内存瓶颈：vLLM与PagedAttention技术深度解析" §2 (block tables, shared blocks)
        and §5 (beam search candidates share blocks).
+  [P2] vLLM architecture deep-dive §2.3: with no free block, evict the block whose K-th
+       most recent access is furthest back (LRU-K, K = 2 named).
 
 Policies: free blocks are a stack (the most recently freed block is handed out first,
 initially 0, 1, 2, ...); a full block is indexed under (parent block, parent generation,
-token ids); released indexed blocks wait in a queue and are evicted oldest first when the
-stack is empty; appending to a partly filled shared block copies it first.
+token ids); released indexed blocks stay cached and, when the stack is empty, the one
+with the oldest K-th most recent access is evicted (a clock ticks once per add, append
+or fork; gaining a reference to a block or writing into it is an access, once per
+operation; fewer than K accesses = oldest; ties: older last access, then deeper in its
+chain, then lower id); appending to a partly filled shared block copies it first.
 """
 from __future__ import annotations
 
@@ -23,17 +28,34 @@ OK, ERR_INVALID, ERR_NO_BLOCK = 0, -1, -3
 
 
 class BlockManagerModel:
-    def __init__(self, num_blocks: int, block_size: int, prefix_caching: bool = False):
+    def __init__(self, num_blocks: int, block_size: int, prefix_caching: bool = False, lru_k: int = 2):
         self.nb = num_blocks
         self.bs = block_size
         self.pc = prefix_caching
+        self.k = lru_k
+        self.clock = 0
         self.ref = [0] * num_blocks
         self.gen = [0] * num_blocks
+        self.times = [[] for _ in range(num_blocks)]     # access times, most recent first
+        self.depth = [0] * num_blocks
         self.free = list(range(num_blocks - 1, -1, -1))  # top = end
-        self.evictable = []                               # oldest first
+        self.evictable = []                               # unordered
         self.key_of = {}                                  # block -> key
         self.index = {}                                   # key -> block
         self.seqs = []                                    # None once freed, else dict
+
+    def _access(self, b):
+        if not self.times[b] or self.times[b][0] != self.clock:
+            self.times[b].insert(0, self.clock)
+
+    def _victim(self):
+        def kth(b):
+            return self.times[b][self.k - 1] if len(self.times[b]) >= self.k else -1
+
+        def last(b):
+            return self.times[b][0] if self.times[b] else -1
+
+        return min(self.evictable, key=lambda b: (kth(b), last(b), -self.depth[b], b))
 
     # ---- pool ----
     def available(self) -> int:
@@ -43,12 +65,14 @@ class BlockManagerModel:
         if self.free:
             b = self.free.pop()
         elif self.evictable:
-            b = self.evictable.pop(0)
+            b = self._victim()
+            self.evictable.remove(b)
             self._unindex(b)
         else:
             raise RuntimeError("no block")
         self.ref[b] = 1
         self.gen[b] += 1
+        self._access(b)
         return b
 
     def _unindex(self, b):
@@ -80,6 +104,7 @@ class BlockManagerModel:
             return
         self.index[k] = b
         self.key_of[b] = k
+        self.depth[b] = j
 
     def _live(self, s):
         return 0 <= s < len(self.seqs) and self.seqs[s] is not None
@@ -100,11 +125,13 @@ class BlockManagerModel:
         evictable_hits = sum(1 for b in hit if b in self.evictable)
         if self.available() - evictable_hits < nblk - len(hit):
             return ERR_NO_BLOCK, 0
+        self.clock += 1
         sq = {"blocks": [], "tokens": list(tokens)}
         for b in hit:
             if b in self.evictable:
                 self.evictable.remove(b)
             self.ref[b] += 1
+            self._access(b)
             sq["blocks"].append(b)
         for _ in range(len(hit), nblk):
             sq["blocks"].append(self._take())
@@ -119,20 +146,21 @@ class BlockManagerModel:
         sq = self.seqs[s]
         pos = len(sq["tokens"])
         src = dst = -1
-        if pos % self.bs == 0:
-            if self.available() < 1:
-                return ERR_NO_BLOCK, -1, -1, -1
+        need_new = pos % self.bs == 0
+        need_copy = not need_new and self.ref[sq["blocks"][-1]] > 1
+        if (need_new or need_copy) and self.available() < 1:
+            return ERR_NO_BLOCK, -1, -1, -1
+        self.clock += 1
+        if need_new:
             sq["blocks"].append(self._take())
-        else:
+        elif need_copy:
             last = sq["blocks"][-1]
-            if self.ref[last] > 1:
-                if self.available() < 1:
-                    return ERR_NO_BLOCK, -1, -1, -1
-                fresh = self._take()
-                self._release(last)
-                sq["blocks"][-1] = fresh
-                src, dst = last, fresh
+            fresh = self._take()
+            self._release(last)
+            sq["blocks"][-1] = fresh
+            src, dst = last, fresh
         sq["tokens"].append(token)
+        self._access(sq["blocks"][-1])
         slot = sq["blocks"][-1] * self.bs + pos % self.bs
         if (pos + 1) % self.bs == 0:
             self._index_full(sq, len(sq["blocks"]) - 1)
@@ -142,8 +170,10 @@ class BlockManagerModel:
         if not self._live(parent):
             return ERR_INVALID
         p = self.seqs[parent]
+        self.clock += 1
         for b in p["blocks"]:
             self.ref[b] += 1
+            self._access(b)
         self.seqs.append({"blocks": list(p["blocks"]), "tokens": list(p["tokens"])})
         return len(self.seqs) - 1
 

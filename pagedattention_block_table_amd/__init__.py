@@ -7,12 +7,12 @@ the library; the first call does, and raises if it has not been built.
 """
 from ._lib import (PA_BF16, PA_F16, PA_F32, PA_FP8_E4M3, BlockManager, DecodePlan,  # noqa: F401
                    PagedAttentionError,
-                   balanced_workspace, pa_append_kv, pa_balanced_workspace_bytes, pa_check_tables,
+                   balanced_workspace, pa_append_kv, pa_balanced_workspace_bytes, pa_copy_blocks, pa_check_tables,
                    pa_debug_fp8_to_f32, pa_debug_trace, pa_decode, pa_decode_balanced,
                    pa_decode_partitioned, pa_partitioned_workspace_bytes, pa_status_str,
                    pa_version)
 
 __all__ = ["pa_decode", "pa_decode_partitioned", "pa_partitioned_workspace_bytes",
            "pa_decode_balanced", "pa_balanced_workspace_bytes", "balanced_workspace",
-           "pa_append_kv", "pa_debug_trace", "pa_check_tables", "pa_debug_fp8_to_f32", "pa_status_str",
+           "pa_append_kv", "pa_copy_blocks", "pa_debug_trace", "pa_check_tables", "pa_debug_fp8_to_f32", "pa_status_str",
            "pa_version", "PagedAttentionError", "DecodePlan", "BlockManager"]

@@ -36,8 +36,9 @@ SIGNATURES = {
     "pa_debug_trace": (_I, _DECODE_ARGS + [_I, _I, _I, _P, _SZ, _P, _P, _P, _P, _P]),
     "pa_check_tables": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "pa_append_kv": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _P]),
+    "pa_copy_blocks": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pa_debug_fp8_to_f32": (_I, [_P, _P, _I, _P]),
-    "pa_bm_create": (_P, [_I, _I, _I]),
+    "pa_bm_create": (_P, [_I, _I, _I, _I]),
     "pa_bm_destroy": (None, [_P]),
     "pa_bm_num_free": (_I, [_P]),
     "pa_bm_add_sequence": (_I, [_P, _P, _I, _P]),
@@ -348,6 +349,22 @@ def pa_append_kv(k_new, v_new, seq_ids, positions, block_tables, k_pool, v_pool,
     return k_pool, v_pool
 
 
+def pa_copy_blocks(k_pool, v_pool, block_pairs, stream=None):
+    """Copy-on-write block copies: block_pairs is int32 [n][2] (src, dst) on the device."""
+    torch = _torch()
+    for n, t in (("k_pool", k_pool), ("v_pool", v_pool), ("block_pairs", block_pairs)):
+        _check_dev(n, t)
+    if k_pool.dim() != 4 or v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
+        raise ValueError("pools must both be [NB][Hkv][BS][D] of one dtype")
+    if block_pairs.dtype != torch.int32 or block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be int32 [n][2]")
+    NB, Hkv, BS, D = k_pool.shape
+    _raise("pa_copy_blocks",
+           lib().pa_copy_blocks(k_pool.data_ptr(), v_pool.data_ptr(), block_pairs.data_ptr(),
+                                block_pairs.shape[0], NB, Hkv, D, BS, dtype_code(k_pool), _stream(stream)))
+    return k_pool, v_pool
+
+
 def pa_check_tables(block_tables, context_lens, num_blocks: int, block_size: int,
                     max_context_len: int = 0, stream=None):
     """Per-sequence contract violation bits (see include/pa.h)."""
@@ -378,11 +395,11 @@ class BlockManager:
     write. Methods raise PagedAttentionError on a failing status (PA_ERR_WORKSPACE when the
     pool has no block to give)."""
 
-    def __init__(self, num_blocks: int, block_size: int, prefix_caching: bool = False):
+    def __init__(self, num_blocks: int, block_size: int, prefix_caching: bool = False, lru_k: int = 2):
         self._L = lib()
-        self._h = self._L.pa_bm_create(int(num_blocks), int(block_size), int(bool(prefix_caching)))
+        self._h = self._L.pa_bm_create(int(num_blocks), int(block_size), int(bool(prefix_caching)), int(lru_k))
         if not self._h:
-            raise ValueError("invalid block manager sizes")
+            raise ValueError("invalid block manager arguments")
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
 

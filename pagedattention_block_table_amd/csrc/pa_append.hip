@@ -121,6 +121,23 @@ int launch_append_d(const AppendArgs& a, int D, int BS, hipStream_t st) {
   return PA_ERR_UNSUPPORTED;
 }
 
+// Copies whole physical blocks (all KV heads, K and V) for copy-on-write: pair i copies
+// block pairs[i][0] to block pairs[i][1]. One thread moves one 16-byte piece; pairs with
+// an id outside the pool, or with src == dst, are skipped.
+__global__ void __launch_bounds__(256) copy_blocks_kernel(char* k_pool, char* v_pool, const int32_t* pairs,
+                                                          int num_pairs, int num_blocks, int64_t pieces_per_block) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)num_pairs * pieces_per_block) return;
+  const int i = (int)(gid / pieces_per_block);
+  const int64_t piece = gid % pieces_per_block;
+  const int src = pairs[2 * i], dst = pairs[2 * i + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) return;
+  const int64_t from = ((int64_t)src * pieces_per_block + piece) * 16;
+  const int64_t to = ((int64_t)dst * pieces_per_block + piece) * 16;
+  *(uint4*)(k_pool + to) = *(const uint4*)(k_pool + from);
+  *(uint4*)(v_pool + to) = *(const uint4*)(v_pool + from);
+}
+
 }  // namespace
 }  // namespace pa
 
@@ -161,6 +178,36 @@ extern "C" int pa_append_kv(const void* k_new, const void* v_new, const int32_t*
       case PA_BF16 * 4 + PA_FP8_E4M3: return launch_append_d<kBF16, kFP8>(a, D, BS, st);
       default: return PA_ERR_UNSUPPORTED;
     }
+  } catch (...) {
+    return PA_ERR_LAUNCH;
+  }
+}
+
+extern "C" int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_pairs, int num_pairs,
+                              int num_blocks, int num_kv_heads, int head_dim, int block_size,
+                              int kv_dtype, void* stream) {
+  using namespace pa;
+  try {
+    if (!k_pool || !v_pool || (num_pairs > 0 && !block_pairs)) return PA_ERR_INVALID;
+    if (num_pairs < 0 || num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
+      return PA_ERR_INVALID;
+    int e = 0;
+    switch (kv_dtype) {
+      case PA_F32: e = 4; break;
+      case PA_F16: case PA_BF16: e = 2; break;
+      case PA_FP8_E4M3: e = 1; break;
+      default: return PA_ERR_INVALID;
+    }
+    const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * e;
+    if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+    if (((uintptr_t)k_pool | (uintptr_t)v_pool) & 15u) return PA_ERR_INVALID;
+    if (num_pairs == 0) return PA_OK;
+    const int64_t pieces = block_bytes / 16;
+    const int64_t grid = ((int64_t)num_pairs * pieces + 255) / 256;
+    if (grid > INT_MAX) return PA_ERR_INVALID;
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (char*)k_pool,
+                       (char*)v_pool, block_pairs, num_pairs, num_blocks, pieces);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
   } catch (...) {
     return PA_ERR_LAUNCH;
   }

@@ -10,6 +10,8 @@
 //        sharing by reference counting; free blocks kept in a list so that allocation and
 //        release are O(1); prefix caching keeps a global hash index over prefix blocks and
 //        reuses a block only when the prefix is exactly identical.
+//   [P2] vLLM architecture deep-dive §2.3 — when no block is free, the block whose K-th
+//        most recent access lies furthest back is evicted (LRU-K; LRU-2 named).
 //
 // Policies (where the pages leave a choice open):
 //   * Free blocks form a stack: allocation pops the most recently freed block (initially
@@ -17,17 +19,26 @@
 //   * With prefix caching, a block is indexed once it is full, under a key made of its
 //     parent block (the previous block of the sequence, -1 for the first) and its token
 //     ids; a lookup hits only if both are equal, so equal keys mean equal prefixes.
-//     An indexed block whose reference count drops to zero stays indexed and joins an
-//     evictable queue (least recently released first); it is reused on a hit, or evicted
-//     (and unindexed) when the free stack is empty.
+//     An indexed block whose reference count drops to zero stays indexed and becomes
+//     evictable; it is reused on a hit, or evicted (and unindexed) when the free stack is
+//     empty.
+//   * Eviction is LRU-K over a logical clock that advances once per add, append or fork:
+//     a block is accessed when a sequence gains a reference to it or writes a token into
+//     it (several accesses within one operation count once). The victim is the evictable
+//     block whose K-th most recent access is oldest, a block with fewer than K accesses
+//     counting as infinitely old; ties go to the older most recent access, then to the
+//     block deeper in its prefix chain (so a chain is evicted from its end), then to the
+//     lower id. There is no swap space, so nothing is written back.
 //   * Appending to a sequence whose last block is partly filled and shared (reference
 //     count > 1) first gives the sequence a private copy (copy-on-write): the manager
 //     allocates the new block and reports (source, destination) so that the caller copies
 //     the block's K/V on the device.
+#include <array>
 #include <cstdint>
 #include <cstring>
-#include <list>
 #include <new>
+#include <set>
+#include <tuple>
 #include <unordered_map>
 #include <vector>
 
@@ -70,51 +81,70 @@ struct BlockKeyHash {
   }
 };
 
+constexpr int kMaxLruK = 4;
+
+// eviction order: (K-th most recent access, most recent access, -chain depth, id), smallest
+// first; -1 stands for "never"
+using EvictKey = std::tuple<int64_t, int64_t, int32_t, int32_t>;
+
 struct Manager {
   int num_blocks;
   int block_size;
   bool prefix_caching;
+  int lru_k;
+  int64_t clock = 0;
   std::vector<int32_t> ref;          // reference count per block
   std::vector<int32_t> free_stack;   // top = back
   std::vector<char> in_free;
-  std::list<int32_t> evictable;      // indexed blocks with no reference, oldest first
-  std::vector<std::list<int32_t>::iterator> evict_pos;
+  std::set<EvictKey> evictable;      // indexed blocks with no reference
+  std::vector<EvictKey> evict_key;   // valid while in_evict
   std::vector<char> in_evict;
   std::vector<char> indexed;
   std::vector<BlockKey> key_of;      // valid when indexed
+  std::vector<int32_t> depth;        // position in its prefix chain, valid when indexed
   std::vector<uint32_t> gen;         // bumped every time a block is taken for new data
+  std::vector<std::array<int64_t, kMaxLruK>> hist;  // access times, most recent first
   std::unordered_map<BlockKey, int32_t, BlockKeyHash> index;
   std::vector<Seq> seqs;
 
-  Manager(int nb, int bs, bool pc)
-      : num_blocks(nb), block_size(bs), prefix_caching(pc), ref(nb, 0), in_free(nb, 1),
-        evict_pos(nb), in_evict(nb, 0), indexed(nb, 0), key_of(nb), gen(nb, 0) {
+  Manager(int nb, int bs, bool pc, int k)
+      : num_blocks(nb), block_size(bs), prefix_caching(pc), lru_k(k), ref(nb, 0), in_free(nb, 1),
+        evict_key(nb), in_evict(nb, 0), indexed(nb, 0), key_of(nb), depth(nb, 0), gen(nb, 0) {
+    std::array<int64_t, kMaxLruK> never;
+    never.fill(-1);
+    hist.assign(nb, never);
     free_stack.reserve(nb);
     for (int b = nb - 1; b >= 0; --b) free_stack.push_back(b);
   }
 
   int available() const { return (int)free_stack.size() + (int)evictable.size(); }
 
-  // a block for new data: the free stack first, else the oldest evictable indexed block
+  void access(int32_t b) {
+    auto& h = hist[b];
+    if (h[0] == clock) return;
+    for (int i = kMaxLruK - 1; i > 0; --i) h[i] = h[i - 1];
+    h[0] = clock;
+  }
+
+  // a block for new data: the free stack first, else the LRU-K victim among the evictable
   int32_t take() {
+    int32_t b = -1;
     if (!free_stack.empty()) {
-      const int32_t b = free_stack.back();
+      b = free_stack.back();
       free_stack.pop_back();
       in_free[b] = 0;
-      ref[b] = 1;
-      ++gen[b];
-      return b;
-    }
-    if (!evictable.empty()) {
-      const int32_t b = evictable.front();
-      evictable.pop_front();
+    } else if (!evictable.empty()) {
+      b = std::get<3>(*evictable.begin());
+      evictable.erase(evictable.begin());
       in_evict[b] = 0;
       unindex(b);
-      ref[b] = 1;
-      ++gen[b];
-      return b;
+    } else {
+      return -1;
     }
-    return -1;
+    ref[b] = 1;
+    ++gen[b];
+    access(b);
+    return b;
   }
 
   void unindex(int32_t b) {
@@ -127,7 +157,8 @@ struct Manager {
   void release(int32_t b) {
     if (--ref[b] > 0) return;
     if (prefix_caching && indexed[b]) {
-      evict_pos[b] = evictable.insert(evictable.end(), b);
+      evict_key[b] = EvictKey{hist[b][lru_k - 1], hist[b][0], -depth[b], b};
+      evictable.insert(evict_key[b]);
       in_evict[b] = 1;
     } else {
       unindex(b);
@@ -138,10 +169,11 @@ struct Manager {
 
   void acquire_cached(int32_t b) {
     if (in_evict[b]) {
-      evictable.erase(evict_pos[b]);
+      evictable.erase(evict_key[b]);
       in_evict[b] = 0;
     }
     ++ref[b];
+    access(b);
   }
 
   // index block j of sequence s once it is full
@@ -158,6 +190,7 @@ struct Manager {
     index.emplace(k, b);
     key_of[b] = std::move(k);
     indexed[b] = 1;
+    depth[b] = (int32_t)j;
   }
 
   bool valid_seq(int s) const { return s >= 0 && s < (int)seqs.size() && seqs[s].live; }
@@ -168,15 +201,16 @@ struct Manager {
 
 struct pa_block_manager {
   pa::Manager m;
-  pa_block_manager(int nb, int bs, bool pc) : m(nb, bs, pc) {}
+  pa_block_manager(int nb, int bs, bool pc, int k) : m(nb, bs, pc, k) {}
 };
 
 extern "C" {
 
-pa_block_manager* pa_bm_create(int num_blocks, int block_size, int enable_prefix_caching) {
-  if (num_blocks <= 0 || block_size <= 0) return nullptr;
+pa_block_manager* pa_bm_create(int num_blocks, int block_size, int enable_prefix_caching, int lru_k) {
+  if (lru_k == 0) lru_k = 2;
+  if (num_blocks <= 0 || block_size <= 0 || lru_k < 1 || lru_k > pa::kMaxLruK) return nullptr;
   try {
-    return new pa_block_manager(num_blocks, block_size, enable_prefix_caching != 0);
+    return new pa_block_manager(num_blocks, block_size, enable_prefix_caching != 0, lru_k);
   } catch (...) {
     return nullptr;
   }
@@ -215,6 +249,7 @@ int pa_bm_add_sequence(pa_block_manager* bm, const int32_t* token_ids, int num_t
     int evictable_hits = 0;
     for (int32_t b : hit) evictable_hits += m.in_evict[b] ? 1 : 0;
     if (m.available() - evictable_hits < nblk - (int)hit.size()) return PA_ERR_WORKSPACE;
+    ++m.clock;
     pa::Seq sq;
     sq.live = true;
     sq.tokens.assign(token_ids, token_ids + num_tokens);
@@ -243,15 +278,17 @@ int pa_bm_append_token(pa_block_manager* bm, int seq, int32_t token_id, int32_t*
     const int64_t pos = (int64_t)sq.tokens.size();
     *copy_src = -1;
     *copy_dst = -1;
-    if (pos % BS == 0) {
-      // the last block is full (or there is none): a new block
-      if (m.available() < 1) return PA_ERR_WORKSPACE;
+    // a new block when the last one is full (or there is none), a private copy when it is
+    // partly filled and shared
+    const bool fresh_block = pos % BS == 0;
+    const bool cow = !fresh_block && m.ref[sq.blocks.back()] > 1;
+    if ((fresh_block || cow) && m.available() < 1) return PA_ERR_WORKSPACE;
+    ++m.clock;
+    if (fresh_block) {
       sq.blocks.push_back(m.take());
     } else {
       const int32_t last = sq.blocks.back();
-      if (m.ref[last] > 1) {
-        // shared, partly filled: copy on write
-        if (m.available() < 1) return PA_ERR_WORKSPACE;
+      if (cow) {
         const int32_t fresh = m.take();
         m.release(last);
         sq.blocks.back() = fresh;
@@ -260,6 +297,7 @@ int pa_bm_append_token(pa_block_manager* bm, int seq, int32_t token_id, int32_t*
       }
     }
     sq.tokens.push_back(token_id);
+    m.access(sq.blocks.back());
     *slot = sq.blocks.back() * BS + (int32_t)(pos % BS);
     if ((pos + 1) % BS == 0) m.index_full_block(sq, sq.blocks.size() - 1);
     return PA_OK;
@@ -274,7 +312,11 @@ int pa_bm_fork(pa_block_manager* bm, int parent) {
     pa::Manager& m = bm->m;
     if (!m.valid_seq(parent)) return PA_ERR_INVALID;
     pa::Seq child = m.seqs[parent];
-    for (int32_t b : child.blocks) ++m.ref[b];
+    ++m.clock;
+    for (int32_t b : child.blocks) {
+      ++m.ref[b];
+      m.access(b);
+    }
     m.seqs.push_back(std::move(child));
     return (int)m.seqs.size() - 1;
   } catch (...) {

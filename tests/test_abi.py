@@ -190,3 +190,23 @@ def test_append_rejects():
     assert call(D=96) == _lib.PA_ERR_UNSUPPORTED
     assert call(BS=64) == _lib.PA_ERR_UNSUPPORTED
     assert call(T=0) == _lib.PA_OK                                 # nothing to write, nothing enqueued
+
+
+def test_copy_blocks_rejects():
+    L = _lib.lib()
+    good = dict(kp=FAKE, vp=FAKE, pairs=FAKE, n=3, NB=8, Hkv=2, D=128, BS=16, kv=_lib.PA_F16)
+
+    def call(**over):
+        a = dict(good)
+        a.update(over)
+        return L.pa_copy_blocks(a["kp"], a["vp"], a["pairs"], a["n"], a["NB"], a["Hkv"], a["D"], a["BS"],
+                                a["kv"], None)
+
+    assert call(kp=0) == _lib.PA_ERR_INVALID
+    assert call(pairs=0) == _lib.PA_ERR_INVALID
+    assert call(n=-1) == _lib.PA_ERR_INVALID
+    assert call(NB=0) == _lib.PA_ERR_INVALID
+    assert call(kv=9) == _lib.PA_ERR_INVALID
+    assert call(vp=FAKE + 8) == _lib.PA_ERR_INVALID
+    assert call(Hkv=1, D=3, BS=1, kv=_lib.PA_FP8_E4M3) == _lib.PA_ERR_UNSUPPORTED  # 3-byte blocks
+    assert call(n=0, pairs=0) == _lib.PA_OK                        # nothing to copy, nothing enqueued

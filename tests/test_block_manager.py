@@ -15,9 +15,9 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libpa
 class Lib:
     """The C++ manager with the model's return conventions (status codes, no exceptions)."""
 
-    def __init__(self, nb, bs, pc=False):
+    def __init__(self, nb, bs, pc=False, k=2):
         self.L = _lib.lib()
-        self.h = self.L.pa_bm_create(nb, bs, int(pc))
+        self.h = self.L.pa_bm_create(nb, bs, int(pc), k)
         self.nb, self.bs = nb, bs
 
     def __del__(self):
@@ -57,7 +57,8 @@ class Lib:
         return self.L.pa_bm_ref_count(self.h, b)
 
 
-IMPLS = {"cpp": lambda nb, bs, pc: Lib(nb, bs, pc), "model": lambda nb, bs, pc: BlockManagerModel(nb, bs, pc)}
+IMPLS = {"cpp": lambda nb, bs, pc, k=2: Lib(nb, bs, pc, k),
+         "model": lambda nb, bs, pc, k=2: BlockManagerModel(nb, bs, pc, k)}
 
 
 def _ref(impl, b):
@@ -166,8 +167,8 @@ def test_beam_fork_copy_on_write(impl):
 
 @pytest.mark.parametrize("impl", sorted(IMPLS))
 def test_eviction_of_cached_blocks(impl):
-    """Released prefix blocks stay reusable until the pool runs out; then the least
-    recently released one is reused for new data and no longer matches its old prefix."""
+    """Released prefix blocks stay reusable until the pool runs out; then the LRU-2
+    victim is reused for new data and no longer matches its old prefix."""
     m = IMPLS[impl](6, 2, True)
     a, _ = m.add_sequence([1, 2, 3, 4, 5, 6])      # blocks 0, 1, 2, all full and indexed
     assert m.free_sequence(a) == OK and m.available() == 6
@@ -179,10 +180,32 @@ def test_eviction_of_cached_blocks(impl):
     d, cd = m.add_sequence([1, 2])                 # block 0 survived the eviction
     assert cd == 2 and m.block_table(d) == [0] and m.available() == 0
     assert m.add_sequence([1, 2, 3, 4])[0] == ERR_NO_BLOCK   # block 1 now holds other data
-    m.free_sequence(c)
-    e, ce = m.add_sequence([1, 2, 3, 4])
-    assert ce == 2 and m.block_table(e) == [0, 1]
+    m.free_sequence(c)                              # 1 and 2 were accessed twice, 3, 4, 5 once
+    e, ce = m.add_sequence([1, 2, 3, 4])           # LRU-2: the end of c's chain goes first
+    assert ce == 2 and m.block_table(e) == [0, 5]
     check_invariants(m, [a, b, c, d, e], 6, 2)
+
+
+@pytest.mark.parametrize("impl", sorted(IMPLS))
+@pytest.mark.parametrize("k", [1, 2])
+def test_lru_k_keeps_a_reused_prefix(impl, k):
+    """[P2] §2.3 LRU-K: a prefix block reused twice outlives a block used once more
+    recently under K = 2 (its second most recent access is older than never); plain LRU
+    (K = 1) evicts the older one instead."""
+    m = IMPLS[impl](4, 2, True, k)
+    a, _ = m.add_sequence([1, 2])            # block 0, accessed at clock 1
+    m.free_sequence(a)
+    b, cb = m.add_sequence([1, 2])           # hit: block 0 accessed again at clock 2
+    assert cb == 2 and m.block_table(b) == [0]
+    m.free_sequence(b)
+    c, _ = m.add_sequence([3, 4])            # block 1, accessed once at clock 3
+    m.free_sequence(c)
+    d, _ = m.add_sequence([5, 6, 7, 8])      # blocks 2, 3: the free stack is now empty
+    e, _ = m.add_sequence([9, 9])            # must evict block 0 or block 1
+    assert m.block_table(e) == ([1] if k == 2 else [0])
+    f, cf = m.add_sequence([1, 2]) if k == 2 else m.add_sequence([3, 4])
+    assert cf == 2                           # the survivor is still a cache hit
+    check_invariants(m, [a, b, c, d, e, f], 4, 2)
 
 
 @pytest.mark.parametrize("impl", sorted(IMPLS))
@@ -204,11 +227,12 @@ def test_out_of_blocks_leaves_state_unchanged(impl):
 # differential: random operation sequences on the C++ manager and the model
 # ----------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("seed,nb,bs,pc", [(1, 64, 4, False), (2, 64, 4, True), (3, 20, 2, True),
-                                           (4, 200, 16, True), (5, 12, 8, False), (6, 30, 4, True)])
-def test_random_operations_match_model(seed, nb, bs, pc):
+@pytest.mark.parametrize("seed,nb,bs,pc,k", [(1, 64, 4, False, 2), (2, 64, 4, True, 2), (3, 20, 2, True, 2),
+                                             (4, 200, 16, True, 2), (5, 12, 8, False, 1), (6, 30, 4, True, 1),
+                                             (7, 24, 2, True, 3), (8, 40, 4, True, 4)])
+def test_random_operations_match_model(seed, nb, bs, pc, k):
     rng = np.random.default_rng(seed)
-    cpp, mod = Lib(nb, bs, pc), BlockManagerModel(nb, bs, pc)
+    cpp, mod = Lib(nb, bs, pc, k), BlockManagerModel(nb, bs, pc, k)
     handles = []
     prompts = [rng.integers(0, 5, rng.integers(0, 3 * bs)).tolist() for _ in range(4)]
     for step in range(600):
@@ -255,4 +279,6 @@ def test_binding_export_and_errors():
         bm.append_token(77, 1)
     with pytest.raises(ValueError):
         _lib.BlockManager(0, 16)
+    with pytest.raises(ValueError):
+        _lib.BlockManager(8, 16, lru_k=5)
     bm.close()
