@@ -29,7 +29,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 METRIC = "paged-attn decode KV GB/s read and % of MI355X HBM peak; seqs·tokens/s"
-DEFAULT_MODE = {0: "direct", 1: "direct", 2: "direct", 3: "balanced", 4: "balanced"}
+DEFAULT_MODE = {0: "direct", 1: "direct", 2: "direct", 3: "balanced", 4: "balanced",
+                "llama7b_fp16_bs128": "direct", "shared_prefix_bf16_bs256": "direct",
+                "long_ctx_fp16_bs512": "balanced", "mixed_fp8_bs256": "balanced"}
 KERNEL_SOURCES = ["pagedattention_block_table_amd/csrc/pa_decode_impl.h",
                   "pagedattention_block_table_amd/csrc/pa_mfma_decode.h",
                   "pagedattention_block_table_amd/csrc/pa_api.hip"]
@@ -111,6 +113,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--workload", default="",
+                    help="a named variant of a config (larger blocks), instead of --config")
     ap.add_argument("--mode", default="auto", choices=["auto", "direct", "partitioned", "balanced"])
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--workgroups", type=int, default=0,
@@ -138,10 +142,10 @@ def main():
         sys.exit(3)
     pa._lib.lib()  # fail loudly if the HIP library is missing
 
-    cfg = args.config
+    cfg = args.workload or args.config
     mode = DEFAULT_MODE[cfg] if args.mode == "auto" else args.mode
     t0 = time.time()
-    b = W.make_batch(cfg)
+    b = W.make_batch(W.VARIANTS[cfg] if args.workload else cfg)
     sp = b.spec
     log(f"[bench] workload {sp.name}: S={sp.num_seqs} H={sp.num_heads} Hkv={sp.num_kv_heads} "
         f"D={sp.head_dim} BS={sp.block_size} kv={sp.kv_dtype} sumL={int(b.context_lens.sum())} "

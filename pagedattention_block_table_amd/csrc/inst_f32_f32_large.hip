@@ -1,0 +1,7 @@
+// Decode kernel instances for io dtype f32 with KV dtype f32 (all head_dim / group
+// combinations, block sizes 64 .. 512), compiled as a translation unit of their own.
+#include "pa_decode_impl.h"
+
+namespace pa {
+int launch_f32_f32_large(const LaunchSpec& ls) { return launch_decode<kF32, kF32, true>(ls); }
+}  // namespace pa

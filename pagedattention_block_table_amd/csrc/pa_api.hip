@@ -153,26 +153,28 @@ int validate(const Common& c) {
   if ((int64_t)c.MB * c.BS > INT_MAX / 2) return PA_ERR_INVALID;
   if (c.kv != c.io && c.kv != PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
   if (c.D != 64 && c.D != 128) return PA_ERR_UNSUPPORTED;
-  if (c.BS != 8 && c.BS != 16 && c.BS != 32) return PA_ERR_UNSUPPORTED;
+  if (c.BS != 8 && c.BS != 16 && c.BS != 32 && c.BS != 64 && c.BS != 128 && c.BS != 256 && c.BS != 512)
+    return PA_ERR_UNSUPPORTED;
   if (!is_pow_group(c.H / c.Hkv)) return PA_ERR_UNSUPPORTED;
   const int lpt = c.D * elem_bytes(c.kv) / 16;
   const int tpl = 64 / lpt;
-  if (c.BS % tpl != 0) return PA_ERR_UNSUPPORTED;
+  if ((c.BS < 32 ? c.BS : 32) % tpl != 0) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
 
 int launch_pair(int io, int kv, const LaunchSpec& ls) {
+  const bool large = ls.block_size > 32;
   if (kv == PA_FP8_E4M3) {
     switch (io) {
-      case PA_F32: return launch_f32_fp8(ls);
-      case PA_F16: return launch_f16_fp8(ls);
-      case PA_BF16: return launch_bf16_fp8(ls);
+      case PA_F32: return large ? launch_f32_fp8_large(ls) : launch_f32_fp8(ls);
+      case PA_F16: return large ? launch_f16_fp8_large(ls) : launch_f16_fp8(ls);
+      case PA_BF16: return large ? launch_bf16_fp8_large(ls) : launch_bf16_fp8(ls);
     }
   } else {
     switch (io) {
-      case PA_F32: return launch_f32_f32(ls);
-      case PA_F16: return launch_f16_f16(ls);
-      case PA_BF16: return launch_bf16_bf16(ls);
+      case PA_F32: return large ? launch_f32_f32_large(ls) : launch_f32_f32(ls);
+      case PA_F16: return large ? launch_f16_f16_large(ls) : launch_f16_f16(ls);
+      case PA_BF16: return large ? launch_bf16_bf16_large(ls) : launch_bf16_bf16(ls);
     }
   }
   return PA_ERR_UNSUPPORTED;

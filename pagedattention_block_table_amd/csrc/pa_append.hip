@@ -104,6 +104,10 @@ int launch_append_bs(const AppendArgs& a, int BS, hipStream_t st) {
     case 8: hipLaunchKernelGGL((append_kernel<SRC, KV, D, 8>), dim3(grid), dim3(256), 0, st, a); break;
     case 16: hipLaunchKernelGGL((append_kernel<SRC, KV, D, 16>), dim3(grid), dim3(256), 0, st, a); break;
     case 32: hipLaunchKernelGGL((append_kernel<SRC, KV, D, 32>), dim3(grid), dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((append_kernel<SRC, KV, D, 64>), dim3(grid), dim3(256), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((append_kernel<SRC, KV, D, 128>), dim3(grid), dim3(256), 0, st, a); break;
+    case 256: hipLaunchKernelGGL((append_kernel<SRC, KV, D, 256>), dim3(grid), dim3(256), 0, st, a); break;
+    case 512: hipLaunchKernelGGL((append_kernel<SRC, KV, D, 512>), dim3(grid), dim3(256), 0, st, a); break;
     default: return PA_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
@@ -163,7 +167,9 @@ extern "C" int pa_append_kv(const void* k_new, const void* v_new, const int32_t*
     if (((uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_pool | (uintptr_t)v_pool) & 15u)
       return PA_ERR_INVALID;
     if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
-    if (block_size != 8 && block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+    if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64 && block_size != 128 &&
+        block_size != 256 && block_size != 512)
+      return PA_ERR_UNSUPPORTED;
     if (num_tokens == 0) return PA_OK;
     AppendArgs a{k_new, v_new, seq_ids, positions, block_tables, k_pool, v_pool, num_tokens,
                  num_seqs, max_blocks_per_seq, num_blocks, num_kv_heads, k_scale, v_scale};

@@ -236,16 +236,21 @@ __device__ __forceinline__ int xcd_unit(int i, int n) {
 // the decode kernel
 // ---------------------------------------------------------------------------------
 
+// Blocks larger than 32 tokens are walked as 32-token sub-blocks: sub-block j covers
+// tokens 32j .. 32j+31, lies in logical block j / SPB at row 32 (j % SPB), and is itself
+// one contiguous run of its (block, kv-head) tile.
 template <int KV, int D, int BS, int G_>
 struct Geometry {
   static constexpr int E = ElemBytes<KV>::value;
   static constexpr int VEC = 16 / E;           // elements per lane load
   static constexpr int LPT = D / VEC;          // lanes per token row
   static constexpr int TPL = 64 / LPT;         // token rows per wave load
-  static constexpr int NL = BS / TPL;          // wave loads per tile
+  static constexpr int SB = BS < 32 ? BS : 32; // tokens per (sub-)block step
+  static constexpr int SPB = BS / SB;          // sub-blocks per block
+  static constexpr int NL = SB / TPL;          // wave loads per sub-block
   static constexpr int ROW_BYTES = D * E;
   static constexpr int TILE = BS * D * E;      // bytes of one (block, kv-head) tile
-  static constexpr bool ok = (LPT >= 1) && (LPT <= 64) && (TPL >= 1) && (BS % TPL == 0);
+  static constexpr bool ok = (LPT >= 1) && (LPT <= 64) && (TPL >= 1) && (SB % TPL == 0) && (BS % SB == 0);
 };
 
 template <int G, int VEC> struct RowState {
@@ -271,7 +276,7 @@ __device__ __forceinline__ uint4 load16(const char* p) {
 #endif
 }
 
-// One chunk of U consecutive logical blocks starting at j0. TAIL: the chunk reaches past
+// One chunk of U consecutive (sub-)blocks starting at j0. TAIL: the chunk reaches past
 // the end of the unit's token range (some rows or whole blocks are invalid).
 template <int IO, int KV, int D, int BS, int G, int U, bool TAIL, bool DBG>
 __device__ __forceinline__ void process_chunk(const DecodeArgs& a, const int32_t* bt,
@@ -281,7 +286,8 @@ __device__ __forceinline__ void process_chunk(const DecodeArgs& a, const int32_t
                                               const float (&qf)[G][16 / ElemBytes<KV>::value],
                                               RowState<G, 16 / ElemBytes<KV>::value>& st) {
   using Geo = Geometry<KV, D, BS, G>;
-  constexpr int VEC = Geo::VEC, NL = Geo::NL, TPL = Geo::TPL, LPT = Geo::LPT;
+  constexpr int VEC = Geo::VEC, NL = Geo::NL, TPL = Geo::TPL, LPT = Geo::LPT, SB = Geo::SB,
+                SPB = Geo::SPB;
   const uint32_t lane_off = (uint32_t)(r * Geo::ROW_BYTES + c * 16);
 
   int bid[U];
@@ -289,7 +295,7 @@ __device__ __forceinline__ void process_chunk(const DecodeArgs& a, const int32_t
   for (int u = 0; u < U; ++u) {
     const int j = j0 + u;
     int b = 0;
-    if (!TAIL || j < j_end) b = bt[j];
+    if (!TAIL || j < j_end) b = bt[j / SPB];
     // contract: 0 <= b < num_blocks; clamp so that a bad table never reads outside the pool
     b = min(max(b, 0), a.num_blocks - 1);
     bid[u] = __builtin_amdgcn_readfirstlane(b);
@@ -299,13 +305,14 @@ __device__ __forceinline__ void process_chunk(const DecodeArgs& a, const int32_t
   uint4 vr[U][NL];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const char* kb = kbase + (int64_t)bid[u] * blk_stride;
-    const char* vb = vbase + (int64_t)bid[u] * blk_stride;
+    const int64_t sub = SPB > 1 ? (int64_t)((j0 + u) % SPB) * SB * Geo::ROW_BYTES : 0;
+    const char* kb = kbase + (int64_t)bid[u] * blk_stride + sub;
+    const char* vb = vbase + (int64_t)bid[u] * blk_stride + sub;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const uint32_t off = lane_off + (uint32_t)(i * TPL * Geo::ROW_BYTES);
       if (TAIL) {
-        const int t = (j0 + u) * BS + i * TPL + r;
+        const int t = (j0 + u) * SB + i * TPL + r;
         if (t < t_end) {
           kr[u][i] = load16(kb + off);
           vr[u][i] = load16(vb + off);
@@ -326,7 +333,7 @@ __device__ __forceinline__ void process_chunk(const DecodeArgs& a, const int32_t
     for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        const int t = (j0 + u) * BS + i * TPL + r;
+        const int t = (j0 + u) * SB + i * TPL + r;
         if (t < t_end) {
           const int64_t row = ((int64_t)s * Hkv + g) * a.dbg_max_ctx + t;
           *(uint4*)((char*)a.dbg_k + row * Geo::ROW_BYTES + c * 16) = kr[u][i];
@@ -352,7 +359,7 @@ __device__ __forceinline__ void process_chunk(const DecodeArgs& a, const int32_t
         for (int e = 0; e < VEC; ++e) acc = fmaf(qf[gi][e], kf[e], acc);
         acc = group_sum<LPT>(acc);
         if (TAIL) {
-          const int t = (j0 + u) * BS + i * TPL + r;
+          const int t = (j0 + u) * SB + i * TPL + r;
           acc = (t < t_end) ? acc : -INFINITY;
         }
         z[u][i][gi] = acc;
@@ -413,8 +420,9 @@ decode_kernel(const DecodeArgs a) {
   const int t_begin = part * a.part_tokens;
   if (part > 0 && t_begin >= L) return;  // nothing in this partition (whole workgroup)
   const int t_end = min(L, t_begin + a.part_tokens);
-  const int j_begin = t_begin / BS;
-  const int j_end = (t_end + BS - 1) / BS;
+  constexpr int SB = Geo::SB;
+  const int j_begin = t_begin / SB;
+  const int j_end = (t_end + SB - 1) / SB;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -446,7 +454,7 @@ decode_kernel(const DecodeArgs a) {
   const char* vbase = (const char*)a.v_pool + (int64_t)g * Geo::TILE;
 
   for (int j0 = j_begin + wave * U; j0 < j_end; j0 += NW * U) {
-    if ((j0 + U) * BS <= t_end) {
+    if ((j0 + U) * SB <= t_end) {
       process_chunk<IO, KV, D, BS, G, U, false, DBG>(a, bt, kbase, vbase, blk_stride, j0, j_end,
                                                      t_end, r, c, s, g, qf, st);
     } else {
@@ -540,8 +548,9 @@ struct LaunchSpec {
 
 template <int IO, int KV, int D, int BS, int G>
 constexpr int pick_unroll() {
-  // Consecutive blocks per wave iteration: about PA_CHUNK_TOKENS tokens, at least one block.
-  return BS >= PA_CHUNK_TOKENS ? 1 : PA_CHUNK_TOKENS / BS;
+  // Consecutive (sub-)blocks per wave iteration: about PA_CHUNK_TOKENS tokens, at least one.
+  constexpr int SB = Geometry<KV, D, BS, G>::SB;
+  return SB >= PA_CHUNK_TOKENS ? 1 : PA_CHUNK_TOKENS / SB;
 }
 
 template <int IO, int KV, int D, int BS, int G>
@@ -599,31 +608,49 @@ int launch_g(const LaunchSpec& ls) {
   }
 }
 
-template <int IO, int KV, int D>
+// LARGE: blocks of 64 .. 512 tokens, else 8 .. 32 (two translation units per dtype pair)
+template <int IO, int KV, int D, bool LARGE>
 int launch_bs(const LaunchSpec& ls) {
-  switch (ls.block_size) {
-    case 8: return launch_g<IO, KV, D, 8>(ls);
-    case 16: return launch_g<IO, KV, D, 16>(ls);
-    case 32: return launch_g<IO, KV, D, 32>(ls);
-    default: return PA_ERR_UNSUPPORTED;
+  if constexpr (LARGE) {
+    switch (ls.block_size) {
+      case 64: return launch_g<IO, KV, D, 64>(ls);
+      case 128: return launch_g<IO, KV, D, 128>(ls);
+      case 256: return launch_g<IO, KV, D, 256>(ls);
+      case 512: return launch_g<IO, KV, D, 512>(ls);
+      default: return PA_ERR_UNSUPPORTED;
+    }
+  } else {
+    switch (ls.block_size) {
+      case 8: return launch_g<IO, KV, D, 8>(ls);
+      case 16: return launch_g<IO, KV, D, 16>(ls);
+      case 32: return launch_g<IO, KV, D, 32>(ls);
+      default: return PA_ERR_UNSUPPORTED;
+    }
   }
 }
 
-template <int IO, int KV>
+template <int IO, int KV, bool LARGE>
 int launch_decode(const LaunchSpec& ls) {
   switch (ls.head_dim) {
-    case 64: return launch_bs<IO, KV, 64>(ls);
-    case 128: return launch_bs<IO, KV, 128>(ls);
+    case 64: return launch_bs<IO, KV, 64, LARGE>(ls);
+    case 128: return launch_bs<IO, KV, 128, LARGE>(ls);
     default: return PA_ERR_UNSUPPORTED;
   }
 }
 
-// Explicit per-pair entry points (one translation unit each, compiled in parallel).
+// Explicit per-pair entry points (one translation unit each, compiled in parallel); the
+// _large ones take block sizes 64 .. 512.
 int launch_f32_f32(const LaunchSpec&);
 int launch_f16_f16(const LaunchSpec&);
 int launch_bf16_bf16(const LaunchSpec&);
 int launch_f32_fp8(const LaunchSpec&);
 int launch_f16_fp8(const LaunchSpec&);
 int launch_bf16_fp8(const LaunchSpec&);
+int launch_f32_f32_large(const LaunchSpec&);
+int launch_f16_f16_large(const LaunchSpec&);
+int launch_bf16_bf16_large(const LaunchSpec&);
+int launch_f32_fp8_large(const LaunchSpec&);
+int launch_f16_fp8_large(const LaunchSpec&);
+int launch_bf16_fp8_large(const LaunchSpec&);
 
 }  // namespace pa

@@ -396,7 +396,7 @@ struct MfmaEngine {
   using vec = typename Mma<IO>::vec;
   using Buf = ChunkBuf<KV, D, NT>;
   static_assert(mfma_supported<IO, KV, D, G>(), "unsupported MFMA decode geometry");
-  static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+  static_assert(BS >= 8 && BS <= 512 && (BS & (BS - 1)) == 0, "block size");
   static_assert(CT % BS == 0 || BS % CT == 0, "chunks and blocks nest");
 
   LaneIds li;

@@ -100,6 +100,16 @@ CONFIGS = {
 }
 
 
+# The same workloads with the larger blocks of [P2] §3.1–§3.2 (256 by default, 128 for
+# short and 512 for long texts); pools keep the same token capacity.
+VARIANTS = {
+    "llama7b_fp16_bs128": CONFIGS[1].replace(name="llama7b_fp16_bs128", block_size=128),
+    "shared_prefix_bf16_bs256": CONFIGS[2].replace(name="shared_prefix_bf16_bs256", block_size=256),
+    "long_ctx_fp16_bs512": CONFIGS[3].replace(name="long_ctx_fp16_bs512", block_size=512, pool_blocks=512),
+    "mixed_fp8_bs256": CONFIGS[4].replace(name="mixed_fp8_bs256", block_size=256),
+}
+
+
 @dataclasses.dataclass
 class PagedBatch:
     spec: Spec

@@ -77,7 +77,8 @@ BAD = [
     (dict(k=FAKE + 8), _lib.PA_ERR_INVALID),
     (dict(kv=_lib.PA_F16), _lib.PA_ERR_UNSUPPORTED),
     (dict(D=96), _lib.PA_ERR_UNSUPPORTED),
-    (dict(BS=64), _lib.PA_ERR_UNSUPPORTED),
+    (dict(BS=48), _lib.PA_ERR_UNSUPPORTED),
+    (dict(BS=1024), _lib.PA_ERR_UNSUPPORTED),
     (dict(H=48, Hkv=3), _lib.PA_ERR_UNSUPPORTED),
     (dict(io=_lib.PA_F16, kv=_lib.PA_FP8_E4M3, D=64, BS=8), _lib.PA_ERR_UNSUPPORTED),
 ]
@@ -188,7 +189,8 @@ def test_append_rejects():
     assert call(kv=_lib.PA_FP8_E4M3, vs=float("nan")) == _lib.PA_ERR_INVALID
     assert call(kp=FAKE + 4) == _lib.PA_ERR_INVALID
     assert call(D=96) == _lib.PA_ERR_UNSUPPORTED
-    assert call(BS=64) == _lib.PA_ERR_UNSUPPORTED
+    assert call(BS=48) == _lib.PA_ERR_UNSUPPORTED
+    assert call(BS=1024) == _lib.PA_ERR_UNSUPPORTED
     assert call(T=0) == _lib.PA_OK                                 # nothing to write, nothing enqueued
 
 

@@ -68,11 +68,22 @@ def _raw(t):
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("tps", [1, 3], ids=["decode", "extend3"])
 def test_append_pools_bit_exact(cfg, tps):
-    import torch
     b = W.make_batch(W.small_variant(cfg))
+    log(f"[append] cfg={cfg} {b.spec.name} tokens/seq={tps}")
+    _append_check(b, 100 + cfg, tps)
+
+
+@pytest.mark.parametrize("cfg,BS", [(1, 64), (2, 128), (4, 256), (3, 512)])
+def test_append_large_blocks(cfg, BS):
+    b = W.repage(W.make_batch(W.small_variant(cfg), keep_logical=True), block_size=BS, seed=3)
+    log(f"[append] cfg={cfg} BS={BS}")
+    _append_check(b, 200 + cfg, 2)
+
+
+def _append_check(b, seed, tps):
+    import torch
     sp = b.spec
-    log(f"[append] cfg={cfg} {sp.name} tokens/seq={tps}")
-    k_new, v_new, seq, pos, tables = _append_case(b, 100 + cfg, tps)
+    k_new, v_new, seq, pos, tables = _append_case(b, seed, tps)
     dev = to_device(b)
     kn = _io_tensor(k_new, sp.io_dtype)
     vn = _io_tensor(v_new, sp.io_dtype)

@@ -58,17 +58,11 @@ def _raw_u8(a):
     return np.ascontiguousarray(a).view(np.uint8)
 
 
-@pytest.mark.parametrize("P,NWG", [(0, 0), (64, 0), (0, 5), (0, 13)],
-                         ids=["direct", "part64", "bal5", "bal13"])
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
-def test_trace_every_position_read_once_bit_exact(cfg, P, NWG):
-    """The instrumented kernels copy each K/V row they consume and count the reads:
-    every (sequence, KV head, position < L) is read exactly once, nothing else is read,
-    and the bytes equal the oracle's block-table gather."""
+def _trace_check(b, P, NWG):
+    """Run the instrumented kernels; every (sequence, KV head, position < L) must be read
+    exactly once, nothing else, with the bytes of the oracle's block-table gather."""
     import torch
-    b = W.make_batch(W.small_variant(cfg))
     sp = b.spec
-    log(f"[trace] cfg={cfg} P={P} NWG={NWG}")
     dev = to_device(b)
     maxL = b.max_context_len
     out, kr, vr, counts = pa.pa_debug_trace(dev["q"], dev["k_pool"], dev["v_pool"],
@@ -100,6 +94,18 @@ def test_trace_every_position_read_once_bit_exact(cfg, P, NWG):
             np.testing.assert_array_equal(_raw_u8(vr[s, g, :L]), _raw_u8(ev))
 
 
+@pytest.mark.parametrize("P,NWG", [(0, 0), (64, 0), (0, 5), (0, 13)],
+                         ids=["direct", "part64", "bal5", "bal13"])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_trace_every_position_read_once_bit_exact(cfg, P, NWG):
+    """The instrumented kernels copy each K/V row they consume and count the reads:
+    every (sequence, KV head, position < L) is read exactly once, nothing else is read,
+    and the bytes equal the oracle's block-table gather."""
+    b = W.make_batch(W.small_variant(cfg))
+    log(f"[trace] cfg={cfg} P={P} NWG={NWG}")
+    _trace_check(b, P, NWG)
+
+
 @pytest.mark.parametrize("mode,NWG", [("direct", 0), ("balanced", 6)], ids=["direct", "bal6"])
 @pytest.mark.parametrize("cfg", [0, 2, 4])
 def test_placement_blocksize_sharing_bitwise(cfg, mode, NWG):
@@ -112,7 +118,7 @@ def test_placement_blocksize_sharing_bitwise(cfg, mode, NWG):
     variants = [W.repage(b, seed=5), W.repage(b, seed=6)]
     if b.spec.shared_prefix:
         variants.append(W.repage(b, unshare=True, seed=7))
-    for bs in (8, 16, 32):
+    for bs in (8, 16, 32, 64, 128, 256, 512):
         if b.spec.kv_dtype == "fp8_e4m3" and b.spec.head_dim == 64 and bs == 8:
             continue
         variants.append(W.repage(b, block_size=bs, seed=bs))
@@ -159,6 +165,42 @@ def test_edge_shapes(io, kv, D, BS, G):
         check_against_oracle(b, got, io_rounding=True)
         zero = b.context_lens == 0
         assert (got[zero] == 0).all()
+
+
+LARGE_LENS = (0, 1, 31, 32, 33, 63, 64, 65, 255, 256, 257, 511, 512, 513, 1000, 1500)
+
+
+@pytest.mark.parametrize("io,kv", [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("bf16", "fp8_e4m3")])
+@pytest.mark.parametrize("D,BS,G", [(128, 64, 1), (64, 128, 2), (128, 256, 4), (128, 512, 8), (128, 512, 1)])
+def test_large_blocks(io, kv, D, BS, G):
+    """Blocks of 64 .. 512 tokens ([P2] §3.1: 256 by default, 128 for short and 512 for
+    long texts): lengths on and around every block and sub-block boundary, every mode."""
+    Hkv = 2
+    spec = W.Spec(f"large_{io}_{kv}_{D}_{BS}_{G}", len(LARGE_LENS), Hkv * G, Hkv, D, BS, io, kv,
+                  ("fixed", LARGE_LENS), seed=5000 + D + BS + G)
+    b = W.make_batch(spec)
+    log(f"[large] {spec.name}")
+    dev = to_device(b)
+    for mode, P in (("direct", None), ("partitioned", BS), ("partitioned", 2 * BS), ("balanced", 1),
+                    ("balanced", 5), ("balanced", 0)):
+        if mode == "balanced":
+            got = to_f64(run(b, dev, mode, num_workgroups=P))
+        else:
+            got = to_f64(run(b, dev, mode, P))
+        check_against_oracle(b, got, io_rounding=True)
+        zero = b.context_lens == 0
+        assert (got[zero] == 0).all()
+
+
+@pytest.mark.parametrize("cfg,BS", [(1, 128), (2, 256), (3, 512), (4, 256)])
+def test_large_block_trace_bit_exact(cfg, BS):
+    """At large block sizes every cached position is still read exactly once, through
+    the right physical block and row."""
+    b = W.repage(W.make_batch(W.small_variant(cfg), keep_logical=True), block_size=BS, seed=BS)
+    log(f"[large-trace] cfg={cfg} BS={BS}")
+    _trace_check(b, 0, 0)
+    _trace_check(b, 2 * BS, 0)
+    _trace_check(b, 0, 7)
 
 
 def test_length_one_returns_value_row_exactly():
