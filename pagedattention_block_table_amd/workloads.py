@@ -387,3 +387,91 @@ def small_variant(cfg: int) -> Spec:
         return base.replace(name="mixed_fp8_small", num_seqs=12,
                             lengths=("choice", (128, 1024, 2049), (0.5, 0.3, 0.2)), seed=2004)
     raise ValueError(cfg)
+
+
+# ----------------------------------------------------------------------------------
+# several new query tokens per sequence (prefill / extend over the paged cache)
+# ----------------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class ExtendBatch:
+    """A decode-style batch (pools, tables, context lengths that count the new tokens)
+    plus the new tokens' queries: sequence s owns rows query_start_loc[s] ..
+    query_start_loc[s+1]-1 of q, the last Q_s positions of its context."""
+    base: PagedBatch
+    query_start_loc: np.ndarray     # int32 [S+1]
+    q: np.ndarray                   # io storage [T][H][D]
+
+    @property
+    def query_lens(self) -> np.ndarray:
+        return np.diff(self.query_start_loc).astype(np.int32)
+
+    @property
+    def max_query_len(self) -> int:
+        ql = self.query_lens
+        return int(ql.max()) if ql.size else 0
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.query_start_loc[-1])
+
+
+def _draw_query_lens(kind: tuple, lens: np.ndarray, rng: np.random.Generator) -> np.ndarray:
+    S = lens.shape[0]
+    if kind[0] == "const":
+        Q = np.full(S, int(kind[1]), dtype=np.int64)
+    elif kind[0] == "fixed":
+        Q = np.asarray(kind[1], dtype=np.int64)
+        assert Q.shape == (S,)
+    elif kind[0] == "all":
+        Q = lens.astype(np.int64)                       # prefill of the whole context
+    elif kind[0] == "choice":
+        Q = rng.choice(np.asarray(kind[1], dtype=np.int64), size=S,
+                       p=np.asarray(kind[2], dtype=np.float64))
+    else:
+        raise ValueError(kind)
+    return np.minimum(Q, lens).astype(np.int32)
+
+
+def make_extend_batch(spec, query_lens: tuple, keep_logical: bool = False) -> ExtendBatch:
+    """Seeded extend batch: make_batch(spec) for the cache, then, from a stream of its
+    own, the query lengths (clamped to the context lengths) and the queries."""
+    base = make_batch(spec, keep_logical=keep_logical)
+    sp = base.spec
+    rng = np.random.default_rng(np.random.SeedSequence([sp.seed, 7919]))
+    Q = _draw_query_lens(query_lens, base.context_lens, rng)
+    qsl = np.zeros(Q.size + 1, dtype=np.int32)
+    np.cumsum(Q, out=qsl[1:])
+    q32 = _normal(rng, (int(qsl[-1]), sp.num_heads, sp.head_dim))
+    return ExtendBatch(base=base, query_start_loc=qsl, q=to_storage(q32, sp.io_dtype))
+
+
+# Extend workloads: a chunked-prefill step of 8192 new tokens ([P2] §3.1 sets
+# max_num_batched_tokens to 8192; §2.1 names prefill and extend) over cached contexts of
+# up to 3.5K tokens, in the LLaMA-7B layer shape and in GQA bf16 with [P2]'s 256-token
+# blocks; and a mixed fp8 batch whose query lengths range from a few tokens (several
+# tokens checked at once) to a 512-token chunk.
+EXTEND = {
+    "extend_llama7b_fp16": (Spec("extend_llama7b_fp16", 16, 32, 32, 128, 16, "f16", "f16",
+                                 ("uniform_sum", ((512, 512), (0, 3584))), seed=1101),
+                            ("const", 512)),
+    "extend_gqa_bf16_bs256": (Spec("extend_gqa_bf16_bs256", 16, 32, 8, 128, 256, "bf16", "bf16",
+                                   ("uniform_sum", ((512, 512), (0, 3584))), seed=1102),
+                              ("const", 512)),
+    "extend_mixed_fp8": (Spec("extend_mixed_fp8", 64, 32, 8, 128, 16, "bf16", "fp8_e4m3",
+                              ("uniform_sum", ((512, 512), (0, 3584))), seed=1103),
+                         ("choice", (4, 64, 512), (0.5, 0.3, 0.2))),
+}
+
+
+def small_extend(name: str):
+    """A reduced extend workload the fp64 oracle finishes in seconds (same dtypes, group
+    and block sizes; ragged query and context lengths)."""
+    spec, ql = EXTEND[name]
+    small = spec.replace(name=spec.name + "_small", num_seqs=4,
+                         lengths=("fixed", (70, 300, 41, 520)), seed=spec.seed + 1000)
+    if ql[0] == "const":
+        ql = ("fixed", (70, 37, 41, 200))    # one pure prefill, one whole-context prefill
+    else:
+        ql = ("fixed", (4, 64, 1, 130))
+    return small, ql
