@@ -28,6 +28,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+MFMA16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 matrix peak, AMD published
+EXTEND_METRIC = "paged extend (chunked prefill) attention TFLOP/s, causal algorithmic flops"
 METRIC = "paged-attn decode KV GB/s read and % of MI355X HBM peak; seqs·tokens/s"
 DEFAULT_MODE = {0: "direct", 1: "direct", 2: "direct", 3: "balanced", 4: "balanced",
                 "llama7b_fp16_bs128": "direct", "shared_prefix_bf16_bs256": "direct",
@@ -107,6 +109,148 @@ def cpu_baseline(b, seconds: float):
             "seq_tokens_per_s": round(tokens / dt, 3)}
 
 
+def extend_flops(e) -> int:
+    """4 * D flops per (query row, head, key it attends to): 2D for q.k, 2D for p*v."""
+    sp = e.base.spec
+    total = 0
+    for s in range(e.base.num_seqs):
+        L = int(e.base.context_lens[s])
+        Q = int(e.query_start_loc[s + 1] - e.query_start_loc[s])
+        # new token i attends to L - Q + i + 1 keys
+        keys = sum(max(0, L - Q + i + 1) for i in range(Q))
+        total += keys
+    return 4 * sp.head_dim * sp.num_heads * total
+
+
+def extend_cpu_baseline(e, seconds: float):
+    """The fp64 extend oracle (as it stands) on whole (sequence, KV head) units, cycled
+    until `seconds` of work; reported in TFLOP/s of the same flop count."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import extend as ext_oracle
+
+    b = e.base
+    sp = b.spec
+    G = sp.num_heads // sp.num_kv_heads
+    units = [(s, g) for g in range(sp.num_kv_heads) for s in range(sp.num_seqs)
+             if e.query_start_loc[s + 1] > e.query_start_loc[s]]
+    n = len(units)
+    order = [units[(i * 7919) % n] for i in range(n)] if n % 7919 else units
+    done = flops = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            s, g = order[done % n]
+            lo, hi = int(e.query_start_loc[s]), int(e.query_start_loc[s + 1])
+            rows = [(t, h) for t in range(lo, hi) for h in range(g * G, (g + 1) * G)]
+            ext_oracle.paged_extend(e.q, b.k_pool, b.v_pool, b.block_tables, b.context_lens,
+                                    e.query_start_loc, b.scale, sp.num_kv_heads, sp.io_dtype, sp.kv_dtype,
+                                    float(b.k_scale), float(b.v_scale), rows=rows)
+            L, Q = int(b.context_lens[s]), hi - lo
+            flops += 4 * sp.head_dim * G * sum(max(0, L - Q + i + 1) for i in range(Q))
+            done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 9), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} (sequence, KV head) units of {sp.name} ({n} per batch, cycled), all new "
+                      f"tokens and {G} query heads each, fp64 numpy oracle on 1 thread, {dt:.1f} s"}
+
+
+def bench_extend(args, name):
+    """One step = one pa_extend call over the whole chunked-prefill batch."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import pagedattention_block_table_amd as pa
+    from pagedattention_block_table_amd import workloads as W
+
+    spec, ql = W.EXTEND[name]
+    t0 = time.time()
+    e = W.make_extend_batch(spec, ql)
+    b = e.base
+    sp = b.spec
+    flops = extend_flops(e)
+    kv_e = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}[sp.kv_dtype]
+    kv_unique = oracle.kv_unique_bytes(b.block_tables, b.context_lens, sp.block_size, sp.num_kv_heads,
+                                       sp.head_dim, kv_e)
+    log(f"[bench] extend workload {sp.name}: S={sp.num_seqs} H={sp.num_heads} Hkv={sp.num_kv_heads} "
+        f"D={sp.head_dim} BS={sp.block_size} kv={sp.kv_dtype} T={e.num_tokens} "
+        f"sumL={int(b.context_lens.sum())} flops={flops / 1e9:.1f} G (generated in {time.time() - t0:.1f}s)")
+
+    def dev_t(x, dt):
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    q = dev_t(e.q, sp.io_dtype)
+    out = torch.empty_like(q)
+    bt = torch.from_numpy(b.block_tables).cuda()
+    cl = torch.from_numpy(b.context_lens).cuda()
+    qsl = torch.from_numpy(e.query_start_loc).cuda()
+    k0 = dev_t(b.k_pool, sp.kv_dtype)
+    v0 = dev_t(b.v_pool, sp.kv_dtype)
+    pool_bytes = k0.numel() * k0.element_size() * 2
+    R = max(2, int(math.ceil(args.replica_bytes / pool_bytes)))
+    ks = [k0] + [k0.clone() for _ in range(R - 1)]
+    vs = [v0] + [v0.clone() for _ in range(R - 1)]
+    stream = torch.cuda.current_stream()
+    mq = e.max_query_len
+
+    def step(i):
+        pa.pa_extend(q, ks[i % R], vs[i % R], bt, cl, qsl, mq, scale=float(b.scale), k_scale=float(b.k_scale),
+                     v_scale=float(b.v_scale), out=out, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    t_wall = time.perf_counter()
+    for i in range(K):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_per_step = wall * 1e3 / K
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        starts[i].record(stream)
+        step(args.warmup + K + i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    durs_ms = [s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)]
+    kern_ms = float(np.mean(durs_ms))
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    res = {
+        "metric": EXTEND_METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": sp.io_dtype, "data": "synthetic",
+        "config": {"workload": sp.name, "num_seqs": sp.num_seqs, "num_heads": sp.num_heads,
+                   "num_kv_heads": sp.num_kv_heads, "head_dim": sp.head_dim, "block_size": sp.block_size,
+                   "io_dtype": sp.io_dtype, "kv_dtype": sp.kv_dtype, "accumulate": "f32",
+                   "new_tokens": e.num_tokens, "max_query_len": mq,
+                   "sum_context_len": int(b.context_lens.sum()), "kv_unique_bytes": kv_unique,
+                   "kv_replicas": R},
+        "kv_GB_per_s": round(kv_unique / (ms_per_step * 1e-3) / 1e9, 2),
+        "new_tokens_per_s": round(e.num_tokens / (ms_per_step * 1e-3), 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel_ms": round(kern_ms, 6), "algorithmic_flops_per_launch": flops,
+                     "p10_p90_ms": [round(float(np.percentile(durs_ms, 10)), 6),
+                                    round(float(np.percentile(durs_ms, 90)), 6)]},
+        "cpu_baseline": None,
+    }
+    log(f"[bench] {ms_per_step * 1e3:.2f} us/step wall, {kern_ms * 1e3:.2f} us/launch (events): "
+        f"{value:.1f} TFLOP/s, {res['kv_GB_per_s']:.0f} GB/s unique KV, mfma frac {achieved / MFMA16_PEAK_TFLOPS:.3f}")
+    del ks, vs
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = extend_cpu_baseline(e, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,7 +258,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--workload", default="",
-                    help="a named variant of a config (larger blocks), instead of --config")
+                    help="a named variant of a config (larger blocks) or an extend workload "
+                         "(extend_*), instead of --config")
     ap.add_argument("--mode", default="auto", choices=["auto", "direct", "partitioned", "balanced"])
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--workgroups", type=int, default=0,
@@ -141,6 +286,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(3)
     pa._lib.lib()  # fail loudly if the HIP library is missing
+    if args.workload in W.EXTEND:
+        bench_extend(args, args.workload)
+        return
 
     cfg = args.workload or args.config
     mode = DEFAULT_MODE[cfg] if args.mode == "auto" else args.mode

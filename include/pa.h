@@ -202,6 +202,31 @@ int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_pairs, int n
                    int num_blocks, int num_kv_heads, int head_dim, int block_size,
                    int kv_dtype, void* stream);
 
+/* Paged attention for several new tokens per sequence: prefill and extend ([P2] §2.1
+ * names both modes next to decode; §2.2's metadata holds block tables, context lengths
+ * and query lengths; [P1] §2 block tables). Sequence s has L = context_lens[s] cached
+ * tokens, counting its new ones, whose K/V are already in the pools (pa_append_kv);
+ * the new ones are its last Q = query_start_loc[s+1] - query_start_loc[s] positions
+ * (the metadata's query lengths are these differences). New token i < Q sits at
+ * position p = L - Q + i; for every query head h (KV head g = h / (H / Hkv)):
+ *   out[query_start_loc[s] + i][h][:] = softmax(scale * K_s[0..p] q) V_s[0..p]
+ *   with q = q[query_start_loc[s] + i][h][:] and K_s / V_s read through the table
+ * i.e. causal among the new tokens (the plainest reading: the pages do not spell it
+ * out). q and out are [T][H][D] in io_dtype with T = query_start_loc[num_seqs];
+ * query_start_loc is a device int32 array [num_seqs + 1], non-decreasing, starting at 0;
+ * max_query_len (host) is >= every Q and sizes the grid. Rows with p < 0 (Q > L,
+ * outside the contract) are written as zeros. fp32 accumulation on the matrix cores:
+ * io_dtype F16 or BF16 (F32 is PA_ERR_UNSUPPORTED), kv_dtype == io_dtype or
+ * PA_FP8_E4M3, head_dim in {64, 128}, block_size a power of two in [8, 512],
+ * num_heads / num_kv_heads in {1, 2, 4, 8}. max_query_len == 0 is a no-op. Asynchronous
+ * on `stream`; allocates nothing. */
+int pa_extend(const void* q, const void* k_pool, const void* v_pool,
+              const int32_t* block_tables, const int32_t* context_lens,
+              const int32_t* query_start_loc, int num_seqs, int max_blocks_per_seq,
+              int num_blocks, int max_query_len, int num_heads, int num_kv_heads,
+              int head_dim, int block_size, float scale, int io_dtype, int kv_dtype,
+              float k_scale, float v_scale, void* out, void* stream);
+
 /* Device-side check of the block-table contract. For each sequence s writes
  * errors[s] = 0 if fine, else a bit set: 1 = context length < 0, 2 = context length
  * above max_blocks_per_seq * block_size, 4 = some used entry outside [0, num_blocks),

@@ -37,6 +37,7 @@ SIGNATURES = {
     "pa_check_tables": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "pa_append_kv": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _P]),
     "pa_copy_blocks": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "pa_extend": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _F, _F, _P, _P]),
     "pa_debug_fp8_to_f32": (_I, [_P, _P, _I, _P]),
     "pa_bm_create": (_P, [_I, _I, _I, _I]),
     "pa_bm_destroy": (None, [_P]),
@@ -199,6 +200,42 @@ def pa_decode_partitioned(q, k_pool, v_pool, block_tables, context_lens, max_con
     _raise("pa_decode_partitioned",
            lib().pa_decode_partitioned(*args, int(max_context_len), int(partition_size),
                                        workspace.data_ptr(), nbytes, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def pa_extend(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_query_len: int,
+              scale: Optional[float] = None, k_scale: float = 1.0, v_scale: float = 1.0,
+              out=None, stream=None):
+    """Prefill / extend: q [T][H][D] packed by query_start_loc (int32 [S+1]); the new
+    tokens are the last Q_s of each context and attend causally. Returns out [T][H][D]."""
+    torch = _torch()
+    for n, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("block_tables", block_tables),
+                 ("context_lens", context_lens), ("query_start_loc", query_start_loc)):
+        _check_dev(n, t)
+    if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
+        raise ValueError("q must be [T][H][D]; k_pool and v_pool [NB][Hkv][BS][D] of one shape and dtype")
+    for n, t in (("block_tables", block_tables), ("context_lens", context_lens),
+                 ("query_start_loc", query_start_loc)):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{n} must be int32")
+    T, H, D = q.shape
+    NB, Hkv, BS, D2 = k_pool.shape
+    S = context_lens.shape[0]
+    if D2 != D or block_tables.dim() != 2 or block_tables.shape[0] != S or query_start_loc.shape != (S + 1,):
+        raise ValueError("shapes of q, pools, block_tables, context_lens and query_start_loc disagree")
+    if out is None:
+        out = torch.empty_like(q)
+    _check_dev("out", out)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _raise("pa_extend",
+           lib().pa_extend(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_tables.data_ptr(),
+                           context_lens.data_ptr(), query_start_loc.data_ptr(), S, block_tables.shape[1],
+                           NB, int(max_query_len), H, Hkv, D, BS, float(scale), dtype_code(q),
+                           dtype_code(k_pool), float(k_scale), float(v_scale), out.data_ptr(),
+                           _stream(stream)))
     return out
 
 

@@ -1,0 +1,395 @@
+// Paged attention for several new query tokens per sequence (prefill / extend).
+//
+// Pages cited by title and section:
+//   [P2] vLLM architecture deep-dive §2.1 — the engine runs prefill (the prompt), decode
+//        and extend (long texts); §2.2 — the attention metadata holds block tables,
+//        context lengths and query lengths.
+//   [P1] "突破GPU内存瓶颈：vLLM与PagedAttention技术深度解析" §2 — the block table maps a
+//        sequence's logical blocks to physical blocks of the pool.
+//   [P3] "内存优化：KV Cache管理、PagedAttention原理与内存池配置" — tokens attend over the
+//        cached keys and values of their request.
+//
+// Sequence s has L = context_lens[s] cached tokens, the last Q of them new, with queries
+// q[query_start_loc[s] + i], i < Q. New token i sits at position p = L - Q + i and
+// attends over positions 0 .. p (causal), through the block table.
+//
+// One workgroup (4 waves) takes 64 query rows of one (sequence, KV head): 64 / G new
+// tokens times the G query heads of the group. Wave w owns rows 16w .. 16w+15 (row r is
+// token r / G, head r % G of the tile). The workgroup walks the keys in 32-token chunks:
+// all 256 lanes copy a chunk's K and V rows (looked up through the block table, fp8
+// widened exactly to the 16-bit MFMA type, rows past L zeroed) into LDS, double
+// buffered, with the next chunk's global loads in flight during the current one.
+//
+// Both products run on the matrix cores as v_mfma_f32_16x16x32 in the transposed
+// orientation, which keeps the probabilities in the registers that computed them:
+//   S^T[token][row] = K[token][:] . Q[row][:]   A = K rows from LDS, B = Q^T (registers)
+//   O^T[d][row]    += V^T[d][token] P^T[token][row]
+// Lane (n = l%16, q = l/16) receives S^T rows 4q + r of both 16-token halves of the
+// chunk for query row n: tokens 4q + r and 16 + 4q + r. The k order inside an MFMA is
+// free, so k = 8q + j stands for token 4q + j (j < 4) and 16 + 4q + j - 4 (j >= 4) in
+// both operands: the lane's own eight probabilities form its B operand, and its A
+// operand (V^T, row d = n) is two transposed LDS reads (ds_read_b64_tr_b16) of rows
+// 4q .. 4q+3 and 16+4q .. 16+4q+3. Probabilities are split into high and low 16-bit
+// parts (two MFMAs) so that the V product keeps fp32 accuracy. Online softmax per query
+// row in log2 units, the running max shared by the row's four lanes and raised lazily.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "pa.h"
+#include "pa_decode_impl.h"
+
+namespace pa {
+namespace {
+
+struct ExtendArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start_loc;
+  void* out;
+  int num_seqs;
+  int max_blocks_per_seq;
+  int num_blocks;
+  int num_heads;
+  int num_kv_heads;
+  int bs_shift;   // log2(block_size)
+  int q_tiles;    // workgroups per (sequence, KV head)
+  float q_mul;    // scale * log2(e) * k_scale
+  float v_scale;
+};
+
+constexpr int kExtWaves = 4;
+constexpr int kExtRows = 16 * kExtWaves;  // query rows per workgroup
+constexpr int kExtChunk = 32;             // key tokens per step
+
+template <int IO, int KV, int D>
+struct ExtGeo {
+  static constexpr int E = ElemBytes<KV>::value;
+  static constexpr int PPR = D * E / 16;                           // 16-byte pieces per row
+  static constexpr int PIECES = kExtChunk * PPR;                   // per chunk, K (and V)
+  static constexpr int NPT = (PIECES + kExtWaves * 64 - 1) / (kExtWaves * 64);  // per thread
+  static constexpr int VPP = 16 / E;                               // values per piece
+  static constexpr int KROW = D + 8;     // LDS K row, 16-bit elements (16-byte pad)
+  static constexpr int VROW = D + 16;    // LDS V row (32-byte pad: transposed reads spread)
+  static constexpr int K_BYTES = kExtChunk * KROW * 2;
+  static constexpr int V_BYTES = kExtChunk * VROW * 2;
+  static constexpr int BUF_BYTES = K_BYTES + V_BYTES;
+  static constexpr int NKS = D / 32;     // k-steps of the score product
+  static constexpr int NDT = D / 16;     // 16-column tiles of head_dim
+};
+
+// one 16-byte global piece -> LDS row slot in the MFMA type (fp8 widened exactly)
+template <int IO, int KV>
+__device__ __forceinline__ void put_piece(uint16_t* dst, const uint4& r) {
+  if constexpr (KV == kFP8) {
+    const uint4 lo = __builtin_bit_cast(uint4, fp8x8_operand<IO>(r.x, r.y));
+    const uint4 hi = __builtin_bit_cast(uint4, fp8x8_operand<IO>(r.z, r.w));
+    *(uint4*)dst = lo;
+    *(uint4*)(dst + 8) = hi;
+  } else {
+    *(uint4*)dst = r;
+  }
+}
+
+template <int IO, int KV, int D, int G>
+__global__ void __launch_bounds__(kExtWaves * 64) extend_kernel(const ExtendArgs a) {
+  using Geo = ExtGeo<IO, KV, D>;
+  using vec = typename Mma<IO>::vec;
+  using M16 = Mma16<IO>;
+  constexpr int QT = kExtRows / G;  // new tokens per workgroup
+  static_assert(kExtRows % G == 0 && 16 % G == 0, "group");
+
+  __shared__ __attribute__((aligned(16))) char lds[2 * Geo::BUF_BYTES];
+
+  // units: (sequence, KV head, query tile), tiles of one (s, g) adjacent (same XCD),
+  // heaviest tile (last tokens: longest causal range) first
+  const int unit = xcd_unit((int)blockIdx.x, (int)gridDim.x);
+  const int qt = a.q_tiles - 1 - unit % a.q_tiles;
+  const int sg = unit / a.q_tiles;
+  const int g = sg % a.num_kv_heads;
+  const int s = sg / a.num_kv_heads;
+  if (s >= a.num_seqs) return;
+
+  const int q0 = a.query_start_loc[s];
+  const int Q = a.query_start_loc[s + 1] - q0;
+  const int i0 = qt * QT;
+  if (Q <= 0 || i0 >= Q) return;  // whole workgroup
+  const int cap = a.max_blocks_per_seq << a.bs_shift;
+  const int L = min(max(a.context_lens[s], 0), cap);
+  const int i_end = min(Q, i0 + QT);
+  const int p0 = L - Q;                      // position of new token 0
+  const int p_last = p0 + i_end - 1;         // last position any row of the tile attends to
+  const int nch = p_last >= 0 ? p_last / kExtChunk + 1 : 0;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 15;
+  const int lq = lane >> 4;
+
+  // this lane's query row (column n of the wave's 16)
+  const int row = 16 * wave + n;
+  const int ti = i0 + row / G;
+  const int h = g * G + row % G;
+  const bool row_ok = ti < i_end;
+  const int pos = p0 + ti;                   // may be < 0 outside the contract
+  // the wave's position range (uniform)
+  const int w_first = i0 + (16 * wave) / G;
+  const int w_last = min(i_end, i0 + (16 * wave + 15) / G + 1) - 1;
+  const bool wave_live = w_first < i_end;
+  const int wp_min = p0 + w_first;
+  const int wp_max = p0 + w_last;
+
+  // Q^T operand: lane (n, lq) holds row n's head_dim values 32ks + 8lq .. +7
+  vec qv[Geo::NKS];
+  {
+    const int64_t base = ((int64_t)(q0 + (row_ok ? ti : 0)) * a.num_heads + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < Geo::NKS; ++ks) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (row_ok) w = *(const uint4*)((const char*)a.q + (base + 32 * ks + 8 * lq) * 2);
+      qv[ks] = __builtin_bit_cast(vec, w);
+    }
+  }
+
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const int bs_mask = (1 << a.bs_shift) - 1;
+  const int64_t row_bytes = (int64_t)D * Geo::E;
+  const int64_t tile_bytes = row_bytes << a.bs_shift;
+  const int64_t blk_stride = tile_bytes * a.num_kv_heads;
+  const char* kb = (const char*)a.k_pool + (int64_t)g * tile_bytes;
+  const char* vb = (const char*)a.v_pool + (int64_t)g * tile_bytes;
+
+  uint4 kreg[Geo::NPT], vreg[Geo::NPT];
+  auto load_chunk = [&](int c) {
+#pragma unroll
+    for (int u = 0; u < Geo::NPT; ++u) {
+      const int piece = tid + u * kExtWaves * 64;
+      const int r = piece / Geo::PPR;
+      const int col = piece % Geo::PPR;
+      const int t = c * kExtChunk + r;
+      uint4 kk = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      if (piece < Geo::PIECES && t < L) {
+        // contract: 0 <= b < num_blocks; clamp so that a bad table never reads outside
+        const int b = min(max(bt[t >> a.bs_shift], 0), a.num_blocks - 1);
+        const int64_t off = (int64_t)b * blk_stride + (int64_t)(t & bs_mask) * row_bytes + 16 * col;
+        kk = *(const uint4*)(kb + off);
+        vv = *(const uint4*)(vb + off);
+      }
+      kreg[u] = kk;
+      vreg[u] = vv;
+    }
+  };
+  auto store_chunk = [&](int buf) {
+    uint16_t* kt = (uint16_t*)(lds + buf * Geo::BUF_BYTES);
+    uint16_t* vt = (uint16_t*)(lds + buf * Geo::BUF_BYTES + Geo::K_BYTES);
+#pragma unroll
+    for (int u = 0; u < Geo::NPT; ++u) {
+      const int piece = tid + u * kExtWaves * 64;
+      if (piece < Geo::PIECES) {
+        const int r = piece / Geo::PPR;
+        const int col = (piece % Geo::PPR) * Geo::VPP;
+        put_piece<IO, KV>(kt + r * Geo::KROW + col, kreg[u]);
+        put_piece<IO, KV>(vt + r * Geo::VROW + col, vreg[u]);
+      }
+    }
+  };
+
+  float m = -3.0e38f;  // running max of row n (log2 units), same in the row's 4 lanes
+  float l = 0.f;       // this lane's share of the running sum
+  f32x4_t o[Geo::NDT];
+#pragma unroll
+  for (int dt = 0; dt < Geo::NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (nch > 0) {
+    load_chunk(0);
+    store_chunk(0);
+  }
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    if (c + 1 < nch) load_chunk(c + 1);
+    const int t0 = c * kExtChunk;
+    if (wave_live && t0 <= wp_max) {
+      const uint16_t* kt = (const uint16_t*)(lds + (c & 1) * Geo::BUF_BYTES);
+      const uint16_t* vt = (const uint16_t*)(lds + (c & 1) * Geo::BUF_BYTES + Geo::K_BYTES);
+      // scores: S^T of the two 16-token halves
+      f32x4_t acc[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        acc[hf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < Geo::NKS; ++ks) {
+          const vec kop = *(const vec*)(kt + (16 * hf + n) * Geo::KROW + 32 * ks + 8 * lq);
+          acc[hf] = Mma<IO>::mma(kop, qv[ks], acc[hf]);
+        }
+      }
+      // z[j]: token t0 + 4lq + j (j < 4) and t0 + 16 + 4lq + j - 4 (j >= 4)
+      float z[8];
+      const bool need_mask = t0 + kExtChunk - 1 > wp_min;  // uniform
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float v = acc[j >> 2][j & 3] * a.q_mul;
+        if (need_mask) {
+          const int t = t0 + 16 * (j >> 2) + 4 * lq + (j & 3);
+          z[j] = t <= pos ? v : -INFINITY;
+        } else {
+          z[j] = v;
+        }
+      }
+      float mx = z[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, z[j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool raise = mx > m + kLazyRescale;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        const float mn = raise ? mx : m;
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        m = mn;
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < Geo::NDT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[dt][r] *= alpha;
+      }
+      uint16_t phi[8], plo[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p = __builtin_amdgcn_exp2f(z[j] - m);
+        l += p;
+        M16::split(p, phi[j], plo[j]);
+      }
+      uint4 bh, bl;
+      bh.x = phi[0] | ((uint32_t)phi[1] << 16);
+      bh.y = phi[2] | ((uint32_t)phi[3] << 16);
+      bh.z = phi[4] | ((uint32_t)phi[5] << 16);
+      bh.w = phi[6] | ((uint32_t)phi[7] << 16);
+      bl.x = plo[0] | ((uint32_t)plo[1] << 16);
+      bl.y = plo[2] | ((uint32_t)plo[3] << 16);
+      bl.z = plo[4] | ((uint32_t)plo[5] << 16);
+      bl.w = plo[6] | ((uint32_t)plo[7] << 16);
+      const vec bhi = __builtin_bit_cast(vec, bh);
+      const vec blo = __builtin_bit_cast(vec, bl);
+      // V^T operand: row d = 16dt + n, tokens 4lq .. 4lq+3 and 16+4lq .. 16+4lq+3
+      const int vr = 4 * lq + (n >> 2);
+      const int vc = 4 * (n & 3);
+#pragma unroll
+      for (int dt = 0; dt < Geo::NDT; ++dt) {
+        const i16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(vt + vr * Geo::VROW + 16 * dt + vc));
+        const i16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(vt + (16 + vr) * Geo::VROW + 16 * dt + vc));
+        const uint2 w0 = __builtin_bit_cast(uint2, x0);
+        const uint2 w1 = __builtin_bit_cast(uint2, x1);
+        const vec av = __builtin_bit_cast(vec, make_uint4(w0.x, w0.y, w1.x, w1.y));
+        o[dt] = Mma<IO>::mma(av, bhi, o[dt]);
+        o[dt] = Mma<IO>::mma(av, blo, o[dt]);
+      }
+    }
+    if (c + 1 < nch) store_chunk((c + 1) & 1);
+    __syncthreads();
+  }
+
+  if (!row_ok) return;
+  float lt = l + __shfl_xor(l, 16);
+  lt += __shfl_xor(lt, 32);
+  // lane (n, lq) holds O^T[16dt + 4lq + r][row n]
+  const float inv = pos >= 0 && lt > 0.f ? a.v_scale / lt : 0.f;
+  const int64_t obase = ((int64_t)(q0 + ti) * a.num_heads + h) * D;
+#pragma unroll
+  for (int dt = 0; dt < Geo::NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) store_io<IO>(a.out, obase + 16 * dt + 4 * lq + r, o[dt][r] * inv);
+}
+
+template <int IO, int KV, int D>
+int launch_ext_g(const ExtendArgs& a, int G, int grid, hipStream_t st) {
+  switch (G) {
+    case 1: hipLaunchKernelGGL((extend_kernel<IO, KV, D, 1>), dim3(grid), dim3(kExtWaves * 64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((extend_kernel<IO, KV, D, 2>), dim3(grid), dim3(kExtWaves * 64), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((extend_kernel<IO, KV, D, 4>), dim3(grid), dim3(kExtWaves * 64), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((extend_kernel<IO, KV, D, 8>), dim3(grid), dim3(kExtWaves * 64), 0, st, a); break;
+    default: return PA_ERR_UNSUPPORTED;
+  }
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+template <int IO, int KV>
+int launch_ext_d(const ExtendArgs& a, int D, int G, int grid, hipStream_t st) {
+  switch (D) {
+    case 64: return launch_ext_g<IO, KV, 64>(a, G, grid, st);
+    case 128: return launch_ext_g<IO, KV, 128>(a, G, grid, st);
+    default: return PA_ERR_UNSUPPORTED;
+  }
+}
+
+bool ext_pos_finite(float x) { return std::isfinite(x) && x > 0.f; }
+
+}  // namespace
+}  // namespace pa
+
+extern "C" int pa_extend(const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         const int32_t* query_start_loc, int num_seqs, int max_blocks_per_seq,
+                         int num_blocks, int max_query_len, int num_heads, int num_kv_heads,
+                         int head_dim, int block_size, float scale, int io_dtype, int kv_dtype,
+                         float k_scale, float v_scale, void* out, void* stream) {
+  using namespace pa;
+  try {
+    if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start_loc || !out)
+      return PA_ERR_INVALID;
+    if (num_seqs <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_query_len < 0 ||
+        num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
+      return PA_ERR_INVALID;
+    if (io_dtype != PA_F32 && io_dtype != PA_F16 && io_dtype != PA_BF16) return PA_ERR_INVALID;
+    if (kv_dtype != PA_F32 && kv_dtype != PA_F16 && kv_dtype != PA_BF16 && kv_dtype != PA_FP8_E4M3)
+      return PA_ERR_INVALID;
+    if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID;
+    if (!ext_pos_finite(scale)) return PA_ERR_INVALID;
+    if (kv_dtype == PA_FP8_E4M3 && (!ext_pos_finite(k_scale) || !ext_pos_finite(v_scale)))
+      return PA_ERR_INVALID;
+    if (((uintptr_t)q | (uintptr_t)k_pool | (uintptr_t)v_pool | (uintptr_t)out) & 15u) return PA_ERR_INVALID;
+    if ((int64_t)max_blocks_per_seq * block_size > INT_MAX / 2) return PA_ERR_INVALID;
+    if (io_dtype == PA_F32) return PA_ERR_UNSUPPORTED;  // matrix-core path: 16-bit queries
+    if (kv_dtype != io_dtype && kv_dtype != PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (block_size < 8 || block_size > 512 || (block_size & (block_size - 1)) != 0) return PA_ERR_UNSUPPORTED;
+    const int G = num_heads / num_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+    if (max_query_len == 0) return PA_OK;
+    ExtendArgs a{};
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.query_start_loc = query_start_loc;
+    a.out = out;
+    a.num_seqs = num_seqs;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_blocks = num_blocks;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.bs_shift = __builtin_ctz((unsigned)block_size);
+    const int QT = kExtRows / G;
+    a.q_tiles = (max_query_len + QT - 1) / QT;
+    a.q_mul = scale * kLog2e * (kv_dtype == PA_FP8_E4M3 ? k_scale : 1.f);
+    a.v_scale = kv_dtype == PA_FP8_E4M3 ? v_scale : 1.f;
+    const int64_t grid = (int64_t)num_seqs * num_kv_heads * a.q_tiles;
+    if (grid > INT_MAX) return PA_ERR_INVALID;
+    hipStream_t st = (hipStream_t)stream;
+    const int D = head_dim;
+    if (io_dtype == PA_F16)
+      return kv_dtype == PA_FP8_E4M3 ? launch_ext_d<kF16, kFP8>(a, D, G, (int)grid, st)
+                                     : launch_ext_d<kF16, kF16>(a, D, G, (int)grid, st);
+    return kv_dtype == PA_FP8_E4M3 ? launch_ext_d<kBF16, kFP8>(a, D, G, (int)grid, st)
+                                   : launch_ext_d<kBF16, kBF16>(a, D, G, (int)grid, st);
+  } catch (...) {
+    return PA_ERR_LAUNCH;
+  }
+}

@@ -212,3 +212,31 @@ def test_copy_blocks_rejects():
     assert call(vp=FAKE + 8) == _lib.PA_ERR_INVALID
     assert call(Hkv=1, D=3, BS=1, kv=_lib.PA_FP8_E4M3) == _lib.PA_ERR_UNSUPPORTED  # 3-byte blocks
     assert call(n=0, pairs=0) == _lib.PA_OK                        # nothing to copy, nothing enqueued
+
+
+def test_extend_rejects():
+    L = _lib.lib()
+    good = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, qsl=FAKE, S=2, MB=4, NB=8, MQ=5, H=8, Hkv=2,
+                D=128, BS=16, scale=0.1, io=_lib.PA_F16, kv=_lib.PA_F16, ks=1.0, vs=1.0, out=FAKE)
+
+    def call(**over):
+        a = dict(good)
+        a.update(over)
+        return L.pa_extend(a["q"], a["k"], a["v"], a["bt"], a["cl"], a["qsl"], a["S"], a["MB"], a["NB"],
+                           a["MQ"], a["H"], a["Hkv"], a["D"], a["BS"], a["scale"], a["io"], a["kv"],
+                           a["ks"], a["vs"], a["out"], None)
+
+    assert call(qsl=0) == _lib.PA_ERR_INVALID
+    assert call(out=0) == _lib.PA_ERR_INVALID
+    assert call(MQ=-1) == _lib.PA_ERR_INVALID
+    assert call(H=6, Hkv=4) == _lib.PA_ERR_INVALID
+    assert call(scale=float("inf")) == _lib.PA_ERR_INVALID
+    assert call(kv=_lib.PA_FP8_E4M3, ks=-1.0) == _lib.PA_ERR_INVALID
+    assert call(q=FAKE + 4) == _lib.PA_ERR_INVALID
+    assert call(io=_lib.PA_F32, kv=_lib.PA_F32) == _lib.PA_ERR_UNSUPPORTED   # 16-bit queries only
+    assert call(kv=_lib.PA_BF16) == _lib.PA_ERR_UNSUPPORTED
+    assert call(D=96) == _lib.PA_ERR_UNSUPPORTED
+    assert call(BS=24) == _lib.PA_ERR_UNSUPPORTED
+    assert call(BS=1024) == _lib.PA_ERR_UNSUPPORTED
+    assert call(H=32, Hkv=2) == _lib.PA_ERR_UNSUPPORTED                      # group of 16
+    assert call(MQ=0) == _lib.PA_OK                                          # nothing enqueued
