@@ -26,6 +26,9 @@ LIB = os.path.join(PKG, "libpa.so")
 ARCH = "gfx950"
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# per translation unit: the extend kernels keep their MFMA accumulators in ordinary VGPRs
+# (they are rescaled by vector ops; in AGPRs every rescale costs copies both ways)
+FILE_FLAGS = {"pa_extend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -38,6 +41,7 @@ def hipcc() -> str:
 def _compile(src: str, verbose: bool, build_dir: str = BUILD, defines=()) -> str:
     obj = os.path.join(build_dir, os.path.basename(src).replace(".hip", ".o"))
     cmd = [hipcc(), "-c", "-fPIC", "-O3", "-std=c++17", f"--offload-arch={ARCH}", *DEVICE_FLAGS,
+           *FILE_FLAGS.get(os.path.basename(src), []),
            *[f"-D{d}" for d in defines],
            "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC, "-o", obj, src]
     if verbose:

@@ -307,8 +307,310 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_kernel(const ExtendArgs
     for (int r = 0; r < 4; ++r) store_io<IO>(a.out, obase + 16 * dt + 4 * lq + r, o[dt][r] * inv);
 }
 
+// ---------------------------------------------------------------------------------
+// 16-bit KV: direct-to-LDS loads, a ring of four chunk buffers, 32 query rows per wave
+// ---------------------------------------------------------------------------------
+//
+// Each wave owns two 16-row query tiles (a workgroup 128 rows), so every K / V operand
+// read from LDS feeds two MFMAs. K and V chunks go from HBM straight into LDS with
+// global_load_lds_dwordx4 (lane l of an instruction lands 16 * l bytes past the
+// instruction's LDS base), three chunks ahead of the one being computed. The copies are
+// issued from inline assembly so that the compiler, which cannot tell which LDS bytes
+// they write, does not wait for all of them before every LDS read; the kernel waits
+// for exactly the chunk it is about to use (s_waitcnt vmcnt) and then synchronises the
+// workgroup. Rows past the end of the context load the last valid row instead (finite
+// data; their probability is zero), so every lane issues every copy and the count of
+// outstanding copies is known. Block ids come through scalar loads.
+//
+// LDS rows are unpadded (the copies fill 1 KiB runs); 16-byte pieces are XOR-swizzled
+// per row so that the K operand reads (16 rows, same column) and the transposed V reads
+// (4 rows, 2 pieces) hit distinct banks.
+
+constexpr int kDmaStages = 4;
+constexpr int kDmaRows = 32 * kExtWaves;  // query rows per workgroup (two tiles per wave)
+
+template <int D>
+struct DmaGeo {
+  static constexpr int PPR = D * 2 / 16;                    // 16-byte pieces per row
+  static constexpr int ROW_B = D * 2;
+  static constexpr int TILE_B = kExtChunk * ROW_B;          // K (or V) of one chunk
+  static constexpr int STAGE_B = 2 * TILE_B;
+  static constexpr int PPT = kExtChunk * PPR / (kExtWaves * 64);  // copies per thread per tile
+  static constexpr int NKS = D / 32;
+  static constexpr int NDT = D / 16;
+  static_assert(PPT >= 1 && kExtChunk * PPR % (kExtWaves * 64) == 0, "whole copies");
+  static __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  static __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
+};
+
+__device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %1, off" ::"{m0}"(lds_base), "v"(src) : "memory");
+}
+
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
+}
+
+template <int IO, int D, int G>
+__global__ void __launch_bounds__(kExtWaves * 64) extend_dma_kernel(const ExtendArgs a) {
+  using Geo = DmaGeo<D>;
+  using vec = typename Mma<IO>::vec;
+  using M16 = Mma16<IO>;
+  constexpr int QT = kDmaRows / G;  // new tokens per workgroup
+  constexpr int NT = 2;             // query tiles per wave
+  constexpr int CPS = 2 * Geo::PPT; // copies per thread per stage
+  // probabilities as f16 keep 11 significant bits (error <= 2^-12 relative, about 1e-3 of
+  // the largest |V| at most); bf16 keeps 8, so there they go as high + low halves
+  constexpr bool SPLIT = IO == kBF16;
+
+  __shared__ __attribute__((aligned(1024))) char lds[kDmaStages * Geo::STAGE_B];
+
+  const int unit = xcd_unit((int)blockIdx.x, (int)gridDim.x);
+  const int qt = a.q_tiles - 1 - unit % a.q_tiles;
+  const int sg = unit / a.q_tiles;
+  const int g = sg % a.num_kv_heads;
+  const int s = sg / a.num_kv_heads;
+  if (s >= a.num_seqs) return;
+
+  const int q0 = a.query_start_loc[s];
+  const int Q = a.query_start_loc[s + 1] - q0;
+  const int i0 = qt * QT;
+  if (Q <= 0 || i0 >= Q) return;  // whole workgroup
+  const int cap = a.max_blocks_per_seq << a.bs_shift;
+  const int L = min(max(a.context_lens[s], 0), cap);
+  const int i_end = min(Q, i0 + QT);
+  const int p0 = L - Q;
+  const int p_last = p0 + i_end - 1;
+  const int nch = p_last >= 0 ? p_last / kExtChunk + 1 : 0;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 15;
+  const int lq = lane >> 4;
+
+  // query rows of this lane: tile tq holds row 32 * wave + 16 * tq + n
+  int ti[NT], hh[NT], pos[NT];
+  bool row_ok[NT];
+#pragma unroll
+  for (int tq = 0; tq < NT; ++tq) {
+    const int row = 32 * wave + 16 * tq + n;
+    ti[tq] = i0 + row / G;
+    hh[tq] = g * G + row % G;
+    row_ok[tq] = ti[tq] < i_end;
+    pos[tq] = p0 + ti[tq];
+  }
+  const int w_first = i0 + (32 * wave) / G;
+  const int w_last = min(i_end, i0 + (32 * wave + 31) / G + 1) - 1;
+  const bool wave_live = w_first < i_end;
+  const int wp_min = p0 + w_first;
+  const int wp_max = p0 + w_last;
+
+  vec qv[NT][Geo::NKS];
+#pragma unroll
+  for (int tq = 0; tq < NT; ++tq) {
+    const int64_t base = ((int64_t)(q0 + (row_ok[tq] ? ti[tq] : 0)) * a.num_heads + hh[tq]) * D;
+#pragma unroll
+    for (int ks = 0; ks < Geo::NKS; ++ks) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (row_ok[tq]) w = *(const uint4*)((const char*)a.q + (base + 32 * ks + 8 * lq) * 2);
+      qv[tq][ks] = __builtin_bit_cast(vec, w);
+    }
+  }
+  // the query loads complete here: afterwards the only outstanding vector-memory
+  // operations are the chunk copies, which the loop counts itself
+  asm volatile("" ::: "memory");
+  wait_vm<0>();
+
+  // copy geometry: thread piece u sits at physical slot P = 256u + 64 wave + lane of a tile
+  const __attribute__((address_space(4))) int32_t* btc =
+      (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)s * a.max_blocks_per_seq);
+  const int bs_mask = (1 << a.bs_shift) - 1;
+  const int64_t tile_bytes = (int64_t)Geo::ROW_B << a.bs_shift;
+  const int64_t blk_stride = tile_bytes * a.num_kv_heads;
+  const char* kb = (const char*)a.k_pool + (int64_t)g * tile_bytes;
+  const char* vb = (const char*)a.v_pool + (int64_t)g * tile_bytes;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  int crow[Geo::PPT], ck[Geo::PPT], cv[Geo::PPT];
+#pragma unroll
+  for (int u = 0; u < Geo::PPT; ++u) {
+    const int P = 256 * u + 64 * wave + lane;
+    crow[u] = P / Geo::PPR;
+    const int pc = P % Geo::PPR;
+    ck[u] = pc ^ Geo::swz_k(crow[u]);
+    cv[u] = pc ^ Geo::swz_v(crow[u]);
+  }
+  auto issue = [&](int c) {
+    const int buf = c % kDmaStages;
+#pragma unroll
+    for (int u = 0; u < Geo::PPT; ++u) {
+      const int first = c * kExtChunk + (256 * u + 64 * wave) / Geo::PPR;  // uniform
+      const int bidx = __builtin_amdgcn_readfirstlane(min(first, L - 1) >> a.bs_shift);
+      // contract: 0 <= b < num_blocks; clamp so that a bad table never reads outside
+      const int b = min(max(btc[bidx], 0), a.num_blocks - 1);
+      const int ts = min(c * kExtChunk + crow[u], L - 1);
+      const int64_t roff = (int64_t)b * blk_stride + (int64_t)(ts & bs_mask) * Geo::ROW_B;
+      const uint32_t dst = lds0 + buf * Geo::STAGE_B + (256 * u + 64 * wave) * 16;
+      lds_copy16(kb + roff + 16 * ck[u], dst);
+      lds_copy16(vb + roff + 16 * cv[u], dst + Geo::TILE_B);
+    }
+  };
+
+  float m[NT], l[NT];
+  f32x4_t o[NT][Geo::NDT];
+#pragma unroll
+  for (int tq = 0; tq < NT; ++tq) {
+    m[tq] = -3.0e38f;
+    l[tq] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < Geo::NDT; ++dt) o[tq][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+#pragma unroll
+  for (int j = 0; j < kDmaStages - 1; ++j)
+    if (j < nch) issue(j);
+
+  for (int c = 0; c < nch; ++c) {
+    // chunk c has landed once at most the copies of the chunks issued after it remain
+    const int newer = min(kDmaStages - 2, nch - 1 - c);
+    if (newer >= 2) wait_vm<2 * CPS>();
+    else if (newer == 1) wait_vm<CPS>();
+    else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (c + kDmaStages - 1 < nch) issue(c + kDmaStages - 1);
+
+    const int t0 = c * kExtChunk;
+    if (wave_live && t0 <= wp_max) {
+      const char* kt = lds + (c % kDmaStages) * Geo::STAGE_B;
+      const char* vt = kt + Geo::TILE_B;
+      f32x4_t acc[NT][2];
+#pragma unroll
+      for (int tq = 0; tq < NT; ++tq)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) acc[tq][hf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int r = 16 * hf + n;
+#pragma unroll
+        for (int ks = 0; ks < Geo::NKS; ++ks) {
+          const int pc = (4 * ks + lq) ^ Geo::swz_k(r);
+          const vec kop = *(const vec*)(kt + r * Geo::ROW_B + 16 * pc);
+#pragma unroll
+          for (int tq = 0; tq < NT; ++tq) acc[tq][hf] = Mma<IO>::mma(kop, qv[tq][ks], acc[tq][hf]);
+        }
+      }
+      const bool need_mask = t0 + kExtChunk - 1 > wp_min;  // uniform
+      vec bhi[NT], blo[NT];
+#pragma unroll
+      for (int tq = 0; tq < NT; ++tq) {
+        float z[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float v = acc[tq][j >> 2][j & 3] * a.q_mul;
+          if (need_mask) {
+            const int t = t0 + 16 * (j >> 2) + 4 * lq + (j & 3);
+            z[j] = t <= pos[tq] ? v : -INFINITY;
+          } else {
+            z[j] = v;
+          }
+        }
+        float mx = z[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, z[j]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool raise = mx > m[tq] + kLazyRescale;
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+          const float mn = raise ? mx : m[tq];
+          const float alpha = __builtin_amdgcn_exp2f(m[tq] - mn);
+          m[tq] = mn;
+          l[tq] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < Geo::NDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[tq][dt][r] *= alpha;
+        }
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          p[j] = __builtin_amdgcn_exp2f(z[j] - m[tq]);
+          l[tq] += p[j];
+        }
+        if constexpr (SPLIT) {
+          uint16_t phi[8], plo[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) M16::split(p[j], phi[j], plo[j]);
+          uint4 bh, bl;
+          bh.x = phi[0] | ((uint32_t)phi[1] << 16);
+          bh.y = phi[2] | ((uint32_t)phi[3] << 16);
+          bh.z = phi[4] | ((uint32_t)phi[5] << 16);
+          bh.w = phi[6] | ((uint32_t)phi[7] << 16);
+          bl.x = plo[0] | ((uint32_t)plo[1] << 16);
+          bl.y = plo[2] | ((uint32_t)plo[3] << 16);
+          bl.z = plo[4] | ((uint32_t)plo[5] << 16);
+          bl.w = plo[6] | ((uint32_t)plo[7] << 16);
+          bhi[tq] = __builtin_bit_cast(vec, bh);
+          blo[tq] = __builtin_bit_cast(vec, bl);
+        } else {
+          vec v;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = (_Float16)p[j];
+          bhi[tq] = v;
+        }
+      }
+      // V^T operand: row d = 16dt + n; tokens 4lq .. 4lq+3 and 16+4lq .. 16+4lq+3
+      const int r0 = 4 * lq + (n >> 2);
+      const int r1 = r0 + 16;
+      const int half = (n & 1) * 8;
+#pragma unroll
+      for (int dt = 0; dt < Geo::NDT; ++dt) {
+        const int c = 2 * dt + ((n & 3) >> 1);
+        const i16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(vt + r0 * Geo::ROW_B + 16 * (c ^ Geo::swz_v(r0)) + half));
+        const i16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(vt + r1 * Geo::ROW_B + 16 * (c ^ Geo::swz_v(r1)) + half));
+        const uint2 w0 = __builtin_bit_cast(uint2, x0);
+        const uint2 w1 = __builtin_bit_cast(uint2, x1);
+        const vec av = __builtin_bit_cast(vec, make_uint4(w0.x, w0.y, w1.x, w1.y));
+#pragma unroll
+        for (int tq = 0; tq < NT; ++tq) {
+          o[tq][dt] = Mma<IO>::mma(av, bhi[tq], o[tq][dt]);
+          if constexpr (SPLIT) o[tq][dt] = Mma<IO>::mma(av, blo[tq], o[tq][dt]);
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int tq = 0; tq < NT; ++tq) {
+    float lt = l[tq] + __shfl_xor(l[tq], 16);
+    lt += __shfl_xor(lt, 32);
+    if (!row_ok[tq]) continue;
+    const float inv = pos[tq] >= 0 && lt > 0.f ? a.v_scale / lt : 0.f;
+    const int64_t obase = ((int64_t)(q0 + ti[tq]) * a.num_heads + hh[tq]) * D;
+#pragma unroll
+    for (int dt = 0; dt < Geo::NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) store_io<IO>(a.out, obase + 16 * dt + 4 * lq + r, o[tq][dt][r] * inv);
+  }
+}
+
 template <int IO, int KV, int D>
 int launch_ext_g(const ExtendArgs& a, int G, int grid, hipStream_t st) {
+  if constexpr (KV == IO) {
+    switch (G) {
+      case 1: hipLaunchKernelGGL((extend_dma_kernel<IO, D, 1>), dim3(grid), dim3(kExtWaves * 64), 0, st, a); break;
+      case 2: hipLaunchKernelGGL((extend_dma_kernel<IO, D, 2>), dim3(grid), dim3(kExtWaves * 64), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((extend_dma_kernel<IO, D, 4>), dim3(grid), dim3(kExtWaves * 64), 0, st, a); break;
+      case 8: hipLaunchKernelGGL((extend_dma_kernel<IO, D, 8>), dim3(grid), dim3(kExtWaves * 64), 0, st, a); break;
+      default: return PA_ERR_UNSUPPORTED;
+    }
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+  }
   switch (G) {
     case 1: hipLaunchKernelGGL((extend_kernel<IO, KV, D, 1>), dim3(grid), dim3(kExtWaves * 64), 0, st, a); break;
     case 2: hipLaunchKernelGGL((extend_kernel<IO, KV, D, 2>), dim3(grid), dim3(kExtWaves * 64), 0, st, a); break;
@@ -376,7 +678,7 @@ extern "C" int pa_extend(const void* q, const void* k_pool, const void* v_pool,
     a.num_heads = num_heads;
     a.num_kv_heads = num_kv_heads;
     a.bs_shift = __builtin_ctz((unsigned)block_size);
-    const int QT = kExtRows / G;
+    const int QT = (kv_dtype == io_dtype ? kDmaRows : kExtRows) / G;  // new tokens per workgroup
     a.q_tiles = (max_query_len + QT - 1) / QT;
     a.q_mul = scale * kLog2e * (kv_dtype == PA_FP8_E4M3 ? k_scale : 1.f);
     a.v_scale = kv_dtype == PA_FP8_E4M3 ? v_scale : 1.f;
