@@ -25,10 +25,12 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 ARCH = "gfx950"
 
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# per translation unit: the extend kernels keep their MFMA accumulators in ordinary VGPRs
-# (they are rescaled by vector ops; in AGPRs every rescale costs copies both ways)
-FILE_FLAGS = {"pa_extend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Packed-FP32 selection off; MFMA accumulators in ordinary VGPRs: the kernels rescale them
+# with vector ops, and AGPR accumulators would cost copies both ways at every rescale (and
+# one more occupancy step for the 8-head decode engine)
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
+FILE_FLAGS = {}  # per translation unit extras
 
 
 def hipcc() -> str:

@@ -247,7 +247,7 @@ int default_balanced_workgroups() {
 // kMaxBalancedSeqs sequences.
 bool balanced_shape(const Common& c) {
   const int g = c.H / c.Hkv;
-  if (g != 1 && g != 2 && g != 4) return false;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return false;
   if (c.io != PA_F16 && c.io != PA_BF16) return false;
   if (c.kv != c.io && c.kv != PA_FP8_E4M3) return false;
   const int row = c.D * elem_bytes(c.kv);

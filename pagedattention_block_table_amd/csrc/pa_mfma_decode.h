@@ -122,11 +122,12 @@ struct MfmaGeo {
   static constexpr bool ok = (KV != kF32) && (CPR % 4 == 0) && (CPL >= 2) && (CPL % 2 == 0);
 };
 
-// Shapes the MFMA kernels take: 1, 2 or 4 query heads per KV head, io f16/bf16, KV = io
-// or fp8, and at least 128 bytes per token row.
+// Shapes the MFMA kernels take: 1, 2, 4 or 8 query heads per KV head (8 only with the V
+// product on the matrix cores), io f16/bf16, KV = io or fp8, and at least 128 bytes per
+// token row.
 template <int IO, int KV, int D, int G>
 constexpr bool mfma_supported() {
-  return (G == 1 || G == 2 || G == 4) && (IO == kF16 || IO == kBF16) && (KV == IO || KV == kFP8) &&
+  return (G == 1 || G == 2 || G == 4 || G == 8) && (IO == kF16 || IO == kBF16) && (KV == IO || KV == kFP8) &&
          MfmaGeo<KV, D>::ok;
 }
 
@@ -395,7 +396,7 @@ struct MfmaEngine {
   static constexpr int TILE_BYTES = BS * Geo::RB;
   using vec = typename Mma<IO>::vec;
   using Buf = ChunkBuf<KV, D, NT>;
-  static_assert(mfma_supported<IO, KV, D, G>(), "unsupported MFMA decode geometry");
+  static_assert(mfma_supported<IO, KV, D, G>() && G <= 4, "unsupported MFMA decode geometry");
   static_assert(BS >= 8 && BS <= 512 && (BS & (BS - 1)) == 0, "block size");
   static_assert(CT % BS == 0 || BS % CT == 0, "chunks and blocks nest");
 
@@ -556,7 +557,9 @@ struct VTileRegs {
 // through LDS as the A operand (row h = head h % G, four tokens per lane), split into a
 // high and a low 16-bit part so that the product keeps fp32 accuracy. The accumulators
 // hold the complete sums over the wave's tokens: lane l, register r of d-tile dt holds
-// head (4*(l/16) + r) % G, column 16*dt + l%16.
+// head (4*(l/16) + r) % G, column 16*dt + l%16. With G = 8 the heads form two halves of
+// four, each with its own query operand, scores and accumulators; the chunk's K and V
+// loads and its V tile serve both.
 template <int IO, int KV, int D, int BS, int G, bool DBG>
 struct MfmaPvEngine {
   using Geo = MfmaGeo<KV, D>;
@@ -573,10 +576,12 @@ struct MfmaPvEngine {
   static constexpr int VT_BYTES = 16 * VT_ROW * 2;
   static constexpr int P_BYTES = 2 * G * 16 * 2;
   static constexpr int kLdsBytes = VT_BYTES + P_BYTES;
+  static constexpr int HG = G < 4 ? G : 4;     // heads per half (rows of A repeat with period HG)
+  static constexpr int NH = G / HG;            // halves: 2 for G = 8, else 1
   using vec = typename Mma<IO>::vec;
   using M16 = Mma16<IO>;
   using v4 = typename M16::v4;
-  static_assert(G == 2 || G == 4, "group");
+  static_assert(G == 2 || G == 4 || G == 8, "group");
   static_assert(mfma_supported<IO, KV, D, G>(), "unsupported MFMA decode geometry");
   static_assert(NV >= 1 && 16 * RB % 1024 == 0, "V tile of whole wave loads");
 
@@ -593,9 +598,9 @@ struct MfmaPvEngine {
   const char* vbase;
   int64_t blk_stride;
   int win[2][NBC];
-  vec qa[Geo::NST];
+  vec qa[NH][Geo::NST];
   float m[G], l[G];
-  f32x4_t o[NDT];
+  f32x4_t o[NH][NDT];
   char* lds;  // this wave's V tile and probability tiles
 
   __device__ __forceinline__ MfmaPvEngine(int lane, char* wave_lds) : li(lane), lds(wave_lds) {}
@@ -635,14 +640,18 @@ struct MfmaPvEngine {
     vbase = (const char*)a.v_pool + (int64_t)g * TILE_BYTES;
     load_window(a, 0, win[0]);
     load_window(a, 1, win[1]);
-    load_q<IO, KV, D, G>(a, s, g, li, qa);
+    // half h2 holds heads g*G + 4*h2 + (0..HG-1): those of "KV head" g*NH + h2 at group HG
+#pragma unroll
+    for (int h2 = 0; h2 < NH; ++h2) load_q<IO, KV, D, HG>(a, s, g * NH + h2, li, qa[h2]);
 #pragma unroll
     for (int r = 0; r < G; ++r) {
       m[r] = -3.0e38f;
       l[r] = 0.f;
     }
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int h2 = 0; h2 < NH; ++h2)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[h2][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
   __device__ __forceinline__ void issue(const DecodeArgs& a, Buf& b, int k) {
@@ -746,17 +755,21 @@ struct MfmaPvEngine {
     // before those reads
     lds_exchange();
 
-    // scores of the G heads for token n (log2 units); register r holds head r % G
-    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < Geo::CPL; ++i)
-#pragma unroll
-      for (int hf = 0; hf < Geo::VEC / 8; ++hf)
-        c = Mma<IO>::mma(qa[i * (Geo::VEC / 8) + hf], k_operand<IO, KV>(b.kr[i], hf), c);
+    // scores of the G heads for token n (log2 units); register r of half h2 holds head
+    // h2*HG + r % HG
     const bool ok = c0 + li.n < t_end;
     float z[G];
 #pragma unroll
-    for (int r = 0; r < G; ++r) z[r] = ok ? c[r] * a.q_mul : -INFINITY;
+    for (int h2 = 0; h2 < NH; ++h2) {
+      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < Geo::CPL; ++i)
+#pragma unroll
+        for (int hf = 0; hf < Geo::VEC / 8; ++hf)
+          c = Mma<IO>::mma(qa[h2][i * (Geo::VEC / 8) + hf], k_operand<IO, KV>(b.kr[i], hf), c);
+#pragma unroll
+      for (int r = 0; r < HG; ++r) z[h2 * HG + r] = ok ? c[r] * a.q_mul : -INFINITY;
+    }
 
     float mx[G];
     bool raise = false;
@@ -780,9 +793,11 @@ struct MfmaPvEngine {
         l[r] *= alpha[r];
       }
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+      for (int h2 = 0; h2 < NH; ++h2)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[dt][r] *= alpha[r % G];
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[h2][dt][r] *= alpha[h2 * HG + r % HG];
     }
 
     // probabilities -> LDS as A operands [hi/lo][head][token]
@@ -799,9 +814,13 @@ struct MfmaPvEngine {
       }
     }
     lds_exchange();
-    const int h = li.n % G;
-    const v4 ahi = *(const v4*)(pt + h * 16 + 4 * li.lg);
-    const v4 alo = *(const v4*)(pt + G * 16 + h * 16 + 4 * li.lg);
+    v4 ahi[NH], alo[NH];
+#pragma unroll
+    for (int h2 = 0; h2 < NH; ++h2) {
+      const int h = h2 * HG + li.n % HG;
+      ahi[h2] = *(const v4*)(pt + h * 16 + 4 * li.lg);
+      alo[h2] = *(const v4*)(pt + G * 16 + h * 16 + 4 * li.lg);
+    }
 
     // O[h][16dt + i] += sum_t P[h][t] V[t][16dt + i]
     const int vrow = 4 * li.lg + (li.n >> 2);
@@ -811,8 +830,11 @@ struct MfmaPvEngine {
       const v4 bv = __builtin_bit_cast(
           v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                   (__attribute__((address_space(3))) i16x4_t*)(vt + vrow * VT_ROW + 16 * dt + vcol)));
-      o[dt] = M16::mma(ahi, bv, o[dt]);
-      o[dt] = M16::mma(alo, bv, o[dt]);
+#pragma unroll
+      for (int h2 = 0; h2 < NH; ++h2) {
+        o[h2][dt] = M16::mma(ahi[h2], bv, o[h2][dt]);
+        o[h2][dt] = M16::mma(alo[h2], bv, o[h2][dt]);
+      }
     }
   }
 
@@ -838,9 +860,11 @@ struct MfmaPvEngine {
     for (int r = 0; r < G; ++r) l[r] = group_sum<16>(l[r]);
     if (li.lg == 0) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+      for (int h2 = 0; h2 < NH; ++h2)
 #pragma unroll
-        for (int r = 0; r < G; ++r) sm_o[wave][r][16 * dt + li.n] = o[dt][r];
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int r = 0; r < HG; ++r) sm_o[wave][h2 * HG + r][16 * dt + li.n] = o[h2][dt][r];
     }
     if (li.lane == 0) {
 #pragma unroll
@@ -861,7 +885,9 @@ struct MfmaPvEngine {
 #endif
 template <int IO, int KV, int D, int BS, int G, bool DBG>
 struct EngineFor {
-  static constexpr bool pv = PA_MFMA_PV && (G == 2 || G == 4) && KV != kFP8;
+  // 8 heads per KV head always take the matrix-core V product (eight FMAs per V element
+  // on the vector ALUs would bound the kernel)
+  static constexpr bool pv = (PA_MFMA_PV && (G == 2 || G == 4) && KV != kFP8) || G == 8;
   using type = typename std::conditional<pv, MfmaPvEngine<IO, KV, D, BS, G, DBG>,
                                          MfmaEngine<IO, KV, D, BS, G, PA_MFMA_TILES, DBG>>::type;
   static constexpr int lds_bytes = pv ? MfmaPvEngine<IO, KV, D, BS, (pv ? G : 4), DBG>::kLdsBytes : 16;

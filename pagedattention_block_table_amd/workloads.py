@@ -107,6 +107,10 @@ VARIANTS = {
     "shared_prefix_bf16_bs256": CONFIGS[2].replace(name="shared_prefix_bf16_bs256", block_size=256),
     "long_ctx_fp16_bs512": CONFIGS[3].replace(name="long_ctx_fp16_bs512", block_size=512, pool_blocks=512),
     "mixed_fp8_bs256": CONFIGS[4].replace(name="mixed_fp8_bs256", block_size=256),
+    # a larger query group: the LLaMA-2-70B attention shape ([P2] §1 benchmarks that model),
+    # 64 query heads over 8 KV heads, bf16, 64 requests of 1K-3K cached tokens
+    "llama70b_gqa8_bf16": Spec("llama70b_gqa8_bf16", 64, 64, 8, 128, 16, "bf16", "bf16",
+                               ("uniform_sum", ((1024, 3072),)), seed=1005),
 }
 
 

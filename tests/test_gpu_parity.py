@@ -203,6 +203,25 @@ def test_large_block_trace_bit_exact(cfg, BS):
     _trace_check(b, 0, 7)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_gqa8_group_modes_and_trace(kv):
+    """Eight query heads per KV head (the LLaMA-2-70B shape) on the matrix-core engine:
+    every mode against the oracle, and every cached position read once."""
+    spec = W.VARIANTS["llama70b_gqa8_bf16"].replace(name=f"gqa8_small_{kv}", num_seqs=5, kv_dtype=kv,
+                                                    lengths=("fixed", (1, 37, 300, 1000, 16)), seed=4242)
+    b = W.make_batch(spec)
+    log(f"[gqa8] {spec.name}")
+    dev = to_device(b)
+    for mode, P in (("direct", None), ("partitioned", 64), ("balanced", 3), ("balanced", 0)):
+        if mode == "balanced":
+            got = to_f64(run(b, dev, mode, num_workgroups=P))
+        else:
+            got = to_f64(run(b, dev, mode, P))
+        check_against_oracle(b, got, io_rounding=True)
+    _trace_check(b, 0, 0)
+    _trace_check(b, 0, 7)
+
+
 def test_length_one_returns_value_row_exactly():
     spec = W.Spec("len1", 3, 8, 2, 128, 16, "f32", "f32", ("fixed", (1, 1, 1)), seed=11)
     b = W.make_batch(spec)
