@@ -518,6 +518,98 @@ decode_kernel(const DecodeArgs a) {
   }
 }
 
+// The vector path as an engine of the chunk schedulers (the balanced grid): the same
+// process_chunk math on chunks of ValuEngine::CT tokens counted from token `base`,
+// chunk k0 + rotated(wave + k*nw, rot, len) for the wave's k-th step.
+template <int IO, int KV, int D, int BS, int G, bool DBG>
+struct ValuEngine {
+  using Geo = Geometry<KV, D, BS, G>;
+  static constexpr int VEC = Geo::VEC, LPT = Geo::LPT, SB = Geo::SB;
+  static constexpr int U = SB >= 32 ? 1 : 32 / SB;  // (sub-)blocks per step
+  static constexpr int CT = U * SB;                  // 32 tokens
+  static_assert(Geo::ok, "unsupported geometry");
+
+  int lane, r, c;
+  int s, g, t_end, j_end, base, k0, len, rot, wave, nw;
+  const int32_t* bt;
+  const char* kbase;
+  const char* vbase;
+  int64_t blk_stride;
+  float qf[G][VEC];
+  RowState<G, VEC> st;
+
+  __device__ __forceinline__ explicit ValuEngine(int l) : lane(l), r(l / LPT), c(l % LPT) {}
+
+  __device__ __forceinline__ void begin(const DecodeArgs& a, int s_, int g_, int t_end_, int base_,
+                                        int k0_, int len_, int rot_, int wave_, int nw_) {
+    s = s_;
+    g = g_;
+    t_end = t_end_;
+    j_end = (t_end + SB - 1) / SB;
+    base = base_;
+    k0 = k0_;
+    len = len_;
+    rot = rot_;
+    wave = wave_;
+    nw = nw_;
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      const int64_t qb = ((int64_t)s * a.num_heads + (int64_t)g * G + gi) * D + c * VEC;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) qf[gi][e] = load_io<IO>(a.q, qb + e) * a.q_mul;
+      st.m[gi] = -3.0e38f;
+      st.l[gi] = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) st.acc[gi][e] = 0.f;
+    }
+    bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    blk_stride = (int64_t)a.num_kv_heads * Geo::TILE;
+    kbase = (const char*)a.k_pool + (int64_t)g * Geo::TILE;
+    vbase = (const char*)a.v_pool + (int64_t)g * Geo::TILE;
+  }
+
+  __device__ __forceinline__ void run(const DecodeArgs& a) {
+    const int nwc = wave < len ? (len - wave + nw - 1) / nw : 0;
+    for (int k = 0; k < nwc; ++k) {
+      int ci = wave + k * nw + rot;
+      ci = ci >= len ? ci - len : ci;
+      const int j0 = (base + CT * (k0 + ci)) / SB;
+      if ((j0 + U) * SB <= t_end) {
+        process_chunk<IO, KV, D, BS, G, U, false, DBG>(a, bt, kbase, vbase, blk_stride, j0, j_end, t_end, r, c,
+                                                       s, g, qf, st);
+      } else {
+        process_chunk<IO, KV, D, BS, G, U, true, DBG>(a, bt, kbase, vbase, blk_stride, j0, j_end, t_end, r, c,
+                                                      s, g, qf, st);
+      }
+    }
+  }
+
+  template <int NW>
+  __device__ __forceinline__ void finish(float (&sm_m)[NW][G], float (&sm_l)[NW][G],
+                                         float (&sm_o)[NW][G][D]) {
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      const float M = rows_max<LPT>(st.m[gi]);
+      const float f = __builtin_amdgcn_exp2f(st.m[gi] - M);
+      st.m[gi] = M;
+      st.l[gi] = rows_sum<LPT>(st.l[gi] * f);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) st.acc[gi][e] = rows_sum<LPT>(st.acc[gi][e] * f);
+    }
+    if (r == 0) {
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) sm_o[wave][gi][c * VEC + e] = st.acc[gi][e];
+        if (c == 0) {
+          sm_m[wave][gi] = st.m[gi];
+          sm_l[wave][gi] = st.l[gi];
+        }
+      }
+    }
+  }
+};
+
 }  // namespace pa
 
 #include "pa_mfma_decode.h"

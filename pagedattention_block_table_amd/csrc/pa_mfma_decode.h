@@ -883,13 +883,20 @@ struct MfmaPvEngine {
 #ifndef PA_MFMA_PV
 #define PA_MFMA_PV 1
 #endif
+#ifndef PA_BAL_VALU
+#define PA_BAL_VALU 1
+#endif
 template <int IO, int KV, int D, int BS, int G, bool DBG>
 struct EngineFor {
   // 8 heads per KV head always take the matrix-core V product (eight FMAs per V element
-  // on the vector ALUs would bound the kernel)
+  // on the vector ALUs would bound the kernel); one head per KV head takes the vector
+  // engine (whole 1 KiB rows per wave load, no MFMA rows wasted)
   static constexpr bool pv = (PA_MFMA_PV && (G == 2 || G == 4) && KV != kFP8) || G == 8;
-  using type = typename std::conditional<pv, MfmaPvEngine<IO, KV, D, BS, G, DBG>,
-                                         MfmaEngine<IO, KV, D, BS, G, PA_MFMA_TILES, DBG>>::type;
+  static constexpr bool valu = PA_BAL_VALU && G == 1;
+  using type = typename std::conditional<
+      valu, ValuEngine<IO, KV, D, BS, G, DBG>,
+      typename std::conditional<pv, MfmaPvEngine<IO, KV, D, BS, G, DBG>,
+                                MfmaEngine<IO, KV, D, BS, G, PA_MFMA_TILES, DBG>>::type>::type;
   static constexpr int lds_bytes = pv ? MfmaPvEngine<IO, KV, D, BS, (pv ? G : 4), DBG>::kLdsBytes : 16;
 };
 
@@ -898,6 +905,12 @@ template <int IO, int KV, int D, int BS, int G, int NT, bool DBG>
 struct EngineMaker<MfmaEngine<IO, KV, D, BS, G, NT, DBG>> {
   static __device__ __forceinline__ MfmaEngine<IO, KV, D, BS, G, NT, DBG> make(int lane, char*) {
     return MfmaEngine<IO, KV, D, BS, G, NT, DBG>(lane);
+  }
+};
+template <int IO, int KV, int D, int BS, int G, bool DBG>
+struct EngineMaker<ValuEngine<IO, KV, D, BS, G, DBG>> {
+  static __device__ __forceinline__ ValuEngine<IO, KV, D, BS, G, DBG> make(int lane, char*) {
+    return ValuEngine<IO, KV, D, BS, G, DBG>(lane);
   }
 };
 template <int IO, int KV, int D, int BS, int G, bool DBG>
