@@ -326,19 +326,29 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_kernel(const ExtendArgs
 // per row so that the K operand reads (16 rows, same column) and the transposed V reads
 // (4 rows, 2 pieces) hit distinct banks.
 
-constexpr int kDmaStages = 4;
-constexpr int kDmaRows = 32 * kExtWaves;  // query rows per workgroup (two tiles per wave)
+#ifndef PA_EXT_STAGES
+#define PA_EXT_STAGES 4
+#endif
+constexpr int kDmaStages = PA_EXT_STAGES;  // chunks in the LDS ring (kDmaStages - 1 in flight)
+constexpr int kDmaRows = 128;  // query rows per workgroup: NW waves of 16 * NT rows
 
-template <int D>
+// waves per workgroup of the ring kernel (16-row query tiles per wave = 128 / (16 NW));
+// head_dim 64 keeps four waves so that every thread issues a whole copy per tile
+#ifndef PA_EXT_WAVES
+#define PA_EXT_WAVES 8
+#endif
+template <int D> constexpr int dma_waves() { return D == 128 ? PA_EXT_WAVES : 4; }
+
+template <int D, int NW>
 struct DmaGeo {
   static constexpr int PPR = D * 2 / 16;                    // 16-byte pieces per row
   static constexpr int ROW_B = D * 2;
   static constexpr int TILE_B = kExtChunk * ROW_B;          // K (or V) of one chunk
   static constexpr int STAGE_B = 2 * TILE_B;
-  static constexpr int PPT = kExtChunk * PPR / (kExtWaves * 64);  // copies per thread per tile
+  static constexpr int PPT = kExtChunk * PPR / (NW * 64);   // copies per thread per tile
   static constexpr int NKS = D / 32;
   static constexpr int NDT = D / 16;
-  static_assert(PPT >= 1 && kExtChunk * PPR % (kExtWaves * 64) == 0, "whole copies");
+  static_assert(PPT >= 1 && kExtChunk * PPR % (NW * 64) == 0, "whole copies");
   static __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
   static __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
 };
@@ -354,13 +364,15 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
 }
 
-template <int IO, int D, int G>
-__global__ void __launch_bounds__(kExtWaves * 64) extend_dma_kernel(const ExtendArgs a) {
-  using Geo = DmaGeo<D>;
+template <int IO, int D, int G, int NW>
+__global__ void __launch_bounds__(NW * 64) extend_dma_kernel(const ExtendArgs a) {
+  using Geo = DmaGeo<D, NW>;
   using vec = typename Mma<IO>::vec;
   using M16 = Mma16<IO>;
   constexpr int QT = kDmaRows / G;  // new tokens per workgroup
-  constexpr int NT = 2;             // query tiles per wave
+  constexpr int NT = kDmaRows / (16 * NW);  // query tiles per wave
+  constexpr int RW = 16 * NT;               // query rows per wave
+  constexpr int NTH = NW * 64;
   constexpr int CPS = 2 * Geo::PPT; // copies per thread per stage
   // probabilities as f16 keep 11 significant bits (error <= 2^-12 relative, about 1e-3 of
   // the largest |V| at most); bf16 keeps 8, so there they go as high + low halves
@@ -392,19 +404,19 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_dma_kernel(const Extend
   const int n = lane & 15;
   const int lq = lane >> 4;
 
-  // query rows of this lane: tile tq holds row 32 * wave + 16 * tq + n
+  // query rows of this lane: tile tq holds row RW * wave + 16 * tq + n
   int ti[NT], hh[NT], pos[NT];
   bool row_ok[NT];
 #pragma unroll
   for (int tq = 0; tq < NT; ++tq) {
-    const int row = 32 * wave + 16 * tq + n;
+    const int row = RW * wave + 16 * tq + n;
     ti[tq] = i0 + row / G;
     hh[tq] = g * G + row % G;
     row_ok[tq] = ti[tq] < i_end;
     pos[tq] = p0 + ti[tq];
   }
-  const int w_first = i0 + (32 * wave) / G;
-  const int w_last = min(i_end, i0 + (32 * wave + 31) / G + 1) - 1;
+  const int w_first = i0 + (RW * wave) / G;
+  const int w_last = min(i_end, i0 + (RW * wave + RW - 1) / G + 1) - 1;
   const bool wave_live = w_first < i_end;
   const int wp_min = p0 + w_first;
   const int wp_max = p0 + w_last;
@@ -426,8 +438,7 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_dma_kernel(const Extend
   wait_vm<0>();
 
   // copy geometry: thread piece u sits at physical slot P = 256u + 64 wave + lane of a tile
-  const __attribute__((address_space(4))) int32_t* btc =
-      (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)s * a.max_blocks_per_seq);
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   const int bs_mask = (1 << a.bs_shift) - 1;
   const int64_t tile_bytes = (int64_t)Geo::ROW_B << a.bs_shift;
   const int64_t blk_stride = tile_bytes * a.num_kv_heads;
@@ -437,23 +448,42 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_dma_kernel(const Extend
   int crow[Geo::PPT], ck[Geo::PPT], cv[Geo::PPT];
 #pragma unroll
   for (int u = 0; u < Geo::PPT; ++u) {
-    const int P = 256 * u + 64 * wave + lane;
+    const int P = NTH * u + 64 * wave + lane;
     crow[u] = P / Geo::PPR;
     const int pc = P % Geo::PPR;
     ck[u] = pc ^ Geo::swz_k(crow[u]);
     cv[u] = pc ^ Geo::swz_v(crow[u]);
   }
-  auto issue = [&](int c) {
-    const int buf = c % kDmaStages;
+  // Block ids of the copies, 64 chunks at a time: lane l of win[u] holds the block of
+  // copy u of chunk 64 * wb + l (the rows of one copy instruction lie in one block). A
+  // window is loaded when the copies first need it and waited for at once (one drain of
+  // the copies in flight per 64 chunks), so no table load sits on the per-chunk path.
+  int win[Geo::PPT];
+  int wb = -1;
+  auto load_window = [&](int w) {
 #pragma unroll
     for (int u = 0; u < Geo::PPT; ++u) {
-      const int first = c * kExtChunk + (256 * u + 64 * wave) / Geo::PPR;  // uniform
-      const int bidx = __builtin_amdgcn_readfirstlane(min(first, L - 1) >> a.bs_shift);
+      const int cc = 64 * w + lane;
+      int b = 0;
+      if (cc < nch) b = bt[min(cc * kExtChunk + (NTH * u + 64 * wave) / Geo::PPR, L - 1) >> a.bs_shift];
       // contract: 0 <= b < num_blocks; clamp so that a bad table never reads outside
-      const int b = min(max(btc[bidx], 0), a.num_blocks - 1);
+      win[u] = min(max(b, 0), a.num_blocks - 1);
+    }
+    asm volatile("" ::: "memory");
+    wait_vm<0>();
+  };
+  auto issue = [&](int c) {
+    const int buf = c % kDmaStages;
+    if ((c >> 6) != wb) {  // uniform
+      wb = c >> 6;
+      load_window(wb);
+    }
+#pragma unroll
+    for (int u = 0; u < Geo::PPT; ++u) {
+      const int b = __builtin_amdgcn_readlane(win[u], c & 63);
       const int ts = min(c * kExtChunk + crow[u], L - 1);
       const int64_t roff = (int64_t)b * blk_stride + (int64_t)(ts & bs_mask) * Geo::ROW_B;
-      const uint32_t dst = lds0 + buf * Geo::STAGE_B + (256 * u + 64 * wave) * 16;
+      const uint32_t dst = lds0 + buf * Geo::STAGE_B + (NTH * u + 64 * wave) * 16;
       lds_copy16(kb + roff + 16 * ck[u], dst);
       lds_copy16(vb + roff + 16 * cv[u], dst + Geo::TILE_B);
     }
@@ -476,8 +506,11 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_dma_kernel(const Extend
   for (int c = 0; c < nch; ++c) {
     // chunk c has landed once at most the copies of the chunks issued after it remain
     const int newer = min(kDmaStages - 2, nch - 1 - c);
-    if (newer >= 2) wait_vm<2 * CPS>();
-    else if (newer == 1) wait_vm<CPS>();
+    static_assert(kDmaStages >= 2 && kDmaStages <= 6, "ring depth");
+    if (kDmaStages >= 6 && newer >= 4) wait_vm<(kDmaStages >= 6 ? 4 : 0) * CPS>();
+    else if (kDmaStages >= 5 && newer >= 3) wait_vm<(kDmaStages >= 5 ? 3 : 0) * CPS>();
+    else if (kDmaStages >= 4 && newer >= 2) wait_vm<(kDmaStages >= 4 ? 2 : 0) * CPS>();
+    else if (newer >= 1) wait_vm<CPS>();
     else wait_vm<0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -602,11 +635,12 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_dma_kernel(const Extend
 template <int IO, int KV, int D>
 int launch_ext_g(const ExtendArgs& a, int G, int grid, hipStream_t st) {
   if constexpr (KV == IO) {
+    constexpr int NW = dma_waves<D>();
     switch (G) {
-      case 1: hipLaunchKernelGGL((extend_dma_kernel<IO, D, 1>), dim3(grid), dim3(kExtWaves * 64), 0, st, a); break;
-      case 2: hipLaunchKernelGGL((extend_dma_kernel<IO, D, 2>), dim3(grid), dim3(kExtWaves * 64), 0, st, a); break;
-      case 4: hipLaunchKernelGGL((extend_dma_kernel<IO, D, 4>), dim3(grid), dim3(kExtWaves * 64), 0, st, a); break;
-      case 8: hipLaunchKernelGGL((extend_dma_kernel<IO, D, 8>), dim3(grid), dim3(kExtWaves * 64), 0, st, a); break;
+      case 1: hipLaunchKernelGGL((extend_dma_kernel<IO, D, 1, NW>), dim3(grid), dim3(NW * 64), 0, st, a); break;
+      case 2: hipLaunchKernelGGL((extend_dma_kernel<IO, D, 2, NW>), dim3(grid), dim3(NW * 64), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((extend_dma_kernel<IO, D, 4, NW>), dim3(grid), dim3(NW * 64), 0, st, a); break;
+      case 8: hipLaunchKernelGGL((extend_dma_kernel<IO, D, 8, NW>), dim3(grid), dim3(NW * 64), 0, st, a); break;
       default: return PA_ERR_UNSUPPORTED;
     }
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
