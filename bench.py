@@ -34,7 +34,7 @@ METRIC = "paged-attn decode KV GB/s read and % of MI355X HBM peak; seqs·tokens/
 DEFAULT_MODE = {0: "direct", 1: "direct", 2: "direct", 3: "balanced", 4: "balanced",
                 "llama7b_fp16_bs128": "direct", "shared_prefix_bf16_bs256": "direct",
                 "long_ctx_fp16_bs512": "balanced", "mixed_fp8_bs256": "balanced",
-                "llama70b_gqa8_bf16": "direct"}
+                "llama70b_gqa8_bf16": "direct", "d256_gqa2_bf16": "direct"}
 KERNEL_SOURCES = ["pagedattention_block_table_amd/csrc/pa_decode_impl.h",
                   "pagedattention_block_table_amd/csrc/pa_mfma_decode.h",
                   "pagedattention_block_table_amd/csrc/pa_api.hip"]

@@ -75,7 +75,8 @@ typedef enum {
   PA_ERR_LAUNCH = -4       /* the HIP launch itself failed */
 } pa_status;
 
-/* Supported shapes: head_dim in {64, 128}; block_size in {8, 16, 32, 64, 128, 256, 512}
+/* Supported shapes: head_dim in {64, 128, 256} (256 on the vector kernel only, single
+ * pass or partitioned); block_size in {8, 16, 32, 64, 128, 256, 512}
  * ([P1] §2 and [P3] use 16; [P2] §3.1 uses 256 by default, 128 for short and 512 for
  * long texts; with fp8 and head_dim 64, block_size >= 16); num_heads / num_kv_heads in
  * {1, 2, 4, 8};
@@ -178,7 +179,7 @@ int pa_debug_trace(const void* q, const void* k_pool, const void* v_pool,
  * +-448, NaN kept as NaN. The caller allocates the blocks (the table entries must exist);
  * a token whose sequence, position or block lies outside the tables or the pool is
  * skipped. Pointers to k_new, v_new and the pools must be 16-byte aligned; head_dim in
- * {64, 128}, block_size in {8, 16, ..., 512} (powers of two). Asynchronous on `stream`;
+ * {64, 128, 256}, block_size in {8, 16, ..., 512} (powers of two). Asynchronous on `stream`;
  * allocates nothing. */
 int pa_append_kv(const void* k_new, const void* v_new, const int32_t* seq_ids,
                  const int32_t* positions, int num_tokens, const int32_t* block_tables,

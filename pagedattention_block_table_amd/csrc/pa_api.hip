@@ -152,7 +152,7 @@ int validate(const Common& c) {
     return PA_ERR_INVALID;
   if ((int64_t)c.MB * c.BS > INT_MAX / 2) return PA_ERR_INVALID;
   if (c.kv != c.io && c.kv != PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
-  if (c.D != 64 && c.D != 128) return PA_ERR_UNSUPPORTED;
+  if (c.D != 64 && c.D != 128 && c.D != 256) return PA_ERR_UNSUPPORTED;
   if (c.BS != 8 && c.BS != 16 && c.BS != 32 && c.BS != 64 && c.BS != 128 && c.BS != 256 && c.BS != 512)
     return PA_ERR_UNSUPPORTED;
   if (!is_pow_group(c.H / c.Hkv)) return PA_ERR_UNSUPPORTED;
@@ -184,8 +184,10 @@ template <int IO>
 int launch_merge_io(int D, const MergeArgs& m, int grid, hipStream_t st) {
   if (D == 64) {
     hipLaunchKernelGGL((merge_kernel<IO, 64>), dim3(grid), dim3(256), 0, st, m);
-  } else {
+  } else if (D == 128) {
     hipLaunchKernelGGL((merge_kernel<IO, 128>), dim3(grid), dim3(256), 0, st, m);
+  } else {
+    hipLaunchKernelGGL((merge_kernel<IO, 256>), dim3(grid), dim3(256), 0, st, m);
   }
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
@@ -251,7 +253,7 @@ bool balanced_shape(const Common& c) {
   if (c.io != PA_F16 && c.io != PA_BF16) return false;
   if (c.kv != c.io && c.kv != PA_FP8_E4M3) return false;
   const int row = c.D * elem_bytes(c.kv);
-  if (row != 128 && row != 256) return false;
+  if (c.D > 128 || (row != 128 && row != 256)) return false;
   return c.S <= kMaxBalancedSeqs;
 }
 

@@ -119,6 +119,7 @@ int launch_append_d(const AppendArgs& a, int D, int BS, hipStream_t st) {
     switch (D) {
       case 64: return launch_append_bs<SRC, KV, 64>(a, BS, st);
       case 128: return launch_append_bs<SRC, KV, 128>(a, BS, st);
+      case 256: return launch_append_bs<SRC, KV, 256>(a, BS, st);
       default: return PA_ERR_UNSUPPORTED;
     }
   }
@@ -166,7 +167,7 @@ extern "C" int pa_append_kv(const void* k_new, const void* v_new, const int32_t*
       return PA_ERR_INVALID;
     if (((uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_pool | (uintptr_t)v_pool) & 15u)
       return PA_ERR_INVALID;
-    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PA_ERR_UNSUPPORTED;
     if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64 && block_size != 128 &&
         block_size != 256 && block_size != 512)
       return PA_ERR_UNSUPPORTED;

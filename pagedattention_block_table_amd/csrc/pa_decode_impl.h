@@ -236,16 +236,18 @@ __device__ __forceinline__ int xcd_unit(int i, int n) {
 // the decode kernel
 // ---------------------------------------------------------------------------------
 
-// Blocks larger than 32 tokens are walked as 32-token sub-blocks: sub-block j covers
-// tokens 32j .. 32j+31, lies in logical block j / SPB at row 32 (j % SPB), and is itself
-// one contiguous run of its (block, kv-head) tile.
+// Blocks larger than SB tokens (32, or 16 / 8 for 512- / 1024-byte rows) are walked as
+// SB-token sub-blocks: sub-block j covers tokens SB j .. SB j + SB - 1, lies in logical
+// block j / SPB at row SB (j % SPB), and is itself one contiguous run of its tile.
 template <int KV, int D, int BS, int G_>
 struct Geometry {
   static constexpr int E = ElemBytes<KV>::value;
   static constexpr int VEC = 16 / E;           // elements per lane load
   static constexpr int LPT = D / VEC;          // lanes per token row
   static constexpr int TPL = 64 / LPT;         // token rows per wave load
-  static constexpr int SB = BS < 32 ? BS : 32; // tokens per (sub-)block step
+  // tokens per (sub-)block step: at most 32, and at most 8 wave loads (head_dim 256)
+  static constexpr int SB_MAX = 8 * TPL < 32 ? 8 * TPL : 32;
+  static constexpr int SB = BS < SB_MAX ? BS : SB_MAX;
   static constexpr int SPB = BS / SB;          // sub-blocks per block
   static constexpr int NL = SB / TPL;          // wave loads per sub-block
   static constexpr int ROW_BYTES = D * E;
@@ -525,8 +527,8 @@ template <int IO, int KV, int D, int BS, int G, bool DBG>
 struct ValuEngine {
   using Geo = Geometry<KV, D, BS, G>;
   static constexpr int VEC = Geo::VEC, LPT = Geo::LPT, SB = Geo::SB;
-  static constexpr int U = SB >= 32 ? 1 : 32 / SB;  // (sub-)blocks per step
-  static constexpr int CT = U * SB;                  // 32 tokens
+  static constexpr int U = SB >= Geo::SB_MAX ? 1 : Geo::SB_MAX / SB;  // (sub-)blocks per step
+  static constexpr int CT = U * SB;                                      // SB_MAX tokens
   static_assert(Geo::ok, "unsupported geometry");
 
   int lane, r, c;
@@ -640,9 +642,12 @@ struct LaunchSpec {
 
 template <int IO, int KV, int D, int BS, int G>
 constexpr int pick_unroll() {
-  // Consecutive (sub-)blocks per wave iteration: about PA_CHUNK_TOKENS tokens, at least one.
-  constexpr int SB = Geometry<KV, D, BS, G>::SB;
-  return SB >= PA_CHUNK_TOKENS ? 1 : PA_CHUNK_TOKENS / SB;
+  // Consecutive (sub-)blocks per wave iteration: SB_MAX tokens (at most PA_CHUNK_TOKENS
+  // and at most 8 wave loads of K), whatever the block size, so that the token order of a
+  // wave and hence the result does not depend on the block size.
+  using Geo = Geometry<KV, D, BS, G>;
+  constexpr int CT = Geo::SB_MAX < PA_CHUNK_TOKENS ? Geo::SB_MAX : PA_CHUNK_TOKENS;
+  return Geo::SB >= CT ? 1 : CT / Geo::SB;
 }
 
 template <int IO, int KV, int D, int BS, int G>
@@ -726,6 +731,7 @@ int launch_decode(const LaunchSpec& ls) {
   switch (ls.head_dim) {
     case 64: return launch_bs<IO, KV, 64, LARGE>(ls);
     case 128: return launch_bs<IO, KV, 128, LARGE>(ls);
+    case 256: return launch_bs<IO, KV, 256, LARGE>(ls);
     default: return PA_ERR_UNSUPPORTED;
   }
 }

@@ -123,12 +123,12 @@ struct MfmaGeo {
 };
 
 // Shapes the MFMA kernels take: 1, 2, 4 or 8 query heads per KV head (8 only with the V
-// product on the matrix cores), io f16/bf16, KV = io or fp8, and at least 128 bytes per
-// token row.
+// product on the matrix cores), io f16/bf16, KV = io or fp8, head_dim 64 or 128 and at
+// least 128 bytes per token row.
 template <int IO, int KV, int D, int G>
 constexpr bool mfma_supported() {
   return (G == 1 || G == 2 || G == 4 || G == 8) && (IO == kF16 || IO == kBF16) && (KV == IO || KV == kFP8) &&
-         MfmaGeo<KV, D>::ok;
+         D <= 128 && MfmaGeo<KV, D>::ok;
 }
 
 // Order in which a wave visits the `len` chunks of a segment: from a per-sequence

@@ -111,6 +111,9 @@ VARIANTS = {
     # 64 query heads over 8 KV heads, bf16, 64 requests of 1K-3K cached tokens
     "llama70b_gqa8_bf16": Spec("llama70b_gqa8_bf16", 64, 64, 8, 128, 16, "bf16", "bf16",
                                ("uniform_sum", ((1024, 3072),)), seed=1005),
+    # head_dim 256 (16 query heads over 8 KV heads, bf16, 32 requests of 0.5K-2K tokens)
+    "d256_gqa2_bf16": Spec("d256_gqa2_bf16", 32, 16, 8, 256, 16, "bf16", "bf16",
+                           ("uniform_sum", ((512, 2048),)), seed=1006),
 }
 
 

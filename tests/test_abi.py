@@ -189,6 +189,7 @@ def test_append_rejects():
     assert call(kv=_lib.PA_FP8_E4M3, vs=float("nan")) == _lib.PA_ERR_INVALID
     assert call(kp=FAKE + 4) == _lib.PA_ERR_INVALID
     assert call(D=96) == _lib.PA_ERR_UNSUPPORTED
+    assert call(D=512) == _lib.PA_ERR_UNSUPPORTED
     assert call(BS=48) == _lib.PA_ERR_UNSUPPORTED
     assert call(BS=1024) == _lib.PA_ERR_UNSUPPORTED
     assert call(T=0) == _lib.PA_OK                                 # nothing to write, nothing enqueued

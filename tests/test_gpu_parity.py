@@ -145,7 +145,8 @@ EDGE_DTYPES = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("f16", "fp8_e4
 
 
 @pytest.mark.parametrize("io,kv", EDGE_DTYPES)
-@pytest.mark.parametrize("D,BS,G", [(64, 16, 1), (128, 8, 2), (128, 16, 4), (64, 32, 8), (128, 32, 8)])
+@pytest.mark.parametrize("D,BS,G", [(64, 16, 1), (128, 8, 2), (128, 16, 4), (64, 32, 8), (128, 32, 8),
+                                    (256, 8, 1), (256, 16, 2), (256, 64, 8)])
 def test_edge_shapes(io, kv, D, BS, G):
     """Empty, single-token, block-boundary and ragged lengths across dtype pairs, head
     dims, block sizes and group sizes, in both modes."""
@@ -338,3 +339,15 @@ def test_full_size(cfg, mode):
     pairs = _sample_pairs(b, cfg)
     err = check_against_oracle(b, got, pairs=pairs)
     log(f"  max|err|={err:.3e} over {'all' if pairs is None else len(pairs)} (s,h)")
+
+
+def test_balanced_beyond_its_sequence_limit_falls_back():
+    """More sequences than the balanced scheduler's prefix sums hold (4096): the call takes
+    the single-pass kernel and still matches the oracle."""
+    spec = W.Spec("many_seqs", 4100, 8, 2, 64, 16, "bf16", "bf16", ("uniform_sum", ((1, 40),)), seed=77)
+    b = W.make_batch(spec)
+    log(f"[many] S={spec.num_seqs}")
+    dev = to_device(b)
+    got = to_f64(run(b, dev, "balanced"))
+    pairs = [(s, h) for s in range(0, spec.num_seqs, 37) for h in range(spec.num_heads)]
+    check_against_oracle(b, got, pairs=pairs, io_rounding=True)

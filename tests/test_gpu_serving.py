@@ -178,3 +178,21 @@ def test_serving_loop(kv):
     assert total_copies >= 3                                  # every fork copied its partial block
     lp.check_pools()
     lp.bm.close()
+
+
+def test_copy_blocks_direct():
+    """pa_copy_blocks copies whole blocks of K and V (every byte, whatever their fill) and
+    skips pairs with an id outside the pool or src == dst."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(3)
+    kp = torch.randn((12, 2, 16, 64), generator=g, device="cuda").to(torch.bfloat16)
+    vp = torch.randn((12, 2, 16, 64), generator=g, device="cuda").to(torch.bfloat16)
+    k0, v0 = kp.clone(), vp.clone()
+    pairs = torch.tensor([[1, 5], [2, 2], [3, 12], [-1, 4], [7, 0]], dtype=torch.int32, device="cuda")
+    pa.pa_copy_blocks(kp, vp, pairs)
+    torch.cuda.synchronize()
+    want_k, want_v = k0.clone(), v0.clone()
+    want_k[5], want_v[5] = k0[1], v0[1]
+    want_k[0], want_v[0] = k0[7], v0[7]
+    assert torch.equal(kp.view(torch.int16), want_k.view(torch.int16))
+    assert torch.equal(vp.view(torch.int16), want_v.view(torch.int16))
