@@ -64,12 +64,44 @@ class Loop:
                         torch.from_numpy(tables).cuda(), self.kp, self.vp,
                         k_scale=self.ks, v_scale=self.vs)
 
-    def add(self, tokens):
+    def add(self, tokens, prefill_check=False):
         h, cached = self.bm.add_sequence(tokens)
         self.tokens[h] = list(tokens)
         self.rows[h] = [_row(tokens[:p + 1]).astype(np.float16).astype(np.float32) for p in range(len(tokens))]
         self._write([(h, p) for p in range(cached, len(tokens))])
+        if prefill_check:
+            self.check_prefill(h, cached)
         return h, cached
+
+    def check_prefill(self, h, cached):
+        """Prefill of the uncached tokens with pa_extend (the cached prefix is only read):
+        each new token attends causally over the whole sequence so far."""
+        torch = self.torch
+        L = len(self.tokens[h])
+        Q = L - cached
+        if Q == 0:
+            return
+        tables, lens = self.bm.export([h], (L + BS - 1) // BS)
+        q = self.rng.standard_normal((Q, H, D)).astype(np.float16)
+        scale = float(np.float32(1 / np.sqrt(D)))
+        out = pa.pa_extend(torch.from_numpy(q).cuda(), self.kp, self.vp, torch.from_numpy(tables).cuda(),
+                           torch.from_numpy(lens).cuda(),
+                           torch.tensor([0, Q], dtype=torch.int32, device="cuda"), Q, scale=scale,
+                           k_scale=self.ks, v_scale=self.vs)
+        got = out.double().cpu().numpy()
+        R = np.stack(self.rows[h])
+        G = H // HKV
+        worst = 0.0
+        for g in range(HKV):
+            K = self._stored_value(R[:, 0, g], self.ks)
+            V = self._stored_value(R[:, 1, g], self.vs)
+            for i in range(Q):
+                p = cached + i
+                for hh in range(g * G, (g + 1) * G):
+                    ref = pa_oracle.attend(q[i, hh].astype(np.float64), K[:p + 1], V[:p + 1], np.float64(scale))
+                    # the first tokens see few keys: allow the f16 rounding of |out| up to ~4
+                    worst = max(worst, float(np.abs(got[i, hh] - ref).max()))
+        assert worst <= TOL[self.kv] + 2.0 ** -10, worst
 
     def fork(self, h):
         c = self.bm.fork(h)
@@ -158,7 +190,7 @@ def test_serving_loop(kv):
     handles = []
     for r in range(5):
         suffix = lp.rng.integers(0, 50, int(lp.rng.integers(3, 30))).tolist()
-        h, cached = lp.add(system + suffix)
+        h, cached = lp.add(system + suffix, prefill_check=r < 3)
         assert cached == (0 if r == 0 else 32)
         handles.append(h)
     log(f"[serving] prefill decode err {lp.check_decode():.2e}")
