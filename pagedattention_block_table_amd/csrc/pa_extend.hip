@@ -308,11 +308,12 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_kernel(const ExtendArgs
 }
 
 // ---------------------------------------------------------------------------------
-// 16-bit KV: direct-to-LDS loads, a ring of four chunk buffers, 32 query rows per wave
+// 16-bit KV: direct-to-LDS loads into a ring of chunk buffers, 128 query rows per workgroup
 // ---------------------------------------------------------------------------------
 //
-// Each wave owns two 16-row query tiles (a workgroup 128 rows), so every K / V operand
-// read from LDS feeds two MFMAs. K and V chunks go from HBM straight into LDS with
+// A workgroup takes 128 query rows: with head_dim 128, eight waves of one 16-row tile
+// (four waves per SIMD); with head_dim 64, four waves of two tiles, each K / V operand
+// read from LDS feeding two MFMAs. K and V chunks go from HBM straight into LDS with
 // global_load_lds_dwordx4 (lane l of an instruction lands 16 * l bytes past the
 // instruction's LDS base), three chunks ahead of the one being computed. The copies are
 // issued from inline assembly so that the compiler, which cannot tell which LDS bytes
@@ -320,7 +321,7 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_kernel(const ExtendArgs
 // for exactly the chunk it is about to use (s_waitcnt vmcnt) and then synchronises the
 // workgroup. Rows past the end of the context load the last valid row instead (finite
 // data; their probability is zero), so every lane issues every copy and the count of
-// outstanding copies is known. Block ids come through scalar loads.
+// outstanding copies is known. Block ids come from a per-lane window of 64 chunks.
 //
 // LDS rows are unpadded (the copies fill 1 KiB runs); 16-byte pieces are XOR-swizzled
 // per row so that the K operand reads (16 rows, same column) and the transposed V reads
@@ -437,7 +438,7 @@ __global__ void __launch_bounds__(NW * 64) extend_dma_kernel(const ExtendArgs a)
   asm volatile("" ::: "memory");
   wait_vm<0>();
 
-  // copy geometry: thread piece u sits at physical slot P = 256u + 64 wave + lane of a tile
+  // copy geometry: thread piece u sits at physical slot P = NTH u + 64 wave + lane of a tile
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   const int bs_mask = (1 << a.bs_shift) - 1;
   const int64_t tile_bytes = (int64_t)Geo::ROW_B << a.bs_shift;
