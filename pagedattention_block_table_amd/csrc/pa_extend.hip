@@ -331,7 +331,10 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_kernel(const ExtendArgs
 #define PA_EXT_STAGES 4
 #endif
 constexpr int kDmaStages = PA_EXT_STAGES;  // chunks in the LDS ring (kDmaStages - 1 in flight)
-constexpr int kDmaRows = 128;  // query rows per workgroup: NW waves of 16 * NT rows
+#ifndef PA_EXT_ROWS
+#define PA_EXT_ROWS 128
+#endif
+constexpr int kDmaRows = PA_EXT_ROWS;  // query rows per workgroup: NW waves of 16 * NT rows
 
 // waves per workgroup of the ring kernel (16-row query tiles per wave = 128 / (16 NW));
 // head_dim 64 keeps four waves so that every thread issues a whole copy per tile
