@@ -383,6 +383,38 @@ def main():
     durs_ms = [s.elapsed_time(e_) for s, e_ in zip(starts, ends)]
     kern_ms = float(np.mean(durs_ms))
 
+    # the same steps replayed from one HIP graph (R captured launches, one per replica):
+    # what a caller that captures its decode loop gets, without per-launch host work.
+    # Workspaces are made before the capture, so the graph holds the decode kernels only.
+    graph_ms = None
+    try:
+        gws = pa.balanced_workspace(q, k0, args.workgroups) if mode == "balanced" else ws
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            gkw = dict(kw, stream=torch.cuda.current_stream())
+            if mode == "direct":
+                gplan = pa.DecodePlan(q, k0, v0, bt, cl, **gkw)
+            elif mode == "balanced":
+                gplan = pa.DecodePlan(q, k0, v0, bt, cl, balanced=True, num_workgroups=args.workgroups,
+                                      workspace=gws, **gkw)
+            else:
+                gplan = pa.DecodePlan(q, k0, v0, bt, cl, max_context_len=maxL, partition_size=P,
+                                      workspace=gws, **gkw)
+            for r in range(R):
+                gplan(ks[r], vs[r])
+        reps = max(1, K // R)
+        graph.replay()
+        torch.cuda.synchronize()
+        t_g = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t_g) * 1e3 / (reps * R)
+        del graph
+    except Exception as exc:  # graph capture unavailable: report the eager numbers only
+        log(f"[bench] graph replay skipped: {exc}")
+
     # the write that precedes each decode step: one new token's K/V per sequence, stored
     # (quantised for fp8) into its block. Timed on its own; the appended rows go to the slot
     # of each sequence's last cached token, so the pool keeps its shape and cost is the same.
@@ -448,6 +480,9 @@ def main():
                                     round(float(np.percentile(durs_ms, 90)), 6)]},
         "cpu_baseline": None,
         "append_kv": app,
+        "graph_replay": None if graph_ms is None else {
+            "ms_per_step": round(graph_ms, 6),
+            "GB_per_s": round(kv_unique / (graph_ms * 1e-3) / 1e9, 2)},
     }
     log(f"[bench] {ms_per_step * 1e3:.2f} us/step wall, {kern_ms * 1e3:.2f} us/launch (events): "
         f"{value:.1f} GB/s KV, roofline frac {achieved / HBM_PEAK_GBS:.3f}")
