@@ -63,6 +63,14 @@ struct ExtendArgs {
   float v_scale;
 };
 
+// max of three scores in one instruction, without the canonicalizing moves fmaxf adds
+// (scores are finite dot products or the -inf of a masked slot for finite inputs)
+__device__ __forceinline__ float max3(float x, float y, float z) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
+  return r;
+}
+
 constexpr int kExtWaves = 4;
 constexpr int kExtRows = 16 * kExtWaves;  // query rows per workgroup
 constexpr int kExtChunk = 32;             // key tokens per step
@@ -111,9 +119,12 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_kernel(const ExtendArgs
   const int unit = xcd_unit((int)blockIdx.x, (int)gridDim.x);
   const int qt = a.q_tiles - 1 - unit % a.q_tiles;
   const int sg = unit / a.q_tiles;
-  const int g = sg % a.num_kv_heads;
-  const int s = sg / a.num_kv_heads;
-  if (s >= a.num_seqs) return;
+  // KV-head-major: each XCD's contiguous range of units holds a few KV heads of every
+  // sequence (balanced however the context lengths differ); the query tiles of one
+  // (sequence, KV head) stay together and share the chunks through that XCD's L2
+  const int s = sg % a.num_seqs;
+  const int g = sg / a.num_seqs;
+  if (g >= a.num_kv_heads) return;
 
   const int q0 = a.query_start_loc[s];
   const int Q = a.query_start_loc[s + 1] - q0;
@@ -200,8 +211,13 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_kernel(const ExtendArgs
     }
   };
 
+  // probabilities as f16 keep 11 significant bits; bf16 keeps 8, so there they go as
+  // high + low halves
+  constexpr bool SPLIT = IO == kBF16;
   float m = -3.0e38f;  // running max of row n (log2 units), same in the row's 4 lanes
-  float l = 0.f;       // this lane's share of the running sum
+  f32x4_t lacc = f32x4_t{0.f, 0.f, 0.f, 0.f};  // softmax denominator of row n
+  constexpr uint32_t kOne2 = IO == kF16 ? 0x3C003C00u : 0x3F803F80u;  // two 16-bit 1.0
+  const vec ones = __builtin_bit_cast(vec, make_uint4(kOne2, kOne2, kOne2, kOne2));
   f32x4_t o[Geo::NDT];
 #pragma unroll
   for (int dt = 0; dt < Geo::NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -228,53 +244,60 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_kernel(const ExtendArgs
           acc[hf] = Mma<IO>::mma(kop, qv[ks], acc[hf]);
         }
       }
-      // z[j]: token t0 + 4lq + j (j < 4) and t0 + 16 + 4lq + j - 4 (j >= 4)
+      // z[j]: token t0 + 4lq + j (j < 4) and t0 + 16 + 4lq + j - 4 (j >= 4), raw dot
+      // products (the scale is folded into the exponent; q_mul > 0)
       float z[8];
-      const bool need_mask = t0 + kExtChunk - 1 > wp_min;  // uniform
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float v = acc[j >> 2][j & 3] * a.q_mul;
-        if (need_mask) {
-          const int t = t0 + 16 * (j >> 2) + 4 * lq + (j & 3);
-          z[j] = t <= pos ? v : -INFINITY;
-        } else {
-          z[j] = v;
-        }
+      for (int j = 0; j < 8; ++j) z[j] = acc[j >> 2][j & 3];
+      if (t0 + kExtChunk - 1 > wp_min) {  // uniform: only chunks that reach the diagonal
+        asm volatile("" ::: "memory");
+        const int lim = pos - t0 - 4 * lq;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) z[j] = 16 * (j >> 2) + (j & 3) <= lim ? z[j] : -INFINITY;
       }
-      float mx = z[0];
-#pragma unroll
-      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, z[j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool raise = mx > m + kLazyRescale;
-      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      // the row's four lanes exchange maxima only when one of them would raise the
+      // row's max past the lazy-rescale threshold
+      float mx = max3(max3(z[0], z[1], z[2]), max3(z[3], z[4], z[5]), fmaxf(z[6], z[7])) * a.q_mul;
+      if (__builtin_amdgcn_ballot_w64(mx > m + kLazyRescale) != 0) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool raise = mx > m + kLazyRescale;
         const float mn = raise ? mx : m;
         const float alpha = __builtin_amdgcn_exp2f(m - mn);
         m = mn;
-        l *= alpha;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lacc[r] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < Geo::NDT; ++dt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) o[dt][r] *= alpha;
       }
-      uint16_t phi[8], plo[8];
+      float p[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p = __builtin_amdgcn_exp2f(z[j] - m);
-        l += p;
-        M16::split(p, phi[j], plo[j]);
+      for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(z[j], a.q_mul, -m));
+      vec bhi, blo;
+      if constexpr (SPLIT) {
+        uint16_t phi[8], plo[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) M16::split(p[j], phi[j], plo[j]);
+        uint4 bh, bl;
+        bh.x = phi[0] | ((uint32_t)phi[1] << 16);
+        bh.y = phi[2] | ((uint32_t)phi[3] << 16);
+        bh.z = phi[4] | ((uint32_t)phi[5] << 16);
+        bh.w = phi[6] | ((uint32_t)phi[7] << 16);
+        bl.x = plo[0] | ((uint32_t)plo[1] << 16);
+        bl.y = plo[2] | ((uint32_t)plo[3] << 16);
+        bl.z = plo[4] | ((uint32_t)plo[5] << 16);
+        bl.w = plo[6] | ((uint32_t)plo[7] << 16);
+        bhi = __builtin_bit_cast(vec, bh);
+        blo = __builtin_bit_cast(vec, bl);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bhi[j] = (_Float16)p[j];
       }
-      uint4 bh, bl;
-      bh.x = phi[0] | ((uint32_t)phi[1] << 16);
-      bh.y = phi[2] | ((uint32_t)phi[3] << 16);
-      bh.z = phi[4] | ((uint32_t)phi[5] << 16);
-      bh.w = phi[6] | ((uint32_t)phi[7] << 16);
-      bl.x = plo[0] | ((uint32_t)plo[1] << 16);
-      bl.y = plo[2] | ((uint32_t)plo[3] << 16);
-      bl.z = plo[4] | ((uint32_t)plo[5] << 16);
-      bl.w = plo[6] | ((uint32_t)plo[7] << 16);
-      const vec bhi = __builtin_bit_cast(vec, bh);
-      const vec blo = __builtin_bit_cast(vec, bl);
+      // the softmax denominator as one more tile with V^T = 1
+      lacc = Mma<IO>::mma(ones, bhi, lacc);
+      if constexpr (SPLIT) lacc = Mma<IO>::mma(ones, blo, lacc);
       // V^T operand: row d = 16dt + n, tokens 4lq .. 4lq+3 and 16+4lq .. 16+4lq+3
       const int vr = 4 * lq + (n >> 2);
       const int vc = 4 * (n & 3);
@@ -288,7 +311,7 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_kernel(const ExtendArgs
         const uint2 w1 = __builtin_bit_cast(uint2, x1);
         const vec av = __builtin_bit_cast(vec, make_uint4(w0.x, w0.y, w1.x, w1.y));
         o[dt] = Mma<IO>::mma(av, bhi, o[dt]);
-        o[dt] = Mma<IO>::mma(av, blo, o[dt]);
+        if constexpr (SPLIT) o[dt] = Mma<IO>::mma(av, blo, o[dt]);
       }
     }
     if (c + 1 < nch) store_chunk((c + 1) & 1);
@@ -296,8 +319,7 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_kernel(const ExtendArgs
   }
 
   if (!row_ok) return;
-  float lt = l + __shfl_xor(l, 16);
-  lt += __shfl_xor(lt, 32);
+  const float lt = lacc[0];
   // lane (n, lq) holds O^T[16dt + 4lq + r][row n]
   const float inv = pos >= 0 && lt > 0.f ? a.v_scale / lt : 0.f;
   const int64_t obase = ((int64_t)(q0 + ti) * a.num_heads + h) * D;
@@ -315,7 +337,7 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_kernel(const ExtendArgs
 // (four waves per SIMD); with head_dim 64, four waves of two tiles, each K / V operand
 // read from LDS feeding two MFMAs. K and V chunks go from HBM straight into LDS with
 // global_load_lds_dwordx4 (lane l of an instruction lands 16 * l bytes past the
-// instruction's LDS base), three chunks ahead of the one being computed. The copies are
+// instruction's LDS base), up to three chunks ahead of the one being computed. The copies are
 // issued from inline assembly so that the compiler, which cannot tell which LDS bytes
 // they write, does not wait for all of them before every LDS read; the kernel waits
 // for exactly the chunk it is about to use (s_waitcnt vmcnt) and then synchronises the
@@ -326,6 +348,14 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_kernel(const ExtendArgs
 // LDS rows are unpadded (the copies fill 1 KiB runs); 16-byte pieces are XOR-swizzled
 // per row so that the K operand reads (16 rows, same column) and the transposed V reads
 // (4 rows, 2 pieces) hit distinct banks.
+//
+// Per chunk a wave runs the softmax of the chunk's scores (computed one step earlier),
+// then the next chunk's scores and this chunk's V product together, so the vector unit
+// and the matrix cores overlap. The vector work is kept small: the scale is folded into
+// the exponent (one fma per score), the causal mask is applied only on chunks that
+// reach the diagonal, the four lanes of a query row exchange their maxima only when one
+// of them would raise the row's max past the lazy-rescale threshold, and the softmax
+// denominator is one more MFMA tile (V^T = 1) instead of a per-lane sum.
 
 #ifndef PA_EXT_STAGES
 #define PA_EXT_STAGES 4
@@ -387,9 +417,12 @@ __global__ void __launch_bounds__(NW * 64) extend_dma_kernel(const ExtendArgs a)
   const int unit = xcd_unit((int)blockIdx.x, (int)gridDim.x);
   const int qt = a.q_tiles - 1 - unit % a.q_tiles;
   const int sg = unit / a.q_tiles;
-  const int g = sg % a.num_kv_heads;
-  const int s = sg / a.num_kv_heads;
-  if (s >= a.num_seqs) return;
+  // KV-head-major: each XCD's contiguous range of units holds a few KV heads of every
+  // sequence (balanced however the context lengths differ); the query tiles of one
+  // (sequence, KV head) stay together and share the chunks through that XCD's L2
+  const int s = sg % a.num_seqs;
+  const int g = sg / a.num_seqs;
+  if (g >= a.num_kv_heads) return;
 
   const int q0 = a.query_start_loc[s];
   const int Q = a.query_start_loc[s + 1] - q0;
@@ -493,139 +526,201 @@ __global__ void __launch_bounds__(NW * 64) extend_dma_kernel(const ExtendArgs a)
     }
   };
 
-  float m[NT], l[NT];
+  float m[NT];
+  f32x4_t lacc[NT];  // softmax denominator (the four entries are equal)
   f32x4_t o[NT][Geo::NDT];
 #pragma unroll
   for (int tq = 0; tq < NT; ++tq) {
     m[tq] = -3.0e38f;
-    l[tq] = 0.f;
+    lacc[tq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < Geo::NDT; ++dt) o[tq][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  constexpr uint32_t kOne2 = IO == kF16 ? 0x3C003C00u : 0x3F803F80u;  // two 16-bit 1.0
+  const vec ones = __builtin_bit_cast(vec, make_uint4(kOne2, kOne2, kOne2, kOne2));
 
+  // Per-lane LDS byte offsets inside a ring stage; the stage base is a compile-time
+  // immediate of each read (the chunk loop is unrolled over the ring's stages).
+  uint32_t koff[2][Geo::NKS];
 #pragma unroll
-  for (int j = 0; j < kDmaStages - 1; ++j)
-    if (j < nch) issue(j);
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int ks = 0; ks < Geo::NKS; ++ks) {
+      const int r = 16 * hf + n;
+      koff[hf][ks] = r * Geo::ROW_B + 16 * ((4 * ks + lq) ^ Geo::swz_k(r));
+    }
+  // V^T operand of tile dt: rows 4lq .. 4lq+3 (and the same 16 rows further), 8 bytes
+  uint32_t voff[Geo::NDT];
+  {
+    const int r0 = 4 * lq + (n >> 2);
+#pragma unroll
+    for (int dt = 0; dt < Geo::NDT; ++dt) {
+      const int cc = 2 * dt + ((n & 3) >> 1);
+      voff[dt] = Geo::TILE_B + r0 * Geo::ROW_B + 16 * (cc ^ Geo::swz_v(r0)) + (n & 1) * 8;
+    }
+  }
 
-  for (int c = 0; c < nch; ++c) {
-    // chunk c has landed once at most the copies of the chunks issued after it remain
-    const int newer = min(kDmaStages - 2, nch - 1 - c);
+  // S^T of one chunk for the wave's query tiles: acc[tq][hf] = K rows 16hf .. 16hf+15
+  auto qk = [&](const char* kt, f32x4_t (&acc)[NT][2]) {
+#pragma unroll
+    for (int tq = 0; tq < NT; ++tq)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) acc[tq][hf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < Geo::NKS; ++ks)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const vec kop = *(const vec*)(kt + koff[hf][ks]);
+#pragma unroll
+        for (int tq = 0; tq < NT; ++tq) acc[tq][hf] = Mma<IO>::mma(kop, qv[tq][ks], acc[tq][hf]);
+      }
+  };
+
+  // online softmax of one chunk's scores (raw dot products; scale folded into the
+  // exponent) into 16-bit probability operands, rescaling o and l when the max rises
+  auto softmax = [&](f32x4_t (&acc)[NT][2], int t0, vec (&bhi)[NT], vec (&blo)[NT]) {
+    const bool need_mask = t0 + kExtChunk - 1 > wp_min;  // uniform
+#pragma unroll
+    for (int tq = 0; tq < NT; ++tq) {
+      float z[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) z[j] = acc[tq][j >> 2][j & 3];
+      if (need_mask) {
+        asm volatile("" ::: "memory");  // a real branch: most chunks need no mask
+        const int lim = pos[tq] - t0 - 4 * lq;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) z[j] = 16 * (j >> 2) + (j & 3) <= lim ? z[j] : -INFINITY;
+      }
+      // The row max is needed only when it may rise past the lazy threshold: test the
+      // lane's own max first (a row's max exceeds it only if one of its four lanes' does)
+      // and exchange across the row's lanes only then.
+      float mx = max3(max3(z[0], z[1], z[2]), max3(z[3], z[4], z[5]), fmaxf(z[6], z[7]));
+      mx *= a.q_mul;  // q_mul > 0
+      if (__builtin_amdgcn_ballot_w64(mx > m[tq] + kLazyRescale) != 0) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool raise = mx > m[tq] + kLazyRescale;
+        const float mn = raise ? mx : m[tq];
+        const float alpha = __builtin_amdgcn_exp2f(m[tq] - mn);
+        m[tq] = mn;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lacc[tq][r] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < Geo::NDT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[tq][dt][r] *= alpha;
+      }
+      const float nm = -m[tq];
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(z[j], a.q_mul, nm));
+      if constexpr (SPLIT) {
+        uint16_t phi[8], plo[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) M16::split(p[j], phi[j], plo[j]);
+        uint4 bh, bl;
+        bh.x = phi[0] | ((uint32_t)phi[1] << 16);
+        bh.y = phi[2] | ((uint32_t)phi[3] << 16);
+        bh.z = phi[4] | ((uint32_t)phi[5] << 16);
+        bh.w = phi[6] | ((uint32_t)phi[7] << 16);
+        bl.x = plo[0] | ((uint32_t)plo[1] << 16);
+        bl.y = plo[2] | ((uint32_t)plo[3] << 16);
+        bl.z = plo[4] | ((uint32_t)plo[5] << 16);
+        bl.w = plo[6] | ((uint32_t)plo[7] << 16);
+        bhi[tq] = __builtin_bit_cast(vec, bh);
+        blo[tq] = __builtin_bit_cast(vec, bl);
+      } else {
+        vec v;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = (_Float16)p[j];
+        bhi[tq] = v;
+      }
+    }
+  };
+
+  // O^T += V^T P^T over the chunk
+  auto pv = [&](const char* st_base, const vec (&bhi)[NT], const vec (&blo)[NT]) {
+#pragma unroll
+    for (int dt = 0; dt < Geo::NDT; ++dt) {
+      const i16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4_t*)(st_base + voff[dt]));
+      const i16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4_t*)(st_base + voff[dt] + 16 * Geo::ROW_B));
+      const uint2 w0 = __builtin_bit_cast(uint2, x0);
+      const uint2 w1 = __builtin_bit_cast(uint2, x1);
+      const vec av = __builtin_bit_cast(vec, make_uint4(w0.x, w0.y, w1.x, w1.y));
+#pragma unroll
+      for (int tq = 0; tq < NT; ++tq) {
+        o[tq][dt] = Mma<IO>::mma(av, bhi[tq], o[tq][dt]);
+        if constexpr (SPLIT) o[tq][dt] = Mma<IO>::mma(av, blo[tq], o[tq][dt]);
+      }
+    }
+    // the softmax denominator as one more tile with V^T = 1: every lane receives its
+    // query row's sum over the chunk's tokens, of the same 16-bit probabilities
+#pragma unroll
+    for (int tq = 0; tq < NT; ++tq) {
+      lacc[tq] = Mma<IO>::mma(ones, bhi[tq], lacc[tq]);
+      if constexpr (SPLIT) lacc[tq] = Mma<IO>::mma(ones, blo[tq], lacc[tq]);
+    }
+  };
+
+  // wait until at most `newer` chunks' copies of this thread are outstanding
+  auto wait_chunks = [&](int newer) {
     static_assert(kDmaStages >= 2 && kDmaStages <= 6, "ring depth");
     if (kDmaStages >= 6 && newer >= 4) wait_vm<(kDmaStages >= 6 ? 4 : 0) * CPS>();
     else if (kDmaStages >= 5 && newer >= 3) wait_vm<(kDmaStages >= 5 ? 3 : 0) * CPS>();
     else if (kDmaStages >= 4 && newer >= 2) wait_vm<(kDmaStages >= 4 ? 2 : 0) * CPS>();
     else if (newer >= 1) wait_vm<CPS>();
     else wait_vm<0>();
+  };
+
+#pragma unroll
+  for (int j = 0; j < kDmaStages - 1; ++j)
+    if (j < nch) issue(j);
+
+  // Software pipeline: iteration c computes the scores of chunk c + 1 (its K is in the
+  // ring by then) before the softmax and V product of chunk c, so the matrix cores work
+  // while the vector unit runs the softmax. The scores alternate between two register
+  // sets by chunk parity (the ring depth is even, so the parity of the unrolled stage
+  // is the parity of the chunk).
+  static_assert(kDmaStages % 2 == 0 && kDmaStages >= 4,
+                "score buffers alternate by stage parity; two chunks in flight ahead of c + 1");
+  f32x4_t sc[2][NT][2];
+  if (nch > 0) {
+    wait_chunks(min(kDmaStages - 2, nch - 1));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (c + kDmaStages - 1 < nch) issue(c + kDmaStages - 1);
-
-    const int t0 = c * kExtChunk;
-    if (wave_live && t0 <= wp_max) {
-      const char* kt = lds + (c % kDmaStages) * Geo::STAGE_B;
-      const char* vt = kt + Geo::TILE_B;
-      f32x4_t acc[NT][2];
+    if (wave_live && 0 <= wp_max) qk(lds, sc[0]);
+  }
+  for (int c0 = 0; c0 < nch; c0 += kDmaStages) {
 #pragma unroll
-      for (int tq = 0; tq < NT; ++tq)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) acc[tq][hf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int r = 16 * hf + n;
-#pragma unroll
-        for (int ks = 0; ks < Geo::NKS; ++ks) {
-          const int pc = (4 * ks + lq) ^ Geo::swz_k(r);
-          const vec kop = *(const vec*)(kt + r * Geo::ROW_B + 16 * pc);
-#pragma unroll
-          for (int tq = 0; tq < NT; ++tq) acc[tq][hf] = Mma<IO>::mma(kop, qv[tq][ks], acc[tq][hf]);
-        }
+    for (int st = 0; st < kDmaStages; ++st) {
+      const int c = c0 + st;
+      if (c >= nch) break;
+      if (c + 1 < nch) {
+        // chunk c + 1 has landed once at most the copies of the chunks after it remain;
+        // the barrier also frees the stage of chunk c - 1 for the copy issued next
+        wait_chunks(min(kDmaStages - 3, nch - 2 - c));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (c + kDmaStages - 1 < nch) issue(c + kDmaStages - 1);
       }
-      const bool need_mask = t0 + kExtChunk - 1 > wp_min;  // uniform
-      vec bhi[NT], blo[NT];
-#pragma unroll
-      for (int tq = 0; tq < NT; ++tq) {
-        float z[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float v = acc[tq][j >> 2][j & 3] * a.q_mul;
-          if (need_mask) {
-            const int t = t0 + 16 * (j >> 2) + 4 * lq + (j & 3);
-            z[j] = t <= pos[tq] ? v : -INFINITY;
-          } else {
-            z[j] = v;
-          }
-        }
-        float mx = z[0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, z[j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const bool raise = mx > m[tq] + kLazyRescale;
-        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-          const float mn = raise ? mx : m[tq];
-          const float alpha = __builtin_amdgcn_exp2f(m[tq] - mn);
-          m[tq] = mn;
-          l[tq] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < Geo::NDT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[tq][dt][r] *= alpha;
-        }
-        float p[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(z[j] - m[tq]);
-          l[tq] += p[j];
-        }
-        if constexpr (SPLIT) {
-          uint16_t phi[8], plo[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) M16::split(p[j], phi[j], plo[j]);
-          uint4 bh, bl;
-          bh.x = phi[0] | ((uint32_t)phi[1] << 16);
-          bh.y = phi[2] | ((uint32_t)phi[3] << 16);
-          bh.z = phi[4] | ((uint32_t)phi[5] << 16);
-          bh.w = phi[6] | ((uint32_t)phi[7] << 16);
-          bl.x = plo[0] | ((uint32_t)plo[1] << 16);
-          bl.y = plo[2] | ((uint32_t)plo[3] << 16);
-          bl.z = plo[4] | ((uint32_t)plo[5] << 16);
-          bl.w = plo[6] | ((uint32_t)plo[7] << 16);
-          bhi[tq] = __builtin_bit_cast(vec, bh);
-          blo[tq] = __builtin_bit_cast(vec, bl);
-        } else {
-          vec v;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) v[j] = (_Float16)p[j];
-          bhi[tq] = v;
-        }
-      }
-      // V^T operand: row d = 16dt + n; tokens 4lq .. 4lq+3 and 16+4lq .. 16+4lq+3
-      const int r0 = 4 * lq + (n >> 2);
-      const int r1 = r0 + 16;
-      const int half = (n & 1) * 8;
-#pragma unroll
-      for (int dt = 0; dt < Geo::NDT; ++dt) {
-        const int c = 2 * dt + ((n & 3) >> 1);
-        const i16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4_t*)(vt + r0 * Geo::ROW_B + 16 * (c ^ Geo::swz_v(r0)) + half));
-        const i16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4_t*)(vt + r1 * Geo::ROW_B + 16 * (c ^ Geo::swz_v(r1)) + half));
-        const uint2 w0 = __builtin_bit_cast(uint2, x0);
-        const uint2 w1 = __builtin_bit_cast(uint2, x1);
-        const vec av = __builtin_bit_cast(vec, make_uint4(w0.x, w0.y, w1.x, w1.y));
-#pragma unroll
-        for (int tq = 0; tq < NT; ++tq) {
-          o[tq][dt] = Mma<IO>::mma(av, bhi[tq], o[tq][dt]);
-          if constexpr (SPLIT) o[tq][dt] = Mma<IO>::mma(av, blo[tq], o[tq][dt]);
-        }
+      const int t0 = c * kExtChunk;
+      if (wave_live && t0 <= wp_max) {
+        vec bhi[NT], blo[NT];
+        softmax(sc[st & 1], t0, bhi, blo);
+        // the next chunk's scores go with this chunk's V product, so the two interleave on
+        // the matrix cores; past the wave's last chunk they are computed and never used
+        // (the stage holds an older chunk then, never one being copied)
+        qk(lds + ((st + 1) % kDmaStages) * Geo::STAGE_B, sc[(st + 1) & 1]);
+        pv(lds + st * Geo::STAGE_B, bhi, blo);
       }
     }
   }
 
 #pragma unroll
   for (int tq = 0; tq < NT; ++tq) {
-    float lt = l[tq] + __shfl_xor(l[tq], 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = lacc[tq][0];
     if (!row_ok[tq]) continue;
     const float inv = pos[tq] >= 0 && lt > 0.f ? a.v_scale / lt : 0.f;
     const int64_t obase = ((int64_t)(q0 + ti[tq]) * a.num_heads + hh[tq]) * D;
