@@ -56,8 +56,16 @@ constexpr float kLazyRescale = 8.0f;
 #define PA_STAGGER 1
 #endif
 #ifndef PA_MFMA_TILES
-#define PA_MFMA_TILES 1
+#define PA_MFMA_TILES 2
 #endif
+
+// Fixed work of one segment of the balanced scheduler (engine set-up, wave merge, write),
+// counted in chunks when the batch is split evenly over the workgroups: without it a
+// workgroup whose range holds many short sequences does more work than the others.
+#ifndef PA_SEG_COST
+#define PA_SEG_COST 8
+#endif
+constexpr int kSegCost = PA_SEG_COST;
 
 // Largest batch the balanced scheduler takes (its chunk prefix sums live in LDS).
 constexpr int kMaxBalancedSeqs = 4096;
@@ -131,6 +139,38 @@ constexpr bool mfma_supported() {
          D <= 128 && MfmaGeo<KV, D>::ok;
 }
 
+// Chunks a wave keeps in flight: the loads of chunks k+1 .. k+kPipeDepth-1 are
+// outstanding while chunk k is computed.
+#ifndef PA_PIPE_DEPTH
+#define PA_PIPE_DEPTH 2
+#endif
+constexpr int kPipeDepth = PA_PIPE_DEPTH;
+
+// Drive an engine's issue / consume over a wave's nwc chunks with kPipeDepth register
+// buffers (the buffer index is a compile-time constant after unrolling). The steady-state
+// loop issues unconditionally: past the last chunk it re-issues chunk nwc - 1 (cached
+// data, never consumed). With every path into the loop header issuing the same loads in
+// the same order, the compiler waits only for the buffer being consumed; a conditional
+// issue would make it wait for the loads of the following chunks as well.
+template <class Eng>
+__device__ __forceinline__ void run_pipelined(Eng& eng, const DecodeArgs& a, int nwc) {
+  if (nwc <= 0) return;
+  typename Eng::Buf b[kPipeDepth];
+#pragma unroll
+  for (int d = 0; d < kPipeDepth; ++d) eng.issue(a, b[d], min(d, nwc - 1));
+  int k = 0;
+  for (; k + kPipeDepth <= nwc; k += kPipeDepth) {
+#pragma unroll
+    for (int d = 0; d < kPipeDepth; ++d) {
+      eng.consume(a, b[d], k + d);
+      eng.issue(a, b[d], min(k + d + kPipeDepth, nwc - 1));
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < kPipeDepth - 1; ++d)
+    if (k + d < nwc) eng.consume(a, b[d], k + d);
+}
+
 // Order in which a wave visits the `len` chunks of a segment: from a per-sequence
 // rotation, so that workgroups that share prefix blocks do not all start on the same
 // block at the same time.
@@ -195,20 +235,26 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, int s, int g, const 
 }
 
 // Issue the K/V loads of the chunk whose first token is c0 (a multiple of the block size
-// or of 16), with off[u] = byte offset of the chunk's u-th block and kbase / vbase
-// pointing at the KV head's tile of block 0. Rows at or past t_end are not loaded.
+// or of 16, and below t_end), with off[u] = byte offset of the chunk's u-th block and
+// kbase / vbase pointing at the KV head's tile of block 0. A lane whose token is at or
+// past t_end reads token c0's row instead (finite data already being fetched; the score
+// of such a token is excluded by select, so its probability is exactly 0). Every load
+// is unconditional: loads under a branch would make the compiler wait for all
+// outstanding loads (the next chunks' too) at the top of the chunk loop.
 template <int KV, int D, int BS, int NT>
 __device__ __forceinline__ void issue_chunk(ChunkBuf<KV, D, NT>& b, const char* kbase, const char* vbase,
                                             const int64_t* off, int c0, int t_end, const LaneIds& li) {
   using Geo = MfmaGeo<KV, D>;
-  constexpr int CT = 16 * NT, RB = Geo::RB, CPL = Geo::CPL, VPL = Geo::VPL;
+  constexpr int RB = Geo::RB, CPL = Geo::CPL, VPL = Geo::VPL;
+  constexpr int CT = 16 * NT;
   constexpr int NBC = CT >= BS ? CT / BS : 1;
   const int jb = c0 / BS;
-  const bool tail = c0 + CT > t_end;
 #pragma unroll
   for (int tau = 0; tau < NT; ++tau) {
-    const int to = c0 + 16 * tau + li.n;          // own token
-    const int tp = c0 + 16 * tau + (li.n ^ 8);    // partner token
+    int to = c0 + 16 * tau + li.n;          // own token
+    int tp = c0 + 16 * tau + (li.n ^ 8);    // partner token
+    to = to < t_end ? to : c0;
+    tp = tp < t_end ? tp : c0;
     int64_t bo = off[0], bp = off[0];
 #pragma unroll
     for (int u = 1; u < NBC; ++u) {
@@ -218,27 +264,13 @@ __device__ __forceinline__ void issue_chunk(ChunkBuf<KV, D, NT>& b, const char* 
     const char* krow = kbase + bo + (to % BS) * RB;
     const char* vrow_o = vbase + bo + (to % BS) * RB;
     const char* vrow_p = vbase + bp + (tp % BS) * RB;
-    if (!tail) {
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) b.kr[tau][i] = load16(krow + 16 * (4 * i + li.lg));
+    for (int i = 0; i < CPL; ++i) b.kr[tau][i] = load16(krow + 16 * (4 * i + li.lg));
 #pragma unroll
-      for (int q = 0; q < VPL; ++q) {
-        const int vc = 4 * (VPL * li.hh + q) + li.lg;
-        b.vo[tau][q] = load16(vrow_o + 16 * vc);
-        b.vp[tau][q] = load16(vrow_p + 16 * vc);
-      }
-    } else {
-      const bool ok_o = to < t_end;
-      const bool ok_p = tp < t_end;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i)
-        b.kr[tau][i] = ok_o ? load16(krow + 16 * (4 * i + li.lg)) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int q = 0; q < VPL; ++q) {
-        const int vc = 4 * (VPL * li.hh + q) + li.lg;
-        b.vo[tau][q] = ok_o ? load16(vrow_o + 16 * vc) : make_uint4(0, 0, 0, 0);
-        b.vp[tau][q] = ok_p ? load16(vrow_p + 16 * vc) : make_uint4(0, 0, 0, 0);
-      }
+    for (int q = 0; q < VPL; ++q) {
+      const int vc = 4 * (VPL * li.hh + q) + li.lg;
+      b.vo[tau][q] = load16(vrow_o + 16 * vc);
+      b.vp[tau][q] = load16(vrow_p + 16 * vc);
     }
   }
 }
@@ -408,6 +440,7 @@ struct MfmaEngine {
   const char* vbase;
   int64_t blk_stride;
   int win[2][NBC];  // block ids of this wave's chunks, windows w and w + 1
+  int cur_win;      // w: the window held in win[0]
   vec qa[Geo::NST];
   WaveState<KV, D, G> st;
 
@@ -417,17 +450,22 @@ struct MfmaEngine {
     return base + CT * (k0 + rotated(wave + k * nw, rot, len));
   }
 
+  // Raw table entries of the wave's chunks 64w .. 64w+63 (lane l: chunk 64w + l); entries
+  // of chunks or blocks past the end read entry 0 of the row instead (never used for a
+  // valid token). Ids are clamped into the pool when they are taken (block_id).
   __device__ __forceinline__ void load_window(const DecodeArgs& a, int w, int (&dst)[NBC]) {
     const int k = 64 * w + li.lane;
     const bool live = wave + k * nw < len;
     const int j = live ? chunk_token(k) / BS : 0;
 #pragma unroll
-    for (int u = 0; u < NBC; ++u) {
-      int b = 0;
-      if (live && j + u < j_end) b = bt[j + u];
-      // contract: 0 <= b < num_blocks; clamp so that a bad table never reads outside the pool
-      dst[u] = min(max(b, 0), a.num_blocks - 1);
-    }
+    for (int u = 0; u < NBC; ++u) dst[u] = bt[live && j + u < j_end ? j + u : 0];
+  }
+
+  // Block id of the u-th block of chunk k (k in the current window), clamped into the
+  // pool so that a bad table never reads outside it (contract: 0 <= id < num_blocks).
+  __device__ __forceinline__ int64_t block_off(const DecodeArgs& a, int u, int k) const {
+    const int b = __builtin_amdgcn_readlane(win[0][u], k & 63);
+    return (int64_t)min(max(b, 0), a.num_blocks - 1) * blk_stride;
   }
 
   __device__ __forceinline__ void begin(const DecodeArgs& a, int s_, int g_, int t_end_, int base_,
@@ -448,21 +486,22 @@ struct MfmaEngine {
     vbase = (const char*)a.v_pool + (int64_t)g * TILE_BYTES;
     load_window(a, 0, win[0]);
     load_window(a, 1, win[1]);
+    cur_win = 0;
     load_q<IO, KV, D, G>(a, s, g, li, qa);
     st.reset();
   }
 
   __device__ __forceinline__ void issue(const DecodeArgs& a, Buf& b, int k) {
-    if ((k & 63) == 0 && k > 0) {
+    if ((k >> 6) != cur_win) {
       // entering window k/64: it was loaded 64 chunks ago; fetch the one after it
+      cur_win = k >> 6;
 #pragma unroll
       for (int u = 0; u < NBC; ++u) win[0][u] = win[1][u];
-      load_window(a, (k >> 6) + 1, win[1]);
+      load_window(a, cur_win + 1, win[1]);
     }
     int64_t off[NBC];
 #pragma unroll
-    for (int u = 0; u < NBC; ++u)
-      off[u] = (int64_t)__builtin_amdgcn_readlane(win[0][u], k & 63) * blk_stride;
+    for (int u = 0; u < NBC; ++u) off[u] = block_off(a, u, k);
     issue_chunk<KV, D, BS, NT>(b, kbase, vbase, off, chunk_token(k), t_end, li);
   }
 
@@ -472,20 +511,10 @@ struct MfmaEngine {
     consume_chunk<IO, KV, D, G, NT>(a, b, qa, c0, t_end, st, li);
   }
 
-  // This wave's chunks of the segment, two in flight.
+  // This wave's chunks of the segment, kPipeDepth in flight.
   __device__ __forceinline__ void run(const DecodeArgs& a) {
     const int nwc = wave < len ? (len - wave + nw - 1) / nw : 0;
-    Buf A, B;
-    if (nwc > 0) issue(a, A, 0);
-    if (nwc > 1) issue(a, B, 1);
-    for (int k = 0; k < nwc; k += 2) {
-      consume(a, A, k);
-      if (k + 2 < nwc) issue(a, A, k + 2);
-      if (k + 1 < nwc) {
-        consume(a, B, k + 1);
-        if (k + 3 < nwc) issue(a, B, k + 3);
-      }
-    }
+    run_pipelined(*this, a, nwc);
   }
 
   // Reduce the wave's state and store it as wave `wave` of the workgroup's LDS arrays.
@@ -598,6 +627,7 @@ struct MfmaPvEngine {
   const char* vbase;
   int64_t blk_stride;
   int win[2][NBC];
+  int cur_win;
   vec qa[NH][Geo::NST];
   float m[G], l[G];
   f32x4_t o[NH][NDT];
@@ -609,17 +639,22 @@ struct MfmaPvEngine {
     return base + CT * (k0 + rotated(wave + k * nw, rot, len));
   }
 
+  // Raw table entries of the wave's chunks 64w .. 64w+63 (lane l: chunk 64w + l); entries
+  // of chunks or blocks past the end read entry 0 of the row instead (never used for a
+  // valid token). Ids are clamped into the pool when they are taken (block_id).
   __device__ __forceinline__ void load_window(const DecodeArgs& a, int w, int (&dst)[NBC]) {
     const int k = 64 * w + li.lane;
     const bool live = wave + k * nw < len;
     const int j = live ? chunk_token(k) / BS : 0;
 #pragma unroll
-    for (int u = 0; u < NBC; ++u) {
-      int b = 0;
-      if (live && j + u < j_end) b = bt[j + u];
-      // contract: 0 <= b < num_blocks; clamp so that a bad table never reads outside the pool
-      dst[u] = min(max(b, 0), a.num_blocks - 1);
-    }
+    for (int u = 0; u < NBC; ++u) dst[u] = bt[live && j + u < j_end ? j + u : 0];
+  }
+
+  // Block id of the u-th block of chunk k (k in the current window), clamped into the
+  // pool so that a bad table never reads outside it (contract: 0 <= id < num_blocks).
+  __device__ __forceinline__ int64_t block_off(const DecodeArgs& a, int u, int k) const {
+    const int b = __builtin_amdgcn_readlane(win[0][u], k & 63);
+    return (int64_t)min(max(b, 0), a.num_blocks - 1) * blk_stride;
   }
 
   __device__ __forceinline__ void begin(const DecodeArgs& a, int s_, int g_, int t_end_, int base_,
@@ -640,6 +675,7 @@ struct MfmaPvEngine {
     vbase = (const char*)a.v_pool + (int64_t)g * TILE_BYTES;
     load_window(a, 0, win[0]);
     load_window(a, 1, win[1]);
+    cur_win = 0;
     // half h2 holds heads g*G + 4*h2 + (0..HG-1): those of "KV head" g*NH + h2 at group HG
 #pragma unroll
     for (int h2 = 0; h2 < NH; ++h2) load_q<IO, KV, D, HG>(a, s, g * NH + h2, li, qa[h2]);
@@ -655,41 +691,40 @@ struct MfmaPvEngine {
   }
 
   __device__ __forceinline__ void issue(const DecodeArgs& a, Buf& b, int k) {
-    if ((k & 63) == 0 && k > 0) {
+    if ((k >> 6) != cur_win) {
+      cur_win = k >> 6;
 #pragma unroll
       for (int u = 0; u < NBC; ++u) win[0][u] = win[1][u];
-      load_window(a, (k >> 6) + 1, win[1]);
+      load_window(a, cur_win + 1, win[1]);
     }
     int64_t off[NBC];
 #pragma unroll
-    for (int u = 0; u < NBC; ++u)
-      off[u] = (int64_t)__builtin_amdgcn_readlane(win[0][u], k & 63) * blk_stride;
+    for (int u = 0; u < NBC; ++u) off[u] = block_off(a, u, k);
     const int c0 = chunk_token(k);
     const int jb = c0 / BS;
-    const bool tail = c0 + CT > t_end;
+    // Rows at or past t_end read token c0's row instead (see issue_chunk): every load is
+    // unconditional.
     // K: lane (n, lg) loads chunks 4i + lg of token n
     {
-      const int to = c0 + li.n;
+      int to = c0 + li.n;
+      to = to < t_end ? to : c0;
       int64_t bo = off[0];
 #pragma unroll
       for (int u = 1; u < NBC; ++u) bo = to / BS - jb == u ? off[u] : bo;
       const char* krow = kbase + bo + (to % BS) * RB;
-      const bool ok = !tail || to < t_end;
 #pragma unroll
-      for (int i = 0; i < Geo::CPL; ++i)
-        b.kr[i] = ok ? load16(krow + 16 * (4 * i + li.lg)) : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < Geo::CPL; ++i) b.kr[i] = load16(krow + 16 * (4 * i + li.lg));
     }
     // V: instruction i covers bytes 1024*i .. of the 16 rows, in memory order
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int byte = 1024 * i + 16 * li.lane;
-      const int t = c0 + byte / RB;
+      int t = c0 + byte / RB;
+      t = t < t_end ? t : c0;
       int64_t bo = off[0];
 #pragma unroll
       for (int u = 1; u < NBC; ++u) bo = t / BS - jb == u ? off[u] : bo;
-      const char* p = vbase + bo + (t % BS) * RB + byte % RB;
-      const bool ok = !tail || t < t_end;
-      b.vt.v[i] = ok ? load16(p) : make_uint4(0, 0, 0, 0);
+      b.vt.v[i] = load16(vbase + bo + (t % BS) * RB + byte % RB);
     }
   }
 
@@ -840,17 +875,7 @@ struct MfmaPvEngine {
 
   __device__ __forceinline__ void run(const DecodeArgs& a) {
     const int nwc = wave < len ? (len - wave + nw - 1) / nw : 0;
-    Buf A, B;
-    if (nwc > 0) issue(a, A, 0);
-    if (nwc > 1) issue(a, B, 1);
-    for (int k = 0; k < nwc; k += 2) {
-      consume(a, A, k);
-      if (k + 2 < nwc) issue(a, A, k + 2);
-      if (k + 1 < nwc) {
-        consume(a, B, k + 1);
-        if (k + 3 < nwc) issue(a, B, k + 3);
-      }
-    }
+    run_pipelined(*this, a, nwc);
   }
 
   template <int NW>
@@ -1013,8 +1038,10 @@ __device__ __forceinline__ int64_t chunk_owner(int64_t x, int64_t C, int64_t nwg
 // Floats per partial-state slot: m[G], l[G], o[G][D].
 template <int G, int D> constexpr int slot_floats() { return G * (D + 2); }
 
+// At least two waves per SIMD (the default grid is two workgroups per CU): the register
+// allocator must fit VGPRs and AGPRs together into 256 per lane.
 template <int IO, int KV, int D, int BS, int G, int NW, bool DBG>
-__global__ void __launch_bounds__(NW * 64)
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 balanced_decode_kernel(const DecodeArgs a) {
   using Sel = EngineFor<IO, KV, D, BS, G, DBG>;
   using Eng = typename Sel::type;
@@ -1035,15 +1062,18 @@ balanced_decode_kernel(const DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
 
-  // 1. chunks per sequence (at least one, so that empty sequences get their zero output
-  //    written) and their exclusive prefix sums, thread t owning a contiguous run of S/NTH
+  // 1. cost of each sequence in chunk units: kSegCost for the fixed work of a segment
+  //    (set-up, wave merge, write) plus its chunks (at least one, so that empty sequences
+  //    get their zero output written); exclusive prefix sums of the costs, thread t owning
+  //    a contiguous run of S/NTH sequences. Real chunk k of sequence s sits at cost
+  //    position sm_pref[s] + kSegCost + k.
   const int per = (S + NTH - 1) / NTH;
   const int i0 = min(S, tid * per);
   const int i1 = min(S, i0 + per);
   int local = 0;
   for (int i = i0; i < i1; ++i) {
     const int L = min(max(a.context_lens[i], 0), a.max_ctx);
-    local += max(1, (L + CT - 1) / CT);
+    local += kSegCost + max(1, (L + CT - 1) / CT);
   }
   int incl = local;  // inclusive scan over the wave
 #pragma unroll
@@ -1059,7 +1089,7 @@ balanced_decode_kernel(const DecodeArgs a) {
   for (int i = i0; i < i1; ++i) {
     sm_pref[i] = run;
     const int L = min(max(a.context_lens[i], 0), a.max_ctx);
-    run += max(1, (L + CT - 1) / CT);
+    run += kSegCost + max(1, (L + CT - 1) / CT);
   }
   if (tid == NTH - 1) {
     int tot = 0;
@@ -1068,19 +1098,18 @@ balanced_decode_kernel(const DecodeArgs a) {
   }
   __syncthreads();
 
-  // 2. this workgroup's chunk range [cb, ce) of the C = Hkv * Cg chunks (KV-head major)
+  // 2. this workgroup's range [cb, ce) of the C = Hkv * Cg cost positions (KV-head major)
   const int Cg = sm_pref[S];
   const int64_t C = (int64_t)a.num_kv_heads * Cg;
   const int64_t nwg = min((int64_t)a.nwg, C);
   const int64_t v = xcd_unit((int)blockIdx.x, (int)gridDim.x);
-  if (v >= nwg) return;  // more workgroups than chunks (whole workgroup)
+  if (v >= nwg) return;  // more workgroups than cost positions (whole workgroup)
   const int64_t cb = chunk_begin(v, C, nwg);
   const int64_t ce = chunk_begin(v + 1, C, nwg);
 
   Eng eng = EngineMaker<Eng>::make(lane, sm_eng[wave]);
   const int H = a.num_heads;
   int64_t c = cb;
-  bool first_seg = true;
   while (c < ce) {
     const int g = (int)(c / Cg);
     const int r = (int)(c - (int64_t)g * Cg);
@@ -1091,10 +1120,14 @@ balanced_decode_kernel(const DecodeArgs a) {
       if (sm_pref[mid] <= r) lo = mid; else hi = mid;
     }
     const int s = lo;
-    const int nch = sm_pref[s + 1] - sm_pref[s];
-    const int k0 = r - sm_pref[s];
-    const int len = (int)min((int64_t)(nch - k0), ce - c);
-    const int k1 = k0 + len;
+    const int u0 = sm_pref[s] + kSegCost;  // cost position of real chunk 0
+    const int nch = sm_pref[s + 1] - u0;
+    const int64_t seg_end = min((int64_t)g * Cg + sm_pref[s + 1], ce);
+    const int k0 = max(0, r - u0);
+    const int k1 = (int)max((int64_t)0, seg_end - (int64_t)g * Cg - u0);
+    c = seg_end;
+    if (k1 <= k0) continue;  // only the fixed-cost part of this sequence is in the range
+    const int len = k1 - k0;
     const int L = min(max(a.context_lens[s], 0), a.max_ctx);
 
     const int rot = PA_STAGGER ? (s * 5) % len : 0;
@@ -1114,9 +1147,12 @@ balanced_decode_kernel(const DecodeArgs a) {
         store_io<IO>(a.out, ((int64_t)s * H + g * G + gi) * D + d, val);
       }
     } else {
-      // a piece: store (m, l, o) in this workgroup's slot (0 = its first segment, 1 = its
-      // last) with device-coherent stores, then count the arrival
-      float* slot = a.ws + ((int64_t)v * 2 + (first_seg ? 0 : 1)) * SLOT;
+      // a piece: store (m, l, o) in one of this workgroup's two slots with device-coherent
+      // stores, then count the arrival. Slot 0 holds the piece of the sequence that starts
+      // inside the workgroup's range and runs past its end, slot 1 the piece of the one that
+      // started before the range (at most one of each).
+      const int64_t ub = (int64_t)g * Cg + u0;  // cost position of this (s, g)'s first chunk
+      float* slot = a.ws + ((int64_t)v * 2 + (cb >= ub ? 0 : 1)) * SLOT;
       for (int idx = tid; idx < G * D; idx += NTH) {
         const int gi = idx / D;
         const int d = idx % D;
@@ -1131,7 +1167,6 @@ balanced_decode_kernel(const DecodeArgs a) {
       // every store of this workgroup has completed before the arrival is counted
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      const int64_t ub = (int64_t)g * Cg + sm_pref[s];  // first chunk of this (s, g)
       const int64_t w0 = chunk_owner(ub, C, nwg);
       const int64_t w1 = chunk_owner(ub + nch - 1, C, nwg);
       int32_t* counter = a.counters + (int64_t)g * S + s;
@@ -1168,8 +1203,6 @@ balanced_decode_kernel(const DecodeArgs a) {
       }
     }
     __syncthreads();  // LDS is reused by the next segment
-    c += len;
-    first_seg = false;
   }
 }
 
