@@ -236,6 +236,17 @@ __device__ __forceinline__ int xcd_unit(int i, int n) {
 // the decode kernel
 // ---------------------------------------------------------------------------------
 
+// Tokens per wave step of the vector kernel, the same for every block size (the token
+// order of a wave, and hence the result, does not depend on the block size).
+#ifndef PA_CHUNK_TOKENS
+#define PA_CHUNK_TOKENS 32
+#endif
+// Steps whose loads a wave of the vector kernel keeps in flight.
+#ifndef PA_VEC_DEPTH
+#define PA_VEC_DEPTH 1
+#endif
+constexpr int kVecDepth = PA_VEC_DEPTH;
+
 // Blocks larger than SB tokens (32, or 16 / 8 for 512- / 1024-byte rows) are walked as
 // SB-token sub-blocks: sub-block j covers tokens SB j .. SB j + SB - 1, lies in logical
 // block j / SPB at row SB (j % SPB), and is itself one contiguous run of its tile.
@@ -245,8 +256,9 @@ struct Geometry {
   static constexpr int VEC = 16 / E;           // elements per lane load
   static constexpr int LPT = D / VEC;          // lanes per token row
   static constexpr int TPL = 64 / LPT;         // token rows per wave load
-  // tokens per (sub-)block step: at most 32, and at most 8 wave loads (head_dim 256)
-  static constexpr int SB_MAX = 8 * TPL < 32 ? 8 * TPL : 32;
+  // tokens per (sub-)block step: at most PA_CHUNK_TOKENS, and at most 8 wave loads
+  // (head_dim 256)
+  static constexpr int SB_MAX = 8 * TPL < PA_CHUNK_TOKENS ? 8 * TPL : PA_CHUNK_TOKENS;
   static constexpr int SB = BS < SB_MAX ? BS : SB_MAX;
   static constexpr int SPB = BS / SB;          // sub-blocks per block
   static constexpr int NL = SB / TPL;          // wave loads per sub-block
@@ -278,56 +290,52 @@ __device__ __forceinline__ uint4 load16(const char* p) {
 #endif
 }
 
-// One chunk of U consecutive (sub-)blocks starting at j0. TAIL: the chunk reaches past
-// the end of the unit's token range (some rows or whole blocks are invalid).
-template <int IO, int KV, int D, int BS, int G, int U, bool TAIL, bool DBG>
-__device__ __forceinline__ void process_chunk(const DecodeArgs& a, const int32_t* bt,
-                                              const char* kbase, const char* vbase,
-                                              int64_t blk_stride, int j0, int j_end, int t_end,
-                                              int r, int c, int s, int g,
-                                              const float (&qf)[G][16 / ElemBytes<KV>::value],
-                                              RowState<G, 16 / ElemBytes<KV>::value>& st) {
+// K/V registers of one wave step: U consecutive (sub-)blocks, NL wave loads each.
+template <int KV, int D, int BS, int G, int U>
+struct StepBuf {
   using Geo = Geometry<KV, D, BS, G>;
-  constexpr int VEC = Geo::VEC, NL = Geo::NL, TPL = Geo::TPL, LPT = Geo::LPT, SB = Geo::SB,
-                SPB = Geo::SPB;
+  uint4 kr[U][Geo::NL];
+  uint4 vr[U][Geo::NL];
+};
+
+// Issue the K/V loads of the step whose first (sub-)block is j0 (j0 * SB < t_end), with
+// bid[u] the physical block of (sub-)block j0 + u. A lane whose row is at or past t_end
+// reads row j0 * SB instead (finite data of this step; the score of such a row is
+// excluded by select, so its probability is exactly 0). Every load is unconditional:
+// loads under a branch make the compiler wait for every outstanding load, those of the
+// next step included, before the step's data is used.
+template <int KV, int D, int BS, int G, int U>
+__device__ __forceinline__ void issue_step(StepBuf<KV, D, BS, G, U>& b, const char* kbase, const char* vbase,
+                                           int64_t blk_stride, const int (&bid)[U], int j0, int t_end,
+                                           int r, int c) {
+  using Geo = Geometry<KV, D, BS, G>;
+  constexpr int NL = Geo::NL, TPL = Geo::TPL, SB = Geo::SB, SPB = Geo::SPB;
   const uint32_t lane_off = (uint32_t)(r * Geo::ROW_BYTES + c * 16);
-
-  int bid[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int j = j0 + u;
-    int b = 0;
-    if (!TAIL || j < j_end) b = bt[j / SPB];
-    // contract: 0 <= b < num_blocks; clamp so that a bad table never reads outside the pool
-    b = min(max(b, 0), a.num_blocks - 1);
-    bid[u] = __builtin_amdgcn_readfirstlane(b);
-  }
-
-  uint4 kr[U][NL];
-  uint4 vr[U][NL];
+  const int64_t sub0 = SPB > 1 ? (int64_t)(j0 % SPB) * SB * Geo::ROW_BYTES : 0;
+  const int64_t first = (int64_t)bid[0] * blk_stride + sub0 + c * 16;  // row j0 * SB
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t sub = SPB > 1 ? (int64_t)((j0 + u) % SPB) * SB * Geo::ROW_BYTES : 0;
-    const char* kb = kbase + (int64_t)bid[u] * blk_stride + sub;
-    const char* vb = vbase + (int64_t)bid[u] * blk_stride + sub;
+    const int64_t tile = (int64_t)bid[u] * blk_stride + sub;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const uint32_t off = lane_off + (uint32_t)(i * TPL * Geo::ROW_BYTES);
-      if (TAIL) {
-        const int t = (j0 + u) * SB + i * TPL + r;
-        if (t < t_end) {
-          kr[u][i] = load16(kb + off);
-          vr[u][i] = load16(vb + off);
-        } else {
-          kr[u][i] = make_uint4(0, 0, 0, 0);
-          vr[u][i] = make_uint4(0, 0, 0, 0);
-        }
-      } else {
-        kr[u][i] = load16(kb + off);
-        vr[u][i] = load16(vb + off);
-      }
+      const int t = (j0 + u) * SB + i * TPL + r;
+      const int64_t off = t < t_end ? tile + lane_off + i * TPL * Geo::ROW_BYTES : first;
+      b.kr[u][i] = load16(kbase + off);
+      b.vr[u][i] = load16(vbase + off);
     }
   }
+}
+
+// Scores, online-softmax update and V accumulation of one loaded step (first (sub-)block
+// j0). TAIL: the step reaches past t_end; those rows get score -inf by select.
+template <int IO, int KV, int D, int BS, int G, int U, bool TAIL, bool DBG>
+__device__ __forceinline__ void consume_step(const DecodeArgs& a, const StepBuf<KV, D, BS, G, U>& b, int j0,
+                                             int t_end, int r, int c, int s, int g,
+                                             const float (&qf)[G][16 / ElemBytes<KV>::value],
+                                             RowState<G, 16 / ElemBytes<KV>::value>& st) {
+  using Geo = Geometry<KV, D, BS, G>;
+  constexpr int VEC = Geo::VEC, NL = Geo::NL, TPL = Geo::TPL, LPT = Geo::LPT, SB = Geo::SB;
 
   if constexpr (DBG) {
     const int Hkv = a.num_kv_heads;
@@ -338,8 +346,8 @@ __device__ __forceinline__ void process_chunk(const DecodeArgs& a, const int32_t
         const int t = (j0 + u) * SB + i * TPL + r;
         if (t < t_end) {
           const int64_t row = ((int64_t)s * Hkv + g) * a.dbg_max_ctx + t;
-          *(uint4*)((char*)a.dbg_k + row * Geo::ROW_BYTES + c * 16) = kr[u][i];
-          *(uint4*)((char*)a.dbg_v + row * Geo::ROW_BYTES + c * 16) = vr[u][i];
+          *(uint4*)((char*)a.dbg_k + row * Geo::ROW_BYTES + c * 16) = b.kr[u][i];
+          *(uint4*)((char*)a.dbg_v + row * Geo::ROW_BYTES + c * 16) = b.vr[u][i];
           if (c == 0) atomicAdd(a.dbg_counts + row, 1);
         }
       }
@@ -353,7 +361,7 @@ __device__ __forceinline__ void process_chunk(const DecodeArgs& a, const int32_t
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       float kf[VEC];
-      widen16<KV>(kr[u][i], kf);
+      widen16<KV>(b.kr[u][i], kf);
 #pragma unroll
       for (int gi = 0; gi < G; ++gi) {
         float acc = 0.f;
@@ -388,7 +396,7 @@ __device__ __forceinline__ void process_chunk(const DecodeArgs& a, const int32_t
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       float vf[VEC];
-      widen16<KV>(vr[u][i], vf);
+      widen16<KV>(b.vr[u][i], vf);
 #pragma unroll
       for (int gi = 0; gi < G; ++gi) {
         const float p = __builtin_amdgcn_exp2f(z[u][i][gi] - st.m[gi]);
@@ -398,6 +406,37 @@ __device__ __forceinline__ void process_chunk(const DecodeArgs& a, const int32_t
       }
     }
   }
+}
+
+// Physical blocks of the (sub-)blocks j0 .. j0+U-1 of a step (j0 < j_end): scalar loads
+// of the table row; (sub-)blocks past the end take the step's first block (their rows
+// are never used). Ids are clamped into the pool so that a bad table never reads outside
+// it (contract: 0 <= id < num_blocks).
+template <int KV, int D, int BS, int G, int U>
+__device__ __forceinline__ void step_blocks(const DecodeArgs& a, const int32_t* bt, int j0, int j_end,
+                                            int (&bid)[U]) {
+  constexpr int SPB = Geometry<KV, D, BS, G>::SPB;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = j0 + u < j_end ? j0 + u : j0;
+    const int b = __builtin_amdgcn_readfirstlane(bt[j / SPB]);
+    bid[u] = min(max(b, 0), a.num_blocks - 1);
+  }
+}
+
+// One step of U consecutive (sub-)blocks starting at j0, loaded and consumed at once.
+template <int IO, int KV, int D, int BS, int G, int U, bool TAIL, bool DBG>
+__device__ __forceinline__ void process_chunk(const DecodeArgs& a, const int32_t* bt,
+                                              const char* kbase, const char* vbase,
+                                              int64_t blk_stride, int j0, int j_end, int t_end,
+                                              int r, int c, int s, int g,
+                                              const float (&qf)[G][16 / ElemBytes<KV>::value],
+                                              RowState<G, 16 / ElemBytes<KV>::value>& st) {
+  int bid[U];
+  step_blocks<KV, D, BS, G, U>(a, bt, j0, j_end, bid);
+  StepBuf<KV, D, BS, G, U> buf;
+  issue_step<KV, D, BS, G, U>(buf, kbase, vbase, blk_stride, bid, j0, t_end, r, c);
+  consume_step<IO, KV, D, BS, G, U, TAIL, DBG>(a, buf, j0, t_end, r, c, s, g, qf, st);
 }
 
 template <int IO, int KV, int D, int BS, int G, int NW, int U, bool DBG>
@@ -455,14 +494,44 @@ decode_kernel(const DecodeArgs a) {
   const char* kbase = (const char*)a.k_pool + (int64_t)g * Geo::TILE;
   const char* vbase = (const char*)a.v_pool + (int64_t)g * Geo::TILE;
 
-  for (int j0 = j_begin + wave * U; j0 < j_end; j0 += NW * U) {
-    if ((j0 + U) * SB <= t_end) {
-      process_chunk<IO, KV, D, BS, G, U, false, DBG>(a, bt, kbase, vbase, blk_stride, j0, j_end,
-                                                     t_end, r, c, s, g, qf, st);
-    } else {
-      process_chunk<IO, KV, D, BS, G, U, true, DBG>(a, bt, kbase, vbase, blk_stride, j0, j_end,
-                                                    t_end, r, c, s, g, qf, st);
+  // This wave's steps k = 0 .. nwc-1 start at (sub-)block j_begin + (wave + k NW) U; the
+  // loads of kVecDepth steps are in flight. Past the last step the issue repeats step
+  // nwc - 1 (cached data, never consumed), so that the loop issues unconditionally.
+  const int steps = (j_end - j_begin + U - 1) / U;
+  const int nwc = wave < steps ? (steps - wave + NW - 1) / NW : 0;
+  if (nwc > 0) {
+    using Buf = StepBuf<KV, D, BS, G, U>;
+    auto j0_of = [&](int k) { return j_begin + (wave + min(k, nwc - 1) * NW) * U; };
+    auto consume = [&](const Buf& b, int k) {
+      const int j0 = j0_of(k);
+      if ((j0 + U) * SB <= t_end) {
+        consume_step<IO, KV, D, BS, G, U, false, DBG>(a, b, j0, t_end, r, c, s, g, qf, st);
+      } else {
+        consume_step<IO, KV, D, BS, G, U, true, DBG>(a, b, j0, t_end, r, c, s, g, qf, st);
+      }
+    };
+    Buf buf[kVecDepth];
+    int nid[kVecDepth][U];  // block ids of the next step issued into each buffer
+#pragma unroll
+    for (int d = 0; d < kVecDepth; ++d) {
+      int bid[U];
+      step_blocks<KV, D, BS, G, U>(a, bt, j0_of(d), j_end, bid);
+      issue_step<KV, D, BS, G, U>(buf[d], kbase, vbase, blk_stride, bid, j0_of(d), t_end, r, c);
+      step_blocks<KV, D, BS, G, U>(a, bt, j0_of(d + kVecDepth), j_end, nid[d]);
     }
+    int k = 0;
+    for (; k + kVecDepth <= nwc; k += kVecDepth) {
+#pragma unroll
+      for (int d = 0; d < kVecDepth; ++d) {
+        consume(buf[d], k + d);
+        const int kn = k + d + kVecDepth;
+        issue_step<KV, D, BS, G, U>(buf[d], kbase, vbase, blk_stride, nid[d], j0_of(kn), t_end, r, c);
+        step_blocks<KV, D, BS, G, U>(a, bt, j0_of(kn + kVecDepth), j_end, nid[d]);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < kVecDepth - 1; ++d)
+      if (k + d < nwc) consume(buf[d], k + d);
   }
 
   // merge the row groups of this wave
@@ -636,8 +705,9 @@ struct LaunchSpec {
 #ifndef PA_WAVES
 #define PA_WAVES 4
 #endif
-#ifndef PA_CHUNK_TOKENS
-#define PA_CHUNK_TOKENS 32
+// Waves per workgroup of the one-unit-per-workgroup matrix-core kernel.
+#ifndef PA_MFMA_WAVES
+#define PA_MFMA_WAVES PA_WAVES
 #endif
 
 template <int IO, int KV, int D, int BS, int G>
@@ -674,12 +744,13 @@ int launch_one(const LaunchSpec& ls) {
     // one workgroup per unit: the matrix-core kernel when query heads share a KV head; for
     // one query head per KV head the vector kernel (whole 1 KiB rows per wave load) is faster
     if constexpr (PA_MFMA && G >= 2 && mfma_supported<IO, KV, D, G>()) {
+      constexpr int NWM = PA_MFMA_WAVES;
       if (ls.debug) {
-        hipLaunchKernelGGL((mfma_decode_kernel<IO, KV, D, BS, G, NW, true>), dim3(ls.grid),
-                           dim3(NW * 64), 0, ls.stream, ls.args);
+        hipLaunchKernelGGL((mfma_decode_kernel<IO, KV, D, BS, G, NWM, true>), dim3(ls.grid),
+                           dim3(NWM * 64), 0, ls.stream, ls.args);
       } else {
-        hipLaunchKernelGGL((mfma_decode_kernel<IO, KV, D, BS, G, NW, false>), dim3(ls.grid),
-                           dim3(NW * 64), 0, ls.stream, ls.args);
+        hipLaunchKernelGGL((mfma_decode_kernel<IO, KV, D, BS, G, NWM, false>), dim3(ls.grid),
+                           dim3(NWM * 64), 0, ls.stream, ls.args);
       }
       return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
     }
