@@ -261,7 +261,7 @@ def main():
     ap.add_argument("--workload", default="",
                     help="a named variant of a config (larger blocks) or an extend workload "
                          "(extend_*), instead of --config")
-    ap.add_argument("--mode", default="auto", choices=["auto", "direct", "partitioned", "balanced"])
+    ap.add_argument("--mode", default="auto", choices=["auto", "direct", "partitioned", "balanced", "ordered"])
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--workgroups", type=int, default=0,
                     help="balanced mode: workgroup count (0 = library default)")
@@ -338,6 +338,8 @@ def main():
         plan = pa.DecodePlan(q, k0, v0, bt, cl, **kw)
     elif mode == "balanced":
         plan = pa.DecodePlan(q, k0, v0, bt, cl, balanced=True, num_workgroups=args.workgroups, **kw)
+    elif mode == "ordered":
+        plan = pa.DecodePlan(q, k0, v0, bt, cl, ordered=True, **kw)
     else:
         plan = pa.DecodePlan(q, k0, v0, bt, cl, max_context_len=maxL, partition_size=P,
                              workspace=ws, **kw)
@@ -388,7 +390,8 @@ def main():
     # Workspaces are made before the capture, so the graph holds the decode kernels only.
     graph_ms = None
     try:
-        gws = pa.balanced_workspace(q, k0, args.workgroups) if mode == "balanced" else ws
+        gws = (pa.balanced_workspace(q, k0, args.workgroups) if mode == "balanced"
+               else pa.ordered_workspace(q) if mode == "ordered" else ws)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
@@ -398,6 +401,8 @@ def main():
             elif mode == "balanced":
                 gplan = pa.DecodePlan(q, k0, v0, bt, cl, balanced=True, num_workgroups=args.workgroups,
                                       workspace=gws, **gkw)
+            elif mode == "ordered":
+                gplan = pa.DecodePlan(q, k0, v0, bt, cl, ordered=True, workspace=gws, **gkw)
             else:
                 gplan = pa.DecodePlan(q, k0, v0, bt, cl, max_context_len=maxL, partition_size=P,
                                       workspace=gws, **gkw)

@@ -147,6 +147,26 @@ int pa_decode_balanced(const void* q, const void* k_pool, const void* v_pool,
                        int num_workgroups, void* workspace, size_t workspace_bytes,
                        void* out, void* stream);
 
+/* Workspace for pa_decode_ordered, in bytes (0 on invalid sizes): one int32 per
+ * sequence, padded to 256 bytes. */
+size_t pa_ordered_workspace_bytes(int num_seqs);
+
+/* Longest-first decode. Same result as pa_decode, bit for bit (the same kernels compute
+ * every (KV head, sequence)); only the dispatch order differs. A first one-workgroup
+ * launch sorts the sequences by context-length class (four classes per doubling of the
+ * length, longest first) into the workspace; the decode launch then hands each XCD its
+ * share of the (KV head, sequence) units longest sequence first, so that batches mixing
+ * short and long contexts ([P2] §5.3's length mix) do not end with a few long sequences
+ * running alone. Workspace: pa_ordered_workspace_bytes(num_seqs) bytes, 16-byte aligned,
+ * overwritten by every call (calls sharing it must be ordered on one stream). Errors as
+ * pa_decode, plus PA_ERR_WORKSPACE when the workspace is missing or too small. */
+int pa_decode_ordered(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      int num_seqs, int max_blocks_per_seq, int num_blocks,
+                      int num_heads, int num_kv_heads, int head_dim, int block_size,
+                      float scale, int io_dtype, int kv_dtype, float k_scale, float v_scale,
+                      void* workspace, size_t workspace_bytes, void* out, void* stream);
+
 /* Instrumented decode for tests ([P1] §2 block-table reading; every cached position
  * is read exactly once). Runs the same kernels as pa_decode (partition_size == 0 and
  * num_workgroups == 0), pa_decode_partitioned (partition_size > 0, workspace required) or

@@ -33,6 +33,8 @@ SIGNATURES = {
     "pa_decode_partitioned": (_I, _DECODE_ARGS + [_I, _I, _P, _SZ, _P, _P]),
     "pa_balanced_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "pa_decode_balanced": (_I, _DECODE_ARGS + [_I, _P, _SZ, _P, _P]),
+    "pa_ordered_workspace_bytes": (_SZ, [_I]),
+    "pa_decode_ordered": (_I, _DECODE_ARGS + [_P, _SZ, _P, _P]),
     "pa_debug_trace": (_I, _DECODE_ARGS + [_I, _I, _I, _P, _SZ, _P, _P, _P, _P, _P]),
     "pa_check_tables": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "pa_append_kv": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _P]),
@@ -264,6 +266,31 @@ def pa_decode_balanced(q, k_pool, v_pool, block_tables, context_lens, scale: Opt
     return out
 
 
+def pa_ordered_workspace_bytes(num_seqs: int) -> int:
+    return int(lib().pa_ordered_workspace_bytes(num_seqs))
+
+
+def ordered_workspace(q):
+    """Workspace for pa_decode_ordered (overwritten by every call)."""
+    torch = _torch()
+    need = pa_ordered_workspace_bytes(q.shape[0])
+    return torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+
+
+def pa_decode_ordered(q, k_pool, v_pool, block_tables, context_lens, scale: Optional[float] = None,
+                      workspace=None, k_scale: float = 1.0, v_scale: float = 1.0, out=None,
+                      stream=None):
+    """Longest-first paged decode (same result as pa_decode); returns out."""
+    args, out, _ = _common(q, k_pool, v_pool, block_tables, context_lens, scale, k_scale, v_scale, out)
+    if workspace is None:
+        workspace = ordered_workspace(q)
+    _check_dev("workspace", workspace)
+    nbytes = workspace.numel() * workspace.element_size()
+    _raise("pa_decode_ordered",
+           lib().pa_decode_ordered(*args, workspace.data_ptr(), nbytes, out.data_ptr(), _stream(stream)))
+    return out
+
+
 def pa_debug_trace(q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
                    scale: Optional[float] = None, partition_size: int = 0, num_workgroups: int = 0,
                    k_scale: float = 1.0, v_scale: float = 1.0, stream=None):
@@ -300,7 +327,8 @@ class DecodePlan:
     def __init__(self, q, k_pool, v_pool, block_tables, context_lens, scale=None,
                  k_scale: float = 1.0, v_scale: float = 1.0, out=None,
                  max_context_len: Optional[int] = None, partition_size: int = 0,
-                 workspace=None, stream=None, balanced: bool = False, num_workgroups: int = 0):
+                 workspace=None, stream=None, balanced: bool = False, num_workgroups: int = 0,
+                 ordered: bool = False):
         torch = _torch()
         args, out, (S, H, D, *_r) = _common(q, k_pool, v_pool, block_tables, context_lens,
                                             scale, k_scale, v_scale, out)
@@ -316,6 +344,14 @@ class DecodePlan:
             self._fn = lib().pa_decode_balanced
             tail = [int(num_workgroups), workspace.data_ptr(),
                     workspace.numel() * workspace.element_size(), out.data_ptr(), st]
+        elif ordered:
+            if workspace is None:
+                workspace = ordered_workspace(q)
+            _check_dev("workspace", workspace)
+            self._keep.append(workspace)
+            self._fn = lib().pa_decode_ordered
+            tail = [workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                    out.data_ptr(), st]
         elif max_context_len is None:
             self._fn = lib().pa_decode
             tail = [out.data_ptr(), st]

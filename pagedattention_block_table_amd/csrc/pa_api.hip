@@ -220,6 +220,47 @@ DecodeArgs base_args(const Common& c) {
   return a;
 }
 
+// Length classes of the ordered mode: four per doubling of the context length
+// (4 floor(log2 L) plus the next two bits of L), longest class dispatched first.
+constexpr int kOrderClasses = 128;
+
+__device__ __forceinline__ int length_class(int L) {
+  if (L <= 1) return 0;
+  const int e = 31 - __builtin_clz((unsigned)L);
+  const int frac = e >= 2 ? (L >> (e - 2)) & 3 : (L << (2 - e)) & 3;
+  return min(4 * e + frac, kOrderClasses - 1);
+}
+
+// Ordered mode, first launch (one workgroup): a counting sort of the sequences by length
+// class, longest class first, into order[0 .. S-1]. Within a class the order is that of
+// the atomics; it only decides when a sequence is scheduled, never what is computed.
+__global__ void __launch_bounds__(1024) order_kernel(const int32_t* context_lens, int S, int max_ctx,
+                                                     int32_t* order) {
+  __shared__ int count[kOrderClasses];
+  for (int i = threadIdx.x; i < kOrderClasses; i += blockDim.x) count[i] = 0;
+  __syncthreads();
+  for (int s = threadIdx.x; s < S; s += blockDim.x) {
+    const int L = min(max(context_lens[s], 0), max_ctx);
+    atomicAdd(&count[length_class(L)], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;  // exclusive prefix sums from the longest class down
+    for (int b = kOrderClasses - 1; b >= 0; --b) {
+      const int n = count[b];
+      count[b] = run;
+      run += n;
+    }
+  }
+  __syncthreads();
+  for (int s = threadIdx.x; s < S; s += blockDim.x) {
+    const int L = min(max(context_lens[s], 0), max_ctx);
+    order[atomicAdd(&count[length_class(L)], 1)] = s;
+  }
+}
+
+size_t ordered_workspace_bytes(int S) { return (size_t)((((int64_t)S * 4) + 255) / 256 * 256); }
+
 int64_t num_parts_for(int max_context_len, int P) {
   const int64_t n = ((int64_t)max_context_len + P - 1) / P;
   return n < 1 ? 1 : n;
@@ -272,7 +313,7 @@ BalancedLayout balanced_layout(int S, int H, int Hkv, int D, int nwg) {
   return b;
 }
 
-enum class Mode { kSingle, kPartitioned, kBalanced };
+enum class Mode { kSingle, kPartitioned, kBalanced, kOrdered };
 
 // Shared body of every entry point. P is the partition size (partitioned mode), nwg the
 // workgroup count (balanced mode).
@@ -328,6 +369,16 @@ int run(const Common& c, Mode mode, int max_context_len, int P, int nwg, void* w
     ls.balanced = true;
     ls.grid = nwg;
     return launch_pair(c.io, c.kv, ls);
+  }
+  if (mode == Mode::kOrdered) {
+    if (!workspace || ws_bytes < ordered_workspace_bytes(c.S)) return PA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PA_ERR_INVALID;
+    if ((int64_t)c.Hkv * c.S > INT_MAX) return PA_ERR_INVALID;
+    hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, st, c.cl, c.S, ls.args.max_ctx,
+                       (int32_t*)workspace);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
+    ls.args.order = (const int32_t*)workspace;
+    ls.args.order_hpx = c.Hkv % 8 == 0 ? c.Hkv / 8 : 0;
   }
   const int64_t grid = (int64_t)c.Hkv * c.S * NP;
   if (grid > INT_MAX) return PA_ERR_INVALID;
@@ -422,6 +473,27 @@ int pa_decode_balanced(const void* q, const void* k_pool, const void* v_pool,
                  kv_dtype, k_scale, v_scale, out};
     return pa::run(c, pa::Mode::kBalanced, -1, 0, num_workgroups, workspace, workspace_bytes,
                    nullptr, nullptr, nullptr, false, (hipStream_t)stream);
+  } catch (...) {
+    return PA_ERR_LAUNCH;
+  }
+}
+
+size_t pa_ordered_workspace_bytes(int num_seqs) {
+  return num_seqs <= 0 ? 0 : pa::ordered_workspace_bytes(num_seqs);
+}
+
+int pa_decode_ordered(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                      int max_blocks_per_seq, int num_blocks, int num_heads, int num_kv_heads,
+                      int head_dim, int block_size, float scale, int io_dtype, int kv_dtype,
+                      float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+                      void* out, void* stream) {
+  try {
+    pa::Common c{q, k_pool, v_pool, block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                 num_blocks, num_heads, num_kv_heads, head_dim, block_size, scale, io_dtype,
+                 kv_dtype, k_scale, v_scale, out};
+    return pa::run(c, pa::Mode::kOrdered, -1, 0, 0, workspace, workspace_bytes, nullptr, nullptr,
+                   nullptr, false, (hipStream_t)stream);
   } catch (...) {
     return PA_ERR_LAUNCH;
   }

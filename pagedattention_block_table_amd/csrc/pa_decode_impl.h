@@ -78,6 +78,8 @@ struct DecodeArgs {
   int nwg;               // balanced mode: workgroups sharing the chunks
   float q_mul;           // scale * log2(e) (* k_scale for fp8)
   float out_mul;         // v_scale for fp8, else 1
+  const int32_t* order;  // ordered mode: sequences by descending context length, else null
+  int order_hpx;         // ordered mode: KV heads per XCD share of the units (0: not whole)
 };
 
 // ---------------------------------------------------------------------------------
@@ -230,6 +232,33 @@ __device__ __forceinline__ int xcd_unit(int i, int n) {
   const int per = n / X;
   const int rem = n % X;
   return xcd * per + min(xcd, rem) + k;
+}
+
+// Sequence s and KV head g of unit index sg (the partition already factored out).
+// Without an order: KV-head major, sequences in index order. With an order (a
+// permutation of the sequences, longest context first): when each XCD's contiguous share
+// of the units is a whole number of KV heads (order_hpx of them), rank major inside the
+// share, so that every XCD starts its longest sequences first; else KV-head major with
+// the sequences taken by rank.
+__device__ __forceinline__ void unit_seq_head(const DecodeArgs& a, int sg, int& s, int& g) {
+  const int S = a.num_seqs;
+  if (a.order == nullptr) {
+    s = sg % S;
+    g = sg / S;
+    return;
+  }
+  int rank;
+  if (a.order_hpx > 0) {
+    const int per = S * a.order_hpx;
+    const int blk = sg / per;
+    const int l = sg - blk * per;
+    rank = l / a.order_hpx;
+    g = blk * a.order_hpx + (l - rank * a.order_hpx);
+  } else {
+    rank = sg % S;
+    g = sg / S;
+  }
+  s = min(max(a.order[rank], 0), S - 1);
 }
 
 // ---------------------------------------------------------------------------------
@@ -453,8 +482,8 @@ decode_kernel(const DecodeArgs a) {
   const int unit = xcd_unit((int)blockIdx.x, (int)gridDim.x);
   const int part = unit % a.num_parts;
   const int sg = unit / a.num_parts;
-  const int s = sg % a.num_seqs;
-  const int g = sg / a.num_seqs;
+  int s, g;
+  unit_seq_head(a, sg, s, g);
 
   int L = a.context_lens[s];
   L = min(max(L, 0), a.max_ctx);

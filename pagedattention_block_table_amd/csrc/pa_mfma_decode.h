@@ -979,8 +979,8 @@ mfma_decode_kernel(const DecodeArgs a) {
   const int unit = xcd_unit((int)blockIdx.x, (int)gridDim.x);
   const int part = unit % a.num_parts;
   const int sg = unit / a.num_parts;
-  const int s = sg % a.num_seqs;
-  const int g = sg / a.num_seqs;
+  int s, g;
+  unit_seq_head(a, sg, s, g);
 
   int L = a.context_lens[s];
   L = min(max(L, 0), a.max_ctx);

@@ -37,12 +37,15 @@ def to_device(b, device="cuda"):
 
 def run(b, dev, mode="direct", partition_size=None, stream=None, num_workgroups=0, workspace=None):
     """HIP decode of a batch; returns the output tensor (io dtype, on the device).
-    mode: "direct" (pa_decode), "partitioned" (partition_size) or "balanced"
-    (num_workgroups, 0 = library default)."""
+    mode: "direct" (pa_decode), "partitioned" (partition_size), "balanced"
+    (num_workgroups, 0 = library default) or "ordered" (pa_decode_ordered)."""
     kw = dict(scale=float(b.scale), k_scale=float(b.k_scale), v_scale=float(b.v_scale), stream=stream)
     if mode == "direct":
         return pa.pa_decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"],
                             dev["context_lens"], **kw)
+    if mode == "ordered":
+        return pa.pa_decode_ordered(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"],
+                                    dev["context_lens"], workspace=workspace, **kw)
     if mode == "balanced":
         return pa.pa_decode_balanced(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"],
                                      dev["context_lens"], num_workgroups=num_workgroups,

@@ -138,6 +138,25 @@ def test_balanced_workspace_checks():
     assert L.pa_decode_balanced(*a, -2, FAKE, need, FAKE, None) == _lib.PA_ERR_INVALID
 
 
+@pytest.mark.parametrize("over,code", BAD, ids=[str(b[0]) for b in BAD])
+def test_ordered_rejects(over, code):
+    # argument errors are reported before anything (the ordering launch included) is enqueued
+    L = _lib.lib()
+    assert L.pa_decode_ordered(*good_args(**over), FAKE, 1 << 20, FAKE, None) == code
+
+
+def test_ordered_workspace_checks():
+    L = _lib.lib()
+    a = good_args()
+    need = _lib.pa_ordered_workspace_bytes(4)
+    assert need == 256
+    assert _lib.pa_ordered_workspace_bytes(100) == 512
+    assert _lib.pa_ordered_workspace_bytes(0) == 0
+    assert L.pa_decode_ordered(*a, FAKE, need - 16, FAKE, None) == _lib.PA_ERR_WORKSPACE
+    assert L.pa_decode_ordered(*a, 0, need, FAKE, None) == _lib.PA_ERR_WORKSPACE
+    assert L.pa_decode_ordered(*a, FAKE + 4, need, FAKE, None) == _lib.PA_ERR_INVALID
+
+
 def test_balanced_workspace_formula():
     # counters: one int32 per (KV head, sequence), padded to 256 bytes; then per workgroup
     # two slots of G maxima, G sums and G x head_dim partial outputs, fp32
