@@ -31,10 +31,10 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 MFMA16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 matrix peak, AMD published
 EXTEND_METRIC = "paged extend (chunked prefill) attention TFLOP/s, causal algorithmic flops"
 METRIC = "paged-attn decode KV GB/s read and % of MI355X HBM peak; seqs·tokens/s"
-DEFAULT_MODE = {0: "direct", 1: "direct", 2: "direct", 3: "balanced", 4: "balanced",
+DEFAULT_MODE = {0: "direct", 1: "direct", 2: "direct", 3: "direct", 4: "ordered",
                 "llama7b_fp16_bs128": "direct", "shared_prefix_bf16_bs256": "direct",
-                "long_ctx_fp16_bs512": "balanced", "mixed_fp8_bs256": "balanced",
-                "llama70b_gqa8_bf16": "direct", "d256_gqa2_bf16": "direct"}
+                "long_ctx_fp16_bs512": "ordered", "mixed_fp8_bs256": "ordered",
+                "llama70b_gqa8_bf16": "ordered", "d256_gqa2_bf16": "direct"}
 KERNEL_SOURCES = ["pagedattention_block_table_amd/csrc/pa_decode_impl.h",
                   "pagedattention_block_table_amd/csrc/pa_mfma_decode.h",
                   "pagedattention_block_table_amd/csrc/pa_api.hip"]
