@@ -244,13 +244,22 @@ __global__ void __launch_bounds__(1024) order_kernel(const int32_t* context_lens
     atomicAdd(&count[length_class(L)], 1);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;  // exclusive prefix sums from the longest class down
-    for (int b = kOrderClasses - 1; b >= 0; --b) {
-      const int n = count[b];
-      count[b] = run;
-      run += n;
+  if (threadIdx.x < 64) {
+    // exclusive prefix sums from the longest class down, one wave: lane l takes the
+    // classes 127 - 2l and 126 - 2l
+    static_assert(kOrderClasses == 128, "two classes per lane of one wave");
+    const int lane = threadIdx.x;
+    const int c0 = count[kOrderClasses - 1 - 2 * lane];
+    const int c1 = count[kOrderClasses - 2 - 2 * lane];
+    int v = c0 + c1;
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) {
+      const int y = __shfl_up(v, k);
+      if (lane >= k) v += y;
     }
+    const int excl = v - c0 - c1;
+    count[kOrderClasses - 1 - 2 * lane] = excl;
+    count[kOrderClasses - 2 - 2 * lane] = excl + c0;
   }
   __syncthreads();
   for (int s = threadIdx.x; s < S; s += blockDim.x) {
