@@ -485,45 +485,28 @@ decode_kernel(const DecodeArgs a) {
   int s, g;
   unit_seq_head(a, sg, s, g);
 
-  constexpr int SB = Geo::SB;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int t_begin = part * a.part_tokens;
-  const int j_begin = t_begin / SB;
-  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-
-  // Block ids of this wave's first step, requested together with the context length
-  // (they do not depend on it; an entry past the sequence's end is read but none of its
-  // rows is loaded), so that the first K/V loads wait for one memory round trip, not two.
-  int bid0[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int jt = min((j_begin + wave * U + u) / Geo::SPB, a.max_blocks_per_seq - 1);
-    bid0[u] = min(max(__builtin_amdgcn_readfirstlane(bt[jt]), 0), a.num_blocks - 1);
-  }
-
   int L = a.context_lens[s];
   L = min(max(L, 0), a.max_ctx);
+  const int t_begin = part * a.part_tokens;
   if (part > 0 && t_begin >= L) return;  // nothing in this partition (whole workgroup)
   const int t_end = min(L, t_begin + a.part_tokens);
+  constexpr int SB = Geo::SB;
+  const int j_begin = t_begin / SB;
   const int j_end = (t_end + SB - 1) / SB;
 
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int r = lane / LPT;
   const int c = lane % LPT;
   const int H = a.num_heads;
 
-  // q of the G heads of this group, this lane's VEC columns (16 bytes per head): loaded
-  // raw here and widened once the first K/V loads are in flight, so that its latency
-  // overlaps theirs instead of preceding them
-  constexpr int QV = 16 / ElemBytes<IO>::value;  // q values per 16-byte piece
-  constexpr int QN = VEC / QV;                   // 16-byte pieces per head and lane
-  uint4 qraw[G][QN];
+  // q of the G heads of this group, this lane's VEC columns, pre-scaled to log2 units
+  float qf[G][VEC];
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) {
     const int64_t base = ((int64_t)s * H + (int64_t)g * G + gi) * D + c * VEC;
 #pragma unroll
-    for (int pc = 0; pc < QN; ++pc)
-      qraw[gi][pc] = *(const uint4*)((const char*)a.q + (base + pc * QV) * ElemBytes<IO>::value);
+    for (int e = 0; e < VEC; ++e) qf[gi][e] = load_io<IO>(a.q, base + e) * a.q_mul;
   }
 
   RowState<G, VEC> st;
@@ -535,6 +518,7 @@ decode_kernel(const DecodeArgs a) {
     for (int e = 0; e < VEC; ++e) st.acc[gi][e] = 0.f;
   }
 
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   const int64_t blk_stride = (int64_t)a.num_kv_heads * Geo::TILE;
   const char* kbase = (const char*)a.k_pool + (int64_t)g * Geo::TILE;
   const char* vbase = (const char*)a.v_pool + (int64_t)g * Geo::TILE;
@@ -548,24 +532,6 @@ decode_kernel(const DecodeArgs a) {
     using Buf = StepBuf<KV, D, BS, G, U>;
     auto j0_of = [&](int k) { return j_begin + (wave + min(k, nwc - 1) * NW) * U; };
     auto consume = [&](const Buf& b, int k) {
-      // q to fp32 in log2 units (scale * log2 e, and k_scale for fp8, folded in), redone
-      // per step (a few conversions) so that nothing waits for q before the first K/V
-      // loads are issued
-      float qf[G][VEC];
-#pragma unroll
-      for (int gi = 0; gi < G; ++gi) {
-#pragma unroll
-        for (int pc = 0; pc < QN; ++pc) {
-          // an empty asm that claims to change the raw q keeps the conversion inside the
-          // loop (else it is hoisted above the first K/V loads, with a wait for q)
-          uint4 qr = qraw[gi][pc];
-          asm volatile("" : "+v"(qr.x), "+v"(qr.y), "+v"(qr.z), "+v"(qr.w));
-          float t[QV];
-          widen16<IO>(qr, t);
-#pragma unroll
-          for (int e = 0; e < QV; ++e) qf[gi][pc * QV + e] = t[e] * a.q_mul;
-        }
-      }
       const int j0 = j0_of(k);
       if ((j0 + U) * SB <= t_end) {
         consume_step<IO, KV, D, BS, G, U, false, DBG>(a, b, j0, t_end, r, c, s, g, qf, st);
@@ -578,12 +544,7 @@ decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int d = 0; d < kVecDepth; ++d) {
       int bid[U];
-      if (d == 0) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) bid[u] = bid0[u];
-      } else {
-        step_blocks<KV, D, BS, G, U>(a, bt, j0_of(d), j_end, bid);
-      }
+      step_blocks<KV, D, BS, G, U>(a, bt, j0_of(d), j_end, bid);
       issue_step<KV, D, BS, G, U>(buf[d], kbase, vbase, blk_stride, bid, j0_of(d), t_end, r, c);
       step_blocks<KV, D, BS, G, U>(a, bt, j0_of(d + kVecDepth), j_end, nid[d]);
     }
