@@ -323,7 +323,7 @@ def _sample_pairs(b, cfg):
 
 FULL = [(0, "direct"), (1, "direct"), (1, "partitioned"), (1, "balanced"), (2, "direct"),
         (2, "partitioned"), (2, "balanced"), (4, "partitioned"), (4, "direct"), (4, "balanced"),
-        (3, "partitioned"), (3, "direct"), (3, "balanced")]
+        (4, "ordered"), (3, "partitioned"), (3, "direct"), (3, "balanced"), (3, "ordered")]
 
 
 @pytest.mark.slow
