@@ -126,10 +126,11 @@ int pa_decode_partitioned(const void* q, const void* k_pool, const void* v_pool,
 size_t pa_balanced_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                                    int num_workgroups);
 
-/* Work-balanced decode. Same result as pa_decode; the schedule differs: the cached tokens
- * of every (KV head, sequence) are cut into 16-token chunks, and a fixed grid of
- * num_workgroups workgroups (0 = library default) takes equal shares of all chunks of the
- * batch, whatever the mix of context lengths. A (KV head, sequence) whose chunks are
+/* Work-balanced decode. Same result as pa_decode up to rounding order; the schedule
+ * differs: the cached tokens of every (KV head, sequence) are cut into chunks of 16 or 32
+ * tokens (by kernel shape), and a fixed grid of num_workgroups workgroups (0 = library
+ * default) takes equal shares of the batch's work (its chunks plus a fixed cost for each
+ * sequence piece a workgroup handles), whatever the mix of context lengths. A (KV head, sequence) whose chunks are
  * shared by several workgroups is finished by the last of them to arrive, which merges
  * the others' partial states by log-sum-exp weighting (the rule of the split-context
  * kernel, [P2] §3.3 / §4.1). Everything happens in one kernel launch.
