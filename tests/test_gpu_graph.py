@@ -65,3 +65,41 @@ def test_graph_replays_match_eager():
         step(torch.cuda.current_stream())
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), r
+
+
+def test_graph_replays_ordered_decode():
+    """The longest-first decode (ordering launch + decode launch) under graph capture, on
+    a mixed-length fp8 batch: every replay, with eager work in between, is bit-identical
+    to the eager call (the ordering kernel clears its counters itself, in LDS)."""
+    import torch
+    b = W.make_batch(W.small_variant(4))
+    dev = to_device(b)
+    kw = dict(scale=float(b.scale), k_scale=float(b.k_scale), v_scale=float(b.v_scale))
+    ws = pa.ordered_workspace(dev["q"])
+    out = torch.empty_like(dev["q"])
+
+    def step(stream):
+        pa.pa_decode_ordered(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"], dev["context_lens"],
+                             workspace=ws, out=out, stream=stream, **kw)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(torch.cuda.current_stream())
+    for r in range(4):
+        out.zero_()
+        ws.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        log(f"[graph-ordered] replay {r}")
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), r
+        step(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), r
