@@ -76,36 +76,36 @@ template <> struct Mma<kF16> {
   static __device__ __forceinline__ f32x4_t mma(const vec& a, const vec& b, const f32x4_t& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
-  // two fp32 values that are exactly representable -> packed pair (exact)
-  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-  }
 };
 template <> struct Mma<kBF16> {
   typedef bf16x8_t vec;
   static __device__ __forceinline__ f32x4_t mma(const vec& a, const vec& b, const f32x4_t& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
-  // fp32 values with at most 8 significant bits: the upper halves are the bf16 codes
-  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo),
-                                 0x07060302u);
-  }
 };
 
 // Eight e4m3 codes (two dwords) -> eight MFMA operands of type MT, exactly: every e4m3
-// value has at most 4 significant bits and fits both f16 and bf16.
+// value has at most 4 significant bits and an exponent inside the f16 and bf16 ranges.
+// gfx950 converts a pair of codes straight to f16 or bf16 (v_cvt_scalef32_pk_*_fp8 with a
+// scale of 1.0, which is exact); word_sel picks bytes {0,1} or {2,3} of the dword, the
+// lower code going to the lower half.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+template <int MT, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_mt(uint32_t w) {
+  if constexpr (MT == kBF16) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+  }
+}
+
 template <int MT>
 __device__ __forceinline__ typename Mma<MT>::vec fp8x8_operand(uint32_t w0, uint32_t w1) {
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
-  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
-  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
   uint4 r;
-  r.x = Mma<MT>::pack2(a.x, a.y);
-  r.y = Mma<MT>::pack2(b.x, b.y);
-  r.z = Mma<MT>::pack2(c.x, c.y);
-  r.w = Mma<MT>::pack2(d.x, d.y);
+  r.x = fp8x2_to_mt<MT, false>(w0);
+  r.y = fp8x2_to_mt<MT, true>(w0);
+  r.z = fp8x2_to_mt<MT, false>(w1);
+  r.w = fp8x2_to_mt<MT, true>(w1);
   return __builtin_bit_cast(typename Mma<MT>::vec, r);
 }
 
@@ -774,10 +774,8 @@ struct MfmaPvEngine {
         uint32_t packed[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], false);
-          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], true);
-          packed[2 * q] = Mma<IO>::pack2(lo.x, lo.y);
-          packed[2 * q + 1] = Mma<IO>::pack2(hi.x, hi.y);
+          packed[2 * q] = fp8x2_to_mt<IO, false>(w[q]);
+          packed[2 * q + 1] = fp8x2_to_mt<IO, true>(w[q]);
         }
         *(uint4*)(vt + t * VT_ROW + col) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
         *(uint4*)(vt + t * VT_ROW + col + 8) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
