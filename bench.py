@@ -1,17 +1,27 @@
 #!/usr/bin/env python3
 """Benchmark of the paged-attention decode step on one MI355X.
 
-One step = one decode call (all kernels of the path) over the whole synthetic batch of
-the chosen workload. Inputs are resident in HBM before timing starts. So that every
-step reads its K/V from HBM and not from the 256 MB Infinity Cache or the L2s, the
-benchmark keeps R identical replicas of the K and V pools (R x pool >= 2 GiB) and step i
-reads replica i mod R, as a decode over many layers does.
+One step = one pass of the whole decode path (block-table gather, scores, online
+softmax, V product, and for the split-context mode the log-sum-exp merge kernel) over
+the whole synthetic batch. Inputs are resident in HBM before timing starts. So that
+every step reads its K/V from HBM and not from the 256 MB Infinity Cache or the L2s,
+the benchmark keeps R identical replicas of the K and V pools (R x pool >= 2 GiB) and
+step i reads replica i mod R, as a decode over many layers does.
 
-Prints ONE JSON line: KV GB/s (unique K/V bytes per step / time per step), % of the
-8 TB/s HBM peak, seq*tokens/s, the roofline of the decode kernel (its duration from
-HIP events on the launch stream) and the fp64 CPU oracle timed on a bounded sample.
+The headline line is the largest single-GPU batch: 8 sequences x 32768 tokens (fp16,
+32 heads, head_dim 128, 32-token blocks, ~4.3 GB of K/V), split into 512-token
+partitions whose states are merged by log-sum-exp (the pages' second, split-context
+kernel for long text). Beside it: the same batch in single-pass mode, the other three
+measured batches (LLaMA-7B serving shape, shared 500-token prefix, 50/30/20 % length mix
+with fp8 KV) in their default modes, the device's plain streaming-read rate for the same
+load shape, and the fp64 CPU oracle on a bounded sample (one thread and all host cores).
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--mode auto]
+Prints ONE JSON line. `value` = unique K/V bytes per step / wall time per step.
+`roofline.achieved` = compulsory bytes per step (unique K/V, q, out, used table entries,
+lengths) / GPU time per step, where the GPU time is measured by two HIP events recorded
+on the launch stream around the timed steps (divided by their count).
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--mode auto]
 """
 from __future__ import annotations
 
@@ -31,13 +41,17 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 MFMA16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 matrix peak, AMD published
 EXTEND_METRIC = "paged extend (chunked prefill) attention TFLOP/s, causal algorithmic flops"
 METRIC = "paged-attn decode KV GB/s read and % of MI355X HBM peak; seqs·tokens/s"
-DEFAULT_MODE = {0: "direct", 1: "direct", 2: "direct", 3: "direct", 4: "ordered",
+HEADLINE_CONFIG = 3
+DEFAULT_MODE = {0: "direct", 1: "direct", 2: "direct", 3: "partitioned", 4: "ordered",
                 "llama7b_fp16_bs128": "direct", "shared_prefix_bf16_bs256": "direct",
                 "long_ctx_fp16_bs512": "ordered", "mixed_fp8_bs256": "ordered",
                 "llama70b_gqa8_bf16": "ordered", "d256_gqa2_bf16": "direct"}
+SUB_CONFIGS = (1, 2, 4)
 KERNEL_SOURCES = ["pagedattention_block_table_amd/csrc/pa_decode_impl.h",
                   "pagedattention_block_table_amd/csrc/pa_mfma_decode.h",
                   "pagedattention_block_table_amd/csrc/pa_api.hip"]
+KV_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
+IO_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 
 
 def log(msg):
@@ -53,7 +67,7 @@ def source_hash() -> str:
 
 
 def read_traffic(workload: str, mode: str):
-    """HBM bytes per launch measured by rocprofv3 counters, if recorded for this exact
+    """HBM bytes per step measured by rocprofv3 counters, if recorded for this exact
     kernel source (profiles/traffic_<workload>_<mode>.md), else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{mode}.md")
     if not os.path.exists(path):
@@ -67,48 +81,301 @@ def read_traffic(workload: str, mode: str):
 
 
 def compulsory_bytes(b, kv_unique: int) -> int:
-    """Bytes every launch must move at least: unique K/V, q, out, used table entries, lengths."""
+    """Bytes every step must move at least: unique K/V, q, out, used table entries, lengths."""
     sp = b.spec
-    io = {"f32": 4, "f16": 2, "bf16": 2}[sp.io_dtype]
     nblk = sum((int(L) + sp.block_size - 1) // sp.block_size for L in b.context_lens)
-    return kv_unique + 2 * b.q.size * io + 4 * nblk + 4 * b.num_seqs
+    return kv_unique + 2 * b.q.size * IO_BYTES[sp.io_dtype] + 4 * nblk + 4 * b.num_seqs
 
 
-def cpu_baseline(b, seconds: float):
-    """Time the fp64 oracle (as it stands) on whole (sequence, KV head) units of the same
-    batch, cycling over the batch in a fixed interleaved order until `seconds` of work;
-    report KV GB/s."""
+# ----------------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle as it stands, on whole (sequence, KV head) units
+# ----------------------------------------------------------------------------------
+
+_CPU_BATCH = None  # the batch the forked oracle workers read (inherited, never copied)
+
+
+def _unit_order(b):
+    sp = b.spec
+    units = [(s, g) for g in range(sp.num_kv_heads) for s in range(sp.num_seqs)]
+    n = len(units)
+    # interleave so that a short sample still spans sequences and heads
+    return [units[(i * 7919) % n] for i in range(n)] if n % 7919 else units
+
+
+def _oracle_units(args):
+    """Worker body: oracle units wid, wid + nw, ... of the interleaved order until
+    `seconds` have passed; returns (K/V bytes, tokens, units, seconds)."""
+    wid, nw, seconds = args
     from threadpoolctl import threadpool_limits
 
     import oracle
 
+    b = _CPU_BATCH
     sp = b.spec
     G = sp.num_heads // sp.num_kv_heads
-    e = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}[sp.kv_dtype]
-    units = [(s, g) for g in range(sp.num_kv_heads) for s in range(sp.num_seqs)]
-    # interleave so that a short sample still spans sequences and heads
-    n = len(units)
-    order = [units[(i * 7919) % n] for i in range(n)] if n % 7919 else units
-    done = 0
-    nbytes = 0
-    tokens = 0
+    e = KV_BYTES[sp.kv_dtype]
+    order = _unit_order(b)
+    n = len(order)
+    done = nbytes = tokens = 0
+    i = wid
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         while True:
-            s, g = order[done % n]
-            oracle.decode_batch(b, pairs=[(s, g * G + i) for i in range(G)])
+            s, g = order[i % n]
+            oracle.decode_batch(b, pairs=[(s, g * G + j) for j in range(G)])
             L = int(b.context_lens[s])
             nbytes += 2 * L * sp.head_dim * e
             tokens += L
             done += 1
-            if time.perf_counter() - t0 >= seconds:
+            i += nw
+            dt = time.perf_counter() - t0
+            if dt >= seconds:
                 break
-        dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} (sequence, KV head) units of {sp.name} ({n} per batch, cycled), all "
-                      f"{G} query heads each, fp64 numpy oracle on 1 thread, {dt:.1f} s",
-            "seq_tokens_per_s": round(tokens / dt, 3)}
+    return nbytes, tokens, done, dt
 
+
+def cpu_baseline(b, seconds: float):
+    """The fp64 oracle on whole (sequence, KV head) units of the same batch, cycling over
+    the batch until `seconds` of work: once on one thread, once on all host cores the
+    process may use (at most 16; forked worker processes, one oracle unit at a time each).
+    Runs before the GPU is initialised, so the fork is safe."""
+    import multiprocessing as mp
+
+    global _CPU_BATCH
+    _CPU_BATCH = b
+    sp = b.spec
+    G = sp.num_heads // sp.num_kv_heads
+    n_units = sp.num_seqs * sp.num_kv_heads
+    one = _oracle_units((0, 1, seconds))
+    affinity = len(os.sched_getaffinity(0))
+    nw = max(1, min(16, affinity))
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(nw) as pool:
+        parts = pool.map(_oracle_units, [(w, nw, seconds) for w in range(nw)])
+    wall = time.perf_counter() - t0
+    dt = max(p[3] for p in parts)
+    nbytes = sum(p[0] for p in parts)
+    tokens = sum(p[1] for p in parts)
+    units = sum(p[2] for p in parts)
+    _CPU_BATCH = None
+    return {"value": round(nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": nw, "kind": "oracle",
+            "sample": f"{units} (sequence, KV head) units of {sp.name} ({n_units} per batch, cycled in an "
+                      f"interleaved order), all {G} query heads each, fp64 numpy oracle, {nw} worker "
+                      f"processes with one BLAS thread each, {dt:.1f} s (pool wall {wall:.1f} s)",
+            "seq_tokens_per_s": round(tokens / dt, 3),
+            "single_thread": {"value": round(one[0] / one[3] / 1e9, 6), "unit": "GB/s", "cores": 1,
+                              "sample": f"{one[2]} units, {one[3]:.1f} s",
+                              "seq_tokens_per_s": round(one[1] / one[3], 3)},
+            "host_cpus": os.cpu_count(), "affinity_cpus": affinity}
+
+
+# ----------------------------------------------------------------------------------
+# GPU timing
+# ----------------------------------------------------------------------------------
+
+def dev_t(torch, x, dt):
+    import numpy as np
+    if dt == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+class DeviceBatch:
+    """One workload on the device: q, tables, lengths, out, and R replicas of the pools."""
+
+    def __init__(self, torch, b, replica_bytes: float):
+        import oracle
+        sp = b.spec
+        self.b = b
+        self.q = dev_t(torch, b.q, sp.io_dtype)
+        self.bt = torch.from_numpy(b.block_tables).cuda()
+        self.cl = torch.from_numpy(b.context_lens).cuda()
+        k0 = dev_t(torch, b.k_pool, sp.kv_dtype)
+        v0 = dev_t(torch, b.v_pool, sp.kv_dtype)
+        pool_bytes = k0.numel() * k0.element_size() * 2
+        self.R = max(2, int(math.ceil(replica_bytes / pool_bytes)))
+        self.ks = [k0] + [k0.clone() for _ in range(self.R - 1)]
+        self.vs = [v0] + [v0.clone() for _ in range(self.R - 1)]
+        self.pool_bytes = pool_bytes
+        self.out = torch.empty_like(self.q)
+        self.kv_unique = oracle.kv_unique_bytes(b.block_tables, b.context_lens, sp.block_size,
+                                                sp.num_kv_heads, sp.head_dim, KV_BYTES[sp.kv_dtype])
+        self.kv_logical = int(b.context_lens.sum()) * sp.num_kv_heads * sp.head_dim * KV_BYTES[sp.kv_dtype] * 2
+        self.algo = compulsory_bytes(b, self.kv_unique)
+
+    def plan(self, pa, mode, P, workgroups, stream, workspace=None):
+        b = self.b
+        kw = dict(scale=float(b.scale), k_scale=float(b.k_scale), v_scale=float(b.v_scale),
+                  out=self.out, stream=stream, workspace=workspace)
+        if mode == "direct":
+            kw.pop("workspace")
+            return pa.DecodePlan(self.q, self.ks[0], self.vs[0], self.bt, self.cl, **kw)
+        if mode == "balanced":
+            return pa.DecodePlan(self.q, self.ks[0], self.vs[0], self.bt, self.cl, balanced=True,
+                                 num_workgroups=workgroups, **kw)
+        if mode == "ordered":
+            return pa.DecodePlan(self.q, self.ks[0], self.vs[0], self.bt, self.cl, ordered=True, **kw)
+        return pa.DecodePlan(self.q, self.ks[0], self.vs[0], self.bt, self.cl,
+                             max_context_len=max(b.max_context_len, 1), partition_size=P, **kw)
+
+    def release(self):
+        del self.ks, self.vs
+
+
+def time_steps(torch, step, warmup: int, K: int, stream):
+    """Warm up, then time K steps back to back: wall time between synchronizations, and
+    GPU time from two HIP events recorded on the launch stream around the K steps.
+    Returns (wall ms per step, GPU ms per step)."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(K):
+        step(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / K
+    return wall, e0.elapsed_time(e1) / K
+
+
+def measure_decode(torch, pa, db: DeviceBatch, mode: str, P: int, steps: int, warmup: int,
+                   workgroups: int = 0, graph: bool = False):
+    """Time one decode mode on a device batch; returns a result dict."""
+    b = db.b
+    sp = b.spec
+    stream = torch.cuda.current_stream()
+    plan = db.plan(pa, mode, P, workgroups, stream)
+    calls = [plan.bound(db.ks[r], db.vs[r]) for r in range(db.R)]
+
+    def step(i):
+        rc = calls[i % db.R]()
+        if rc != 0:
+            raise pa.PagedAttentionError("decode", rc)
+
+    wall_ms, gpu_ms = time_steps(torch, step, warmup, steps, stream)
+    sum_l = int(b.context_lens.sum())
+    r = {"workload": sp.name, "mode": mode,
+         "partition_size": P if mode == "partitioned" else None,
+         "us_per_step": round(wall_ms * 1e3, 3), "gpu_us_per_step": round(gpu_ms * 1e3, 3),
+         "kv_unique_bytes": db.kv_unique, "algorithmic_bytes": db.algo,
+         "GB_per_s": round(db.kv_unique / (wall_ms * 1e-3) / 1e9, 2),
+         "pct_of_hbm_peak": round(100.0 * db.kv_unique / (wall_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+         "roofline_frac": round(db.algo / (gpu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+         "seq_tokens_per_s": round(sum_l / (wall_ms * 1e-3), 1),
+         "traffic": read_traffic(sp.name, mode)}
+    if graph:
+        r["graph_replay"] = graph_replay(torch, pa, db, mode, P, workgroups, steps)
+    return r
+
+
+def graph_replay(torch, pa, db: DeviceBatch, mode, P, workgroups, steps):
+    """The same steps captured once into a HIP graph (R launches, one per replica) and
+    replayed: what a caller that captures its decode loop sees. Workspaces are made before
+    the capture, so the graph holds the decode kernels only."""
+    b = db.b
+    try:
+        ws = None
+        if mode == "balanced":
+            ws = pa.balanced_workspace(db.q, db.ks[0], workgroups)
+        elif mode == "ordered":
+            ws = pa.ordered_workspace(db.q)
+        elif mode == "partitioned":
+            sp = b.spec
+            need = pa.pa_partitioned_workspace_bytes(sp.num_seqs, sp.num_heads, sp.head_dim,
+                                                     max(b.max_context_len, 1), P)
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            gplan = db.plan(pa, mode, P, workgroups, torch.cuda.current_stream(), workspace=ws)
+            for r in range(db.R):
+                gplan(db.ks[r], db.vs[r])
+        reps = max(1, steps // db.R)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / (reps * db.R)
+        del g
+        return {"us_per_step": round(ms * 1e3, 3), "GB_per_s": round(db.kv_unique / (ms * 1e-3) / 1e9, 2)}
+    except Exception as exc:  # graph capture unavailable: report the eager numbers only
+        log(f"[bench] graph replay skipped: {exc}")
+        return None
+
+
+def measure_append(torch, pa, db: DeviceBatch, steps: int):
+    """The write that precedes each decode step: one new token's K/V per sequence, stored
+    (quantised for fp8) into its block, timed on its own. The rows go to the slot of each
+    sequence's last cached token, so the pool keeps its shape."""
+    b = db.b
+    sp = b.spec
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[sp.io_dtype]
+    kn = torch.randn((sp.num_seqs, sp.num_kv_heads, sp.head_dim), generator=gen, device="cuda").to(tdt)
+    vn = torch.randn((sp.num_seqs, sp.num_kv_heads, sp.head_dim), generator=gen, device="cuda").to(tdt)
+    sid = torch.arange(sp.num_seqs, dtype=torch.int32, device="cuda")
+    pos = torch.clamp(db.cl - 1, min=0)
+    k0, v0 = db.ks[0], db.vs[0]
+
+    def step(i):
+        pa.pa_append_kv(kn, vn, sid, pos, db.bt, k0, v0, k_scale=float(b.k_scale), v_scale=float(b.v_scale),
+                        stream=stream)
+
+    _, gpu_ms = time_steps(torch, step, 3, steps, stream)
+    nbytes = sp.num_seqs * (sp.num_kv_heads * sp.head_dim * 2 * (IO_BYTES[sp.io_dtype] + KV_BYTES[sp.kv_dtype]) + 12)
+    return {"us_per_launch": round(gpu_ms * 1e3, 3), "bytes_per_launch": nbytes,
+            "GB_per_s": round(nbytes / (gpu_ms * 1e-3) / 1e9, 2)}
+
+
+def stream_read_ceiling(torch, pa, sizes, replica_bytes: float, steps: int):
+    """Plain streaming read (pa_debug_stream_read: 16-byte loads, 1 KiB per wave
+    instruction, nothing else) of buffers of the given sizes, cold like the decode steps
+    (replicas cycled, >= 2 GiB in all). Every (loads per thread, grid) pair of a small sweep
+    is timed with events over `steps` launches; the best is the ceiling for that size."""
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    out = {}
+    for label, nbytes in sizes:
+        run_b = 16 * 16 * 256  # multiple of every unroll's run
+        nbytes = nbytes // run_b * run_b
+        R = max(2, int(math.ceil(replica_bytes / nbytes)))
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+        for t in bufs:
+            t.fill_(1)
+        best = None
+        sweep = []
+        for unroll in (4, 8, 16):
+            for wgs in (0, 2048, 4096, 8192):
+                def step(i, unroll=unroll, wgs=wgs):
+                    rc = pa._lib.lib().pa_debug_stream_read(bufs[i % R].data_ptr(), nbytes, unroll, wgs,
+                                                            sink.data_ptr(), stream.cuda_stream)
+                    if rc != 0:
+                        raise pa.PagedAttentionError("pa_debug_stream_read", rc)
+                _, gpu_ms = time_steps(torch, step, 3, steps, stream)
+                gbs = nbytes / (gpu_ms * 1e-3) / 1e9
+                sweep.append((unroll, wgs, round(gpu_ms * 1e3, 2), round(gbs, 1)))
+                if best is None or gbs > best[3]:
+                    best = (unroll, wgs, gpu_ms, gbs)
+        out[label] = {"bytes": nbytes, "GB_per_s": round(best[3], 1),
+                      "pct_of_hbm_peak": round(100 * best[3] / HBM_PEAK_GBS, 2),
+                      "us": round(best[2] * 1e3, 2), "unroll": best[0], "workgroups": best[1] or "one pass",
+                      "sweep_unroll_wgs_us_GBps": sweep}
+        log(f"[bench] stream read {label}: best {best[3]:.0f} GB/s ({best[2] * 1e3:.1f} us, unroll {best[0]}, "
+            f"wgs {best[1] or 'one pass'})")
+        del bufs
+    return out
+
+
+# ----------------------------------------------------------------------------------
+# extend
+# ----------------------------------------------------------------------------------
 
 def extend_flops(e) -> int:
     """4 * D flops per (query row, head, key it attends to): 2D for q.k, 2D for p*v."""
@@ -118,14 +385,13 @@ def extend_flops(e) -> int:
         L = int(e.base.context_lens[s])
         Q = int(e.query_start_loc[s + 1] - e.query_start_loc[s])
         # new token i attends to L - Q + i + 1 keys
-        keys = sum(max(0, L - Q + i + 1) for i in range(Q))
-        total += keys
+        total += sum(max(0, L - Q + i + 1) for i in range(Q))
     return 4 * sp.head_dim * sp.num_heads * total
 
 
 def extend_cpu_baseline(e, seconds: float):
     """The fp64 extend oracle (as it stands) on whole (sequence, KV head) units, cycled
-    until `seconds` of work; reported in TFLOP/s of the same flop count."""
+    until `seconds` of work, one thread; reported in TFLOP/s of the same flop count."""
     from threadpoolctl import threadpool_limits
 
     from oracle import extend as ext_oracle
@@ -160,38 +426,37 @@ def extend_cpu_baseline(e, seconds: float):
 
 def bench_extend(args, name):
     """One step = one pa_extend call over the whole chunked-prefill batch."""
-    import numpy as np
-    import torch
-
-    import oracle
-    import pagedattention_block_table_amd as pa
     from pagedattention_block_table_amd import workloads as W
 
     spec, ql = W.EXTEND[name]
     t0 = time.time()
     e = W.make_extend_batch(spec, ql)
+    cpu = None if args.no_cpu_baseline else extend_cpu_baseline(e, args.cpu_seconds)
+
+    import torch
+
+    import oracle
+    import pagedattention_block_table_amd as pa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(3)
+    pa._lib.lib()  # fail loudly if the HIP library is missing
     b = e.base
     sp = b.spec
     flops = extend_flops(e)
-    kv_e = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}[sp.kv_dtype]
     kv_unique = oracle.kv_unique_bytes(b.block_tables, b.context_lens, sp.block_size, sp.num_kv_heads,
-                                       sp.head_dim, kv_e)
+                                       sp.head_dim, KV_BYTES[sp.kv_dtype])
     log(f"[bench] extend workload {sp.name}: S={sp.num_seqs} H={sp.num_heads} Hkv={sp.num_kv_heads} "
         f"D={sp.head_dim} BS={sp.block_size} kv={sp.kv_dtype} T={e.num_tokens} "
         f"sumL={int(b.context_lens.sum())} flops={flops / 1e9:.1f} G (generated in {time.time() - t0:.1f}s)")
-
-    def dev_t(x, dt):
-        if dt == "bf16":
-            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
-
-    q = dev_t(e.q, sp.io_dtype)
+    q = dev_t(torch, e.q, sp.io_dtype)
     out = torch.empty_like(q)
     bt = torch.from_numpy(b.block_tables).cuda()
     cl = torch.from_numpy(b.context_lens).cuda()
     qsl = torch.from_numpy(e.query_start_loc).cuda()
-    k0 = dev_t(b.k_pool, sp.kv_dtype)
-    v0 = dev_t(b.v_pool, sp.kv_dtype)
+    k0 = dev_t(torch, b.k_pool, sp.kv_dtype)
+    v0 = dev_t(torch, b.v_pool, sp.kv_dtype)
     pool_bytes = k0.numel() * k0.element_size() * 2
     R = max(2, int(math.ceil(args.replica_bytes / pool_bytes)))
     ks = [k0] + [k0.clone() for _ in range(R - 1)]
@@ -203,31 +468,13 @@ def bench_extend(args, name):
         pa.pa_extend(q, ks[i % R], vs[i % R], bt, cl, qsl, mq, scale=float(b.scale), k_scale=float(b.k_scale),
                      v_scale=float(b.v_scale), out=out, stream=stream)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
     K = args.steps
-    t_wall = time.perf_counter()
-    for i in range(K):
-        step(args.warmup + i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    ms_per_step = wall * 1e3 / K
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    torch.cuda.synchronize()
-    for i in range(K):
-        starts[i].record(stream)
-        step(args.warmup + K + i)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    durs_ms = [s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)]
-    kern_ms = float(np.mean(durs_ms))
-    value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (kern_ms * 1e-3) / 1e12
+    wall_ms, gpu_ms = time_steps(torch, step, args.warmup, K, stream)
+    value = flops / (wall_ms * 1e-3) / 1e12
+    achieved = flops / (gpu_ms * 1e-3) / 1e12
     res = {
         "metric": EXTEND_METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": round(wall_ms, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": sp.io_dtype, "data": "synthetic",
         "config": {"workload": sp.name, "num_seqs": sp.num_seqs, "num_heads": sp.num_heads,
                    "num_kv_heads": sp.num_kv_heads, "head_dim": sp.head_dim, "block_size": sp.block_size,
@@ -235,29 +482,29 @@ def bench_extend(args, name):
                    "new_tokens": e.num_tokens, "max_query_len": mq,
                    "sum_context_len": int(b.context_lens.sum()), "kv_unique_bytes": kv_unique,
                    "kv_replicas": R},
-        "kv_GB_per_s": round(kv_unique / (ms_per_step * 1e-3) / 1e9, 2),
-        "new_tokens_per_s": round(e.num_tokens / (ms_per_step * 1e-3), 1),
+        "kv_GB_per_s": round(kv_unique / (wall_ms * 1e-3) / 1e9, 2),
+        "new_tokens_per_s": round(e.num_tokens / (wall_ms * 1e-3), 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel_ms": round(kern_ms, 6), "algorithmic_flops_per_launch": flops,
-                     "p10_p90_ms": [round(float(np.percentile(durs_ms, 10)), 6),
-                                    round(float(np.percentile(durs_ms, 90)), 6)]},
-        "cpu_baseline": None,
+                     "kernel_ms": round(gpu_ms, 6), "algorithmic_flops_per_launch": flops},
+        "cpu_baseline": cpu,
     }
-    log(f"[bench] {ms_per_step * 1e3:.2f} us/step wall, {kern_ms * 1e3:.2f} us/launch (events): "
+    log(f"[bench] {wall_ms * 1e3:.2f} us/step wall, {gpu_ms * 1e3:.2f} us/step GPU (events): "
         f"{value:.1f} TFLOP/s, {res['kv_GB_per_s']:.0f} GB/s unique KV, mfma frac {achieved / MFMA16_PEAK_TFLOPS:.3f}")
     del ks, vs
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = extend_cpu_baseline(e, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
+
+# ----------------------------------------------------------------------------------
+# main
+# ----------------------------------------------------------------------------------
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--config", type=int, default=HEADLINE_CONFIG)
     ap.add_argument("--workload", default="",
                     help="a named variant of a config (larger blocks) or an extend workload "
                          "(extend_*), instead of --config")
@@ -268,6 +515,9 @@ def main():
     ap.add_argument("--replica-bytes", type=float, default=2 * 2**30)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="headline workload only: skip the other batches, the single-pass mode of the "
+                         "headline batch and the streaming-read ceiling")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for rocprofv3)")
     args = ap.parse_args()
@@ -277,16 +527,8 @@ def main():
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
-    import torch
-
-    import pagedattention_block_table_amd as pa
     from pagedattention_block_table_amd import workloads as W
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(3)
-    pa._lib.lib()  # fail loudly if the HIP library is missing
     if args.workload in W.EXTEND:
         bench_extend(args, args.workload)
         return
@@ -299,57 +541,26 @@ def main():
     log(f"[bench] workload {sp.name}: S={sp.num_seqs} H={sp.num_heads} Hkv={sp.num_kv_heads} "
         f"D={sp.head_dim} BS={sp.block_size} kv={sp.kv_dtype} sumL={int(b.context_lens.sum())} "
         f"(generated in {time.time() - t0:.1f}s)")
+    # the oracle runs first, before anything initialises the GPU (its workers are forked)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(b, args.cpu_seconds)
+        log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s on {cpu['cores']} cores, "
+            f"{cpu['single_thread']['value']:.3f} GB/s on one")
 
-    import oracle
-    e = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}[sp.kv_dtype]
-    kv_unique = oracle.kv_unique_bytes(b.block_tables, b.context_lens, sp.block_size,
-                                       sp.num_kv_heads, sp.head_dim, e)
-    kv_logical = int(b.context_lens.sum()) * sp.num_kv_heads * sp.head_dim * e * 2
-    algo_bytes = compulsory_bytes(b, kv_unique)
+    import torch
 
-    def dev_t(x, dt):
-        if dt == "bf16":
-            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    import pagedattention_block_table_amd as pa
 
-    q = dev_t(b.q, sp.io_dtype)
-    bt = torch.from_numpy(b.block_tables).cuda()
-    cl = torch.from_numpy(b.context_lens).cuda()
-    k0 = dev_t(b.k_pool, sp.kv_dtype)
-    v0 = dev_t(b.v_pool, sp.kv_dtype)
-    pool_bytes = k0.numel() * k0.element_size() * 2
-    R = max(2, int(math.ceil(args.replica_bytes / pool_bytes)))
-    ks = [k0] + [k0.clone() for _ in range(R - 1)]
-    vs = [v0] + [v0.clone() for _ in range(R - 1)]
-    out = torch.empty_like(q)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(3)
+    pa._lib.lib()  # fail loudly if the HIP library is missing
+
     P = args.partition_size or sp.partition_size or 512
-    maxL = max(b.max_context_len, 1)
-    ws = None
-    if mode == "partitioned":
-        need = pa.pa_partitioned_workspace_bytes(sp.num_seqs, sp.num_heads, sp.head_dim, maxL, P)
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
-    log(f"[bench] mode={mode} P={P if mode == 'partitioned' else '-'} replicas={R} "
-        f"(pool {pool_bytes / 1e6:.1f} MB each), KV unique {kv_unique / 1e6:.2f} MB")
-
-    kw = dict(scale=float(b.scale), k_scale=float(b.k_scale), v_scale=float(b.v_scale),
-              out=out, stream=stream)
-    if mode == "direct":
-        plan = pa.DecodePlan(q, k0, v0, bt, cl, **kw)
-    elif mode == "balanced":
-        plan = pa.DecodePlan(q, k0, v0, bt, cl, balanced=True, num_workgroups=args.workgroups, **kw)
-    elif mode == "ordered":
-        plan = pa.DecodePlan(q, k0, v0, bt, cl, ordered=True, **kw)
-    else:
-        plan = pa.DecodePlan(q, k0, v0, bt, cl, max_context_len=maxL, partition_size=P,
-                             workspace=ws, **kw)
-
-    calls = [plan.bound(ks[r], vs[r]) for r in range(R)]
-
-    def step(i):
-        rc = calls[i % R]()
-        if rc != 0:
-            raise pa.PagedAttentionError("decode", rc)
+    db = DeviceBatch(torch, b, args.replica_bytes)
+    log(f"[bench] mode={mode} P={P if mode == 'partitioned' else '-'} replicas={db.R} "
+        f"(pool {db.pool_bytes / 1e6:.1f} MB each), KV unique {db.kv_unique / 1e6:.2f} MB")
 
     if args.calibrate_copy:
         src = torch.empty(2**30, dtype=torch.uint8, device="cuda")
@@ -359,105 +570,57 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    head = measure_decode(torch, pa, db, mode, P, args.steps, args.warmup, args.workgroups, graph=True)
+    log(f"[bench] {sp.name} {mode}: {head['us_per_step']:.2f} us/step wall, {head['gpu_us_per_step']:.2f} us/step "
+        f"GPU: {head['GB_per_s']:.1f} GB/s KV, roofline frac {head['roofline_frac']:.4f}")
+    app = measure_append(torch, pa, db, args.steps) if sp.io_dtype in IO_BYTES else None
 
-    K = args.steps
-    # timed region: K steps back to back, bracketed by synchronizations (the throughput)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    for i in range(K):
-        step(args.warmup + i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    ms_per_step = wall * 1e3 / K
-    # kernel duration: the same K steps again, each bracketed by HIP events on the launch
-    # stream (recording events costs host time, so this pass is kept out of the throughput)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    torch.cuda.synchronize()
-    for i in range(K):
-        starts[i].record(stream)
-        step(args.warmup + K + i)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    durs_ms = [s.elapsed_time(e_) for s, e_ in zip(starts, ends)]
-    kern_ms = float(np.mean(durs_ms))
+    alt = {}
+    subs = {}
+    ceiling = None
+    if not args.no_sub:
+        for m in ("direct", "partitioned"):
+            if m != mode:
+                r = measure_decode(torch, pa, db, m, P, args.steps, args.warmup)
+                alt[m] = {k: r[k] for k in ("mode", "partition_size", "us_per_step", "gpu_us_per_step",
+                                            "GB_per_s", "pct_of_hbm_peak", "roofline_frac", "traffic")}
+                log(f"[bench] {sp.name} {m}: {r['us_per_step']:.2f} us/step, frac {r['roofline_frac']:.4f}")
+    replicas = db.R
+    db.release()
+    del db
+    torch.cuda.empty_cache()
 
-    # the same steps replayed from one HIP graph (R captured launches, one per replica):
-    # what a caller that captures its decode loop gets, without per-launch host work.
-    # Workspaces are made before the capture, so the graph holds the decode kernels only.
-    graph_ms = None
-    try:
-        gws = (pa.balanced_workspace(q, k0, args.workgroups) if mode == "balanced"
-               else pa.ordered_workspace(q) if mode == "ordered" else ws)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            gkw = dict(kw, stream=torch.cuda.current_stream())
-            if mode == "direct":
-                gplan = pa.DecodePlan(q, k0, v0, bt, cl, **gkw)
-            elif mode == "balanced":
-                gplan = pa.DecodePlan(q, k0, v0, bt, cl, balanced=True, num_workgroups=args.workgroups,
-                                      workspace=gws, **gkw)
-            elif mode == "ordered":
-                gplan = pa.DecodePlan(q, k0, v0, bt, cl, ordered=True, workspace=gws, **gkw)
-            else:
-                gplan = pa.DecodePlan(q, k0, v0, bt, cl, max_context_len=maxL, partition_size=P,
-                                      workspace=gws, **gkw)
-            for r in range(R):
-                gplan(ks[r], vs[r])
-        reps = max(1, K // R)
-        graph.replay()
-        torch.cuda.synchronize()
-        t_g = time.perf_counter()
-        for _ in range(reps):
-            graph.replay()
-        torch.cuda.synchronize()
-        graph_ms = (time.perf_counter() - t_g) * 1e3 / (reps * R)
-        del graph
-    except Exception as exc:  # graph capture unavailable: report the eager numbers only
-        log(f"[bench] graph replay skipped: {exc}")
+    if not args.no_sub and not args.workload:
+        for c in SUB_CONFIGS:
+            if c == cfg:
+                continue
+            bc = W.make_batch(c)
+            dbc = DeviceBatch(torch, bc, args.replica_bytes)
+            mc = DEFAULT_MODE[c]
+            r = measure_decode(torch, pa, dbc, mc, bc.spec.partition_size or 512, args.steps, args.warmup)
+            subs[bc.spec.name] = r
+            log(f"[bench] {bc.spec.name} {mc}: {r['us_per_step']:.2f} us/step wall, {r['gpu_us_per_step']:.2f} GPU, "
+                f"{r['GB_per_s']:.1f} GB/s, frac {r['roofline_frac']:.4f}")
+            dbc.release()
+            del dbc, bc
+            torch.cuda.empty_cache()
+    if not args.no_sub:
+        sizes = [("131MB", 131 * 10**6), ("1GB", 10**9), ("4.3GB", 2**32)]
+        ceiling = stream_read_ceiling(torch, pa, sizes, args.replica_bytes, max(20, args.steps // 4))
 
-    # the write that precedes each decode step: one new token's K/V per sequence, stored
-    # (quantised for fp8) into its block. Timed on its own; the appended rows go to the slot
-    # of each sequence's last cached token, so the pool keeps its shape and cost is the same.
-    app = None
-    if sp.io_dtype in ("f32", "f16", "bf16"):
-        gen = torch.Generator(device="cuda").manual_seed(7)
-        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[sp.io_dtype]
-        kn = torch.randn((sp.num_seqs, sp.num_kv_heads, sp.head_dim), generator=gen, device="cuda").to(tdt)
-        vn = torch.randn((sp.num_seqs, sp.num_kv_heads, sp.head_dim), generator=gen, device="cuda").to(tdt)
-        sid = torch.arange(sp.num_seqs, dtype=torch.int32, device="cuda")
-        pos = torch.clamp(cl - 1, min=0)
-        appk = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K)]
-        for i in range(3):
-            pa.pa_append_kv(kn, vn, sid, pos, bt, k0, v0, k_scale=float(b.k_scale), v_scale=float(b.v_scale))
-        torch.cuda.synchronize()
-        for i in range(K):
-            appk[2 * i].record(stream)
-            pa.pa_append_kv(kn, vn, sid, pos, bt, k0, v0, k_scale=float(b.k_scale), v_scale=float(b.v_scale))
-            appk[2 * i + 1].record(stream)
-        torch.cuda.synchronize()
-        app_ms = float(np.mean([appk[2 * i].elapsed_time(appk[2 * i + 1]) for i in range(K)]))
-        io_b = {"f32": 4, "f16": 2, "bf16": 2}[sp.io_dtype]
-        app_bytes = sp.num_seqs * (sp.num_kv_heads * sp.head_dim * 2 * (io_b + e) + 12)
-        app = {"us_per_launch": round(app_ms * 1e3, 3), "bytes_per_launch": app_bytes,
-               "GB_per_s": round(app_bytes / (app_ms * 1e-3) / 1e9, 2)}
-
-    value = kv_unique / (ms_per_step * 1e-3) / 1e9
-    achieved = algo_bytes / (kern_ms * 1e-3) / 1e9
-    traffic = read_traffic(sp.name, mode)
+    wall_ms = head["us_per_step"] * 1e-3
+    gpu_ms = head["gpu_us_per_step"] * 1e-3
+    value = head["kv_unique_bytes"] / (wall_ms * 1e-3) / 1e9
+    achieved = head["algorithmic_bytes"] / (gpu_ms * 1e-3) / 1e9
     sum_l = int(b.context_lens.sum())
     res = {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
+        "ms_per_step": round(wall_ms, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -471,29 +634,26 @@ def main():
                    "block_size": sp.block_size, "io_dtype": sp.io_dtype, "kv_dtype": sp.kv_dtype,
                    "accumulate": "f32", "sum_context_len": sum_l,
                    "max_context_len": b.max_context_len, "pool_blocks": b.num_blocks,
-                   "kv_unique_bytes": kv_unique, "kv_logical_bytes": kv_logical,
-                   "kv_replicas": R},
+                   "kv_unique_bytes": head["kv_unique_bytes"], "kv_logical_bytes": sum_l * sp.num_kv_heads
+                   * sp.head_dim * KV_BYTES[sp.kv_dtype] * 2, "kv_replicas": replicas},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "seq_tokens_per_s": round(sum_l / (ms_per_step * 1e-3), 1),
-        "seqs_per_s": round(sp.num_seqs / (ms_per_step * 1e-3), 1),
+        "seq_tokens_per_s": round(sum_l / (wall_ms * 1e-3), 1),
+        "seqs_per_s": round(sp.num_seqs / (wall_ms * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "kernel_ms": round(kern_ms, 6),
-                     "algorithmic_bytes_per_launch": algo_bytes,
-                     "p10_p90_ms": [round(float(np.percentile(durs_ms, 10)), 6),
-                                    round(float(np.percentile(durs_ms, 90)), 6)]},
-        "cpu_baseline": None,
+                     "traffic": head["traffic"],
+                     "kernel_ms": round(gpu_ms, 6),
+                     "algorithmic_bytes_per_launch": head["algorithmic_bytes"],
+                     "timing": "HIP events on the launch stream around the timed steps; one step = "
+                               + ("the partition kernel plus the log-sum-exp merge kernel"
+                                  if mode == "partitioned" else "the decode launch(es) of the mode")},
+        "cpu_baseline": cpu,
+        "alt_modes": alt or None,
+        "configs": subs or None,
+        "stream_read_ceiling": ceiling,
         "append_kv": app,
-        "graph_replay": None if graph_ms is None else {
-            "ms_per_step": round(graph_ms, 6),
-            "GB_per_s": round(kv_unique / (graph_ms * 1e-3) / 1e9, 2)},
+        "graph_replay": head.get("graph_replay"),
     }
-    log(f"[bench] {ms_per_step * 1e3:.2f} us/step wall, {kern_ms * 1e3:.2f} us/launch (events): "
-        f"{value:.1f} GB/s KV, roofline frac {achieved / HBM_PEAK_GBS:.3f}")
-    del ks, vs
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

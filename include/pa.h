@@ -137,9 +137,10 @@ size_t pa_balanced_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads
  * Workspace: pa_balanced_workspace_bytes(...) bytes, 16-byte aligned. Its counter area
  * must be zero before the first call (e.g. hipMemset once after allocating); every
  * completed call leaves it zero again. Calls sharing a workspace must be ordered on one
- * stream. Shapes outside the matrix-core kernels (fp32 io or KV, 8 query heads per KV
- * head, rows of 64 bytes) and batches of more than 4096 sequences run the single-pass
- * kernel of pa_decode instead and leave the workspace untouched. */
+ * stream. Shapes the balanced kernel does not take run the single-pass kernel of
+ * pa_decode instead and leave the workspace untouched: fp32 io or KV, head_dim 256, token
+ * rows (head_dim times the KV element size) other than 128 or 256 bytes (e.g. fp8 with
+ * head_dim 64), and batches of more than 4096 sequences. */
 int pa_decode_balanced(const void* q, const void* k_pool, const void* v_pool,
                        const int32_t* block_tables, const int32_t* context_lens,
                        int num_seqs, int max_blocks_per_seq, int num_blocks,
@@ -260,6 +261,25 @@ int pa_check_tables(const int32_t* block_tables, const int32_t* context_lens,
 /* Converts n OCP e4m3 codes to fp32 with the same in-register conversion the decode
  * kernels use (for tests of the fp8 path). */
 int pa_debug_fp8_to_f32(const uint8_t* codes, float* out, int n, void* stream);
+
+/* Converts n OCP e4m3 codes to 16-bit values with the conversion that feeds the matrix
+ * cores (the K operand of the score product for fp8 KV, and the V tile of the matrix-core
+ * V product): out_dtype PA_F16 or PA_BF16 selects the type, out receives n 16-bit codes
+ * in the order of the input (for tests of the fp8 path; every e4m3 value is exact in
+ * both types). PA_ERR_INVALID on null pointers, n <= 0 or another out_dtype. */
+int pa_debug_fp8_to_16bit(const uint8_t* codes, uint16_t* out, int n, int out_dtype, void* stream);
+
+/* Measurement aid: reads bytes of device memory at buf once with the decode kernels'
+ * load shape (16-byte loads, each wave instruction one contiguous 1 KiB run) and nothing
+ * else, so that the time of this launch is the device's streaming-read rate for that shape
+ * (the ceiling the decode kernels' K/V streams are compared with). unroll in {4, 8, 16} is
+ * the loads each thread issues before using any; bytes must be a positive multiple of
+ * 4096 * unroll and buf 16-byte aligned. num_workgroups 0 gives every workgroup one
+ * iteration (bytes / (4096 * unroll) workgroups), else the workgroups stride over the
+ * buffer. sink: 256 uint32 of device memory, almost never written (only when the folded
+ * words hit a fixed pattern). PA_ERR_INVALID on other arguments. Asynchronous on `stream`. */
+int pa_debug_stream_read(const void* buf, size_t bytes, int unroll, int num_workgroups,
+                         uint32_t* sink, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * Host block manager ([P1] §2 and §5; [P3] paged-pool and prefix-caching sections): owns

@@ -41,6 +41,8 @@ SIGNATURES = {
     "pa_copy_blocks": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pa_extend": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _F, _F, _P, _P]),
     "pa_debug_fp8_to_f32": (_I, [_P, _P, _I, _P]),
+    "pa_debug_fp8_to_16bit": (_I, [_P, _P, _I, _I, _P]),
+    "pa_debug_stream_read": (_I, [_P, _SZ, _I, _I, _P, _P]),
     "pa_bm_create": (_P, [_I, _I, _I, _I]),
     "pa_bm_destroy": (None, [_P]),
     "pa_bm_num_free": (_I, [_P]),
@@ -459,6 +461,18 @@ def pa_debug_fp8_to_f32(codes, stream=None):
     out = torch.empty(codes.numel(), dtype=torch.float32, device=codes.device)
     _raise("pa_debug_fp8_to_f32",
            lib().pa_debug_fp8_to_f32(codes.data_ptr(), out.data_ptr(), codes.numel(), _stream(stream)))
+    return out
+
+
+def pa_debug_fp8_to_16bit(codes, out_dtype, stream=None):
+    """The matrix-core fp8 conversion: codes (uint8) -> out_dtype (torch.float16 or
+    torch.bfloat16) on the device."""
+    torch = _torch()
+    _check_dev("codes", codes)
+    out = torch.empty(codes.numel(), dtype=out_dtype, device=codes.device)
+    _raise("pa_debug_fp8_to_16bit",
+           lib().pa_debug_fp8_to_16bit(codes.data_ptr(), out.data_ptr(), codes.numel(), dtype_code(out),
+                                       _stream(stream)))
     return out
 
 

@@ -110,6 +110,29 @@ __global__ void fp8_probe_kernel(const uint8_t* codes, float* out, int n) {
     if (base + k < n) out[base + k] = f[k];
 }
 
+// The matrix-core operand conversion (fp8x8_operand, also used for the V tile): lane i
+// converts the 16 codes base .. base + 15 as two operands of eight 16-bit values.
+template <int MT>
+__global__ void fp8_mt_probe_kernel(const uint8_t* codes, uint16_t* out, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int base = i * 16;
+  if (base >= n) return;
+  uint32_t w[4];
+  for (int k = 0; k < 4; ++k) {
+    uint32_t x = 0;
+    for (int j = 0; j < 4; ++j) {
+      const int idx = base + 4 * k + j;
+      x |= (uint32_t)(idx < n ? codes[idx] : 0) << (8 * j);
+    }
+    w[k] = x;
+  }
+  const uint4 lo = __builtin_bit_cast(uint4, fp8x8_operand<MT>(w[0], w[1]));
+  const uint4 hi = __builtin_bit_cast(uint4, fp8x8_operand<MT>(w[2], w[3]));
+  const uint32_t r[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  for (int k = 0; k < 16; ++k)
+    if (base + k < n) out[base + k] = (uint16_t)(r[k / 2] >> (16 * (k % 2)));
+}
+
 bool is_pow_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
 int elem_bytes(int dt) {
@@ -550,6 +573,21 @@ int pa_debug_fp8_to_f32(const uint8_t* codes, float* out, int n, void* stream) {
   const int lanes = (n + 15) / 16;
   const int grid = (lanes + 255) / 256;
   hipLaunchKernelGGL(pa::fp8_probe_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, codes, out, n);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int pa_debug_fp8_to_16bit(const uint8_t* codes, uint16_t* out, int n, int out_dtype, void* stream) {
+  if (!codes || !out || n <= 0) return PA_ERR_INVALID;
+  if (out_dtype != PA_F16 && out_dtype != PA_BF16) return PA_ERR_INVALID;
+  const int lanes = (n + 15) / 16;
+  const int grid = (lanes + 255) / 256;
+  if (out_dtype == PA_F16) {
+    hipLaunchKernelGGL(pa::fp8_mt_probe_kernel<pa::kF16>, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                       codes, out, n);
+  } else {
+    hipLaunchKernelGGL(pa::fp8_mt_probe_kernel<pa::kBF16>, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                       codes, out, n);
+  }
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -1145,10 +1145,10 @@ balanced_decode_kernel(const DecodeArgs a) {
         store_io<IO>(a.out, ((int64_t)s * H + g * G + gi) * D + d, val);
       }
     } else {
-      // a piece: store (m, l, o) in one of this workgroup's two slots with device-coherent
-      // stores, then count the arrival. Slot 0 holds the piece of the sequence that starts
-      // inside the workgroup's range and runs past its end, slot 1 the piece of the one that
-      // started before the range (at most one of each).
+      // a piece: store (m, l, o) in one of this workgroup's two slots, then count the
+      // arrival. Slot 0 holds the piece of the (sequence, KV head) that began at or before
+      // the start of the workgroup's range (cb >= ub), slot 1 the piece of the one that
+      // begins inside the range and runs past its end (at most one of each).
       const int64_t ub = (int64_t)g * Cg + u0;  // cost position of this (s, g)'s first chunk
       float* slot = a.ws + ((int64_t)v * 2 + (cb >= ub ? 0 : 1)) * SLOT;
       for (int idx = tid; idx < G * D; idx += NTH) {
@@ -1162,18 +1162,23 @@ balanced_decode_kernel(const DecodeArgs a) {
           __hip_atomic_store(slot + G + gi, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
-      // every store of this workgroup has completed before the arrival is counted
-      __builtin_amdgcn_s_waitcnt(0);
+      // Release: every thread's slot stores are ordered, at agent scope (all XCDs), before
+      // the barrier and thereby before the arrival below. The workgroups of one unit may run
+      // on different XCDs, each with its own L2.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       __syncthreads();
       const int64_t w0 = chunk_owner(ub, C, nwg);
       const int64_t w1 = chunk_owner(ub + nch - 1, C, nwg);
       int32_t* counter = a.counters + (int64_t)g * S + s;
       if (tid == 0) {
-        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         sm_last = old == (int)(w1 - w0);
       }
       __syncthreads();
       if (sm_last) {
+        // Acquire: the pieces of the other workgroups, released before their arrivals,
+        // are visible to every thread of this one.
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         // last piece to arrive: merge all pieces of (s, g) and write the output
         for (int idx = tid; idx < G * D; idx += NTH) {
           const int gi = idx / D;

@@ -54,6 +54,34 @@ def test_fp8_hardware_conversion_matches_table():
     np.testing.assert_array_equal(got[~nan], ref[~nan])
 
 
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+def test_fp8_matrix_core_conversion_matches_table(io):
+    """The conversion that feeds the matrix cores (K operand and V tile of the fp8 decode
+    and extend kernels) gives, for every e4m3 code in each of the four byte positions of a
+    dword, the exact 16-bit code of the table value: signed zeros and subnormals
+    (m * 2^-9) included, NaN codes to a NaN."""
+    import torch
+    codes = torch.arange(256, dtype=torch.uint8, device="cuda")
+    # the 256 codes in all four byte positions: rotate by 0..3 so each code meets each lane slot
+    codes = torch.cat([torch.roll(codes, k) for k in range(4)])
+    dt = torch.float16 if io == "f16" else torch.bfloat16
+    got = pa.pa_debug_fp8_to_16bit(codes, dt).cpu().view(torch.int16).numpy().view(np.uint16)
+    ref_val = oracle.FP8_E4M3_TABLE[codes.cpu().numpy()]
+    nan = np.isnan(ref_val)
+    if io == "f16":
+        ref_bits = ref_val.astype(np.float16).view(np.uint16)
+        got_nan = (got & 0x7C00) == 0x7C00
+        got_nan &= (got & 0x03FF) != 0
+    else:
+        # every e4m3 value has at most 4 significant bits: the float32 value's top half is exact
+        f32 = ref_val.astype(np.float32)
+        assert (f32.view(np.uint32)[~nan] & 0xFFFF == 0).all()
+        ref_bits = (f32.view(np.uint32) >> 16).astype(np.uint16)
+        got_nan = ((got & 0x7F80) == 0x7F80) & ((got & 0x007F) != 0)
+    np.testing.assert_array_equal(got_nan, nan)
+    np.testing.assert_array_equal(got[~nan], ref_bits[~nan])
+
+
 def _raw_u8(a):
     return np.ascontiguousarray(a).view(np.uint8)
 
