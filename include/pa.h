@@ -72,7 +72,8 @@ typedef enum {
   PA_ERR_INVALID = -1,     /* null pointer, non-positive size, bad dtype code, ... */
   PA_ERR_UNSUPPORTED = -2, /* valid but not compiled: head_dim, block_size, group, dtype pair */
   PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than pa_partitioned_workspace_bytes */
-  PA_ERR_LAUNCH = -4       /* the HIP launch itself failed */
+  PA_ERR_LAUNCH = -4,      /* the HIP launch itself failed */
+  PA_ERR_SCRATCH = -5      /* the request needs more than the library's static scratch */
 } pa_status;
 
 /* Supported shapes: head_dim in {64, 128, 256} (256 on the vector kernel only, single
@@ -117,6 +118,31 @@ int pa_decode_partitioned(const void* q, const void* k_pool, const void* v_pool,
                           float v_scale, int max_context_len, int partition_size,
                           void* workspace, size_t workspace_bytes,
                           void* out, void* stream);
+
+/* Bytes of the device scratch of pa_decode_partitioned_noalloc (per GPU). */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* pa_decode_partitioned without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same kernels and the same result, bit for bit, as pa_decode_partitioned
+ * with the same arguments; the partition states live instead in a device array that the
+ * library holds, PA_NOALLOC_SCRATCH_BYTES (16 MiB) on each GPU it runs on, until the
+ * process ends. Calls whose pa_partitioned_workspace_bytes(num_seqs, num_heads, head_dim,
+ * max_context_len, partition_size) exceeds that return PA_ERR_SCRATCH before anything is
+ * enqueued (16 MiB holds e.g. 8 sequences x 32 heads x head_dim 128 up to 32768 tokens in
+ * 512-token partitions). The call allocates nothing; its first call on a device looks up
+ * that device's copy of the array (no allocation). Every call on one GPU uses that GPU's
+ * one array, so calls that overlap on a GPU (two streams, two threads) race and give
+ * undefined results: order them on one stream. Nothing needs to be cleared between calls
+ * (each call writes every partition state it reads). Errors as pa_decode_partitioned,
+ * plus PA_ERR_SCRATCH. */
+int pa_decode_partitioned_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int num_seqs, int max_blocks_per_seq, int num_blocks,
+                                  int num_heads, int num_kv_heads, int head_dim, int block_size,
+                                  float scale, int io_dtype, int kv_dtype, float k_scale,
+                                  float v_scale, int max_context_len, int partition_size,
+                                  void* out, void* stream);
 
 /* Workspace for pa_decode_balanced, in bytes (0 on invalid sizes): one int32 arrival
  * counter per (KV head, sequence), padded to 256 bytes, then two fp32 partial-state slots

@@ -18,7 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpa.so")
 
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
-PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_LAUNCH = 0, -1, -2, -3, -4
+PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_LAUNCH, PA_ERR_SCRATCH = 0, -1, -2, -3, -4, -5
+PA_NOALLOC_SCRATCH_BYTES = 16 << 20
 DEFAULT_PARTITION = 512
 
 # name -> (restype, argtypes), mirroring include/pa.h
@@ -31,6 +32,7 @@ SIGNATURES = {
     "pa_decode": (_I, _DECODE_ARGS + [_P, _P]),
     "pa_partitioned_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "pa_decode_partitioned": (_I, _DECODE_ARGS + [_I, _I, _P, _SZ, _P, _P]),
+    "pa_decode_partitioned_noalloc": (_I, _DECODE_ARGS + [_I, _I, _P, _P]),
     "pa_balanced_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "pa_decode_balanced": (_I, _DECODE_ARGS + [_I, _P, _SZ, _P, _P]),
     "pa_ordered_workspace_bytes": (_SZ, [_I]),
@@ -204,6 +206,19 @@ def pa_decode_partitioned(q, k_pool, v_pool, block_tables, context_lens, max_con
     _raise("pa_decode_partitioned",
            lib().pa_decode_partitioned(*args, int(max_context_len), int(partition_size),
                                        workspace.data_ptr(), nbytes, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def pa_decode_partitioned_noalloc(q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
+                                  scale: Optional[float] = None, partition_size: int = 0,
+                                  k_scale: float = 1.0, v_scale: float = 1.0, out=None, stream=None):
+    """Split-context paged decode whose partition states live in the library's static device
+    scratch (no workspace; calls on one GPU must not overlap); returns out. With out given,
+    the call allocates nothing."""
+    args, out, _ = _common(q, k_pool, v_pool, block_tables, context_lens, scale, k_scale, v_scale, out)
+    _raise("pa_decode_partitioned_noalloc",
+           lib().pa_decode_partitioned_noalloc(*args, int(max_context_len), int(partition_size),
+                                               out.data_ptr(), _stream(stream)))
     return out
 
 

@@ -12,9 +12,16 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "pa.h"
 #include "pa_decode_impl.h"
+
+// Partition states of pa_decode_partitioned_noalloc: one copy per GPU, held by the loaded
+// code object until the process ends. Host code never passes this name to a kernel (on
+// the host it is only a stand-in); it uses the device address from hipGetSymbolAddress.
+static __device__ __align__(256) char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
 
 namespace pa {
 namespace {
@@ -291,6 +298,26 @@ __global__ void __launch_bounds__(1024) order_kernel(const int32_t* context_lens
   }
 }
 
+// Device address of the current device's copy of `scratch`, looked up once per device
+// (with that device current) and kept.
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];
+
+int scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_LAUNCH;
+  if (dev < 0 || dev >= kMaxScratchDevices) return PA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return PA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
 size_t ordered_workspace_bytes(int S) { return (size_t)((((int64_t)S * 4) + 255) / 256 * 256); }
 
 int64_t num_parts_for(int max_context_len, int P) {
@@ -479,6 +506,35 @@ int pa_decode_partitioned(const void* q, const void* k_pool, const void* v_pool,
   }
 }
 
+int pa_decode_partitioned_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                                  int max_blocks_per_seq, int num_blocks, int num_heads, int num_kv_heads,
+                                  int head_dim, int block_size, float scale, int io_dtype, int kv_dtype,
+                                  float k_scale, float v_scale, int max_context_len, int partition_size,
+                                  void* out, void* stream) {
+  try {
+    if (partition_size < 0 || max_context_len < 0) return PA_ERR_INVALID;
+    const int P = partition_size == 0 ? pa::kDefaultPartition : partition_size;
+    pa::Common c{q, k_pool, v_pool, block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                 num_blocks, num_heads, num_kv_heads, head_dim, block_size, scale, io_dtype,
+                 kv_dtype, k_scale, v_scale, out};
+    // every host check before the first HIP call
+    int rc = pa::validate(c);
+    if (rc != PA_OK) return rc;
+    if (P % block_size != 0) return PA_ERR_INVALID;
+    const size_t need = pa_partitioned_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, P);
+    if (need == 0) return PA_ERR_INVALID;
+    if (need > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_SCRATCH;
+    void* ws = nullptr;
+    rc = pa::scratch_ptr(&ws);
+    if (rc != PA_OK) return rc;
+    return pa::run(c, pa::Mode::kPartitioned, max_context_len, P, 0, ws, PA_NOALLOC_SCRATCH_BYTES, nullptr,
+                   nullptr, nullptr, false, (hipStream_t)stream);
+  } catch (...) {
+    return PA_ERR_LAUNCH;
+  }
+}
+
 size_t pa_balanced_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                                    int num_workgroups) {
   if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_workgroups < 0 ||
@@ -598,6 +654,7 @@ const char* pa_status_str(int status) {
     case PA_ERR_UNSUPPORTED: return "unsupported shape or dtype combination";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_LAUNCH: return "kernel launch failed";
+    case PA_ERR_SCRATCH: return "request exceeds the library's static scratch (PA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

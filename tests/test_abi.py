@@ -187,6 +187,22 @@ def test_small_entry_points_reject():
     assert L.pa_debug_stream_read(FAKE, 4096 * 8, 8, -1, FAKE, None) == _lib.PA_ERR_INVALID
 
 
+def test_noalloc_refuses_requests_beyond_its_scratch():
+    """The allocation-free decode checks the partition-state size against its static scratch
+    on the host, before any HIP call."""
+    L = _lib.lib()
+    a = good_args(S=8, H=32, Hkv=32, D=128, BS=32, MB=1024, NB=8192, io=_lib.PA_F16, kv=_lib.PA_F16)
+    assert _lib.pa_partitioned_workspace_bytes(8, 32, 128, 65536, 512) > _lib.PA_NOALLOC_SCRATCH_BYTES
+    assert L.pa_decode_partitioned_noalloc(*a, 65536, 512, FAKE, None) == _lib.PA_ERR_SCRATCH
+    assert L.pa_decode_partitioned_noalloc(*a, 65536, 0, FAKE, None) == _lib.PA_ERR_SCRATCH
+    assert L.pa_decode_partitioned_noalloc(*a, 32768, 48, FAKE, None) == _lib.PA_ERR_INVALID  # P % BS
+    assert L.pa_decode_partitioned_noalloc(*a, -1, 512, FAKE, None) == _lib.PA_ERR_INVALID
+    assert L.pa_decode_partitioned_noalloc(*a, 32768, -512, FAKE, None) == _lib.PA_ERR_INVALID
+    bad = good_args(q=0)
+    assert L.pa_decode_partitioned_noalloc(*bad, 100, 16, FAKE, None) == _lib.PA_ERR_INVALID
+    assert "scratch" in _lib.pa_status_str(_lib.PA_ERR_SCRATCH)
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 4, 64)
