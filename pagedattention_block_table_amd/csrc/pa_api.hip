@@ -22,7 +22,6 @@
 // the host it is only a stand-in); it uses the device address from hipGetSymbolAddress.
 static __device__ __align__(256) char scratch[PA_NOALLOC_SCRATCH_BYTES];
 
-
 namespace pa {
 namespace {
 
@@ -39,44 +38,97 @@ struct MergeArgs {
   int max_ctx;
 };
 
-// Log-sum-exp merge of the partitions of one (sequence, head) per wave ([P2] §3.3 /
+// Log-sum-exp merge of the partitions of one (sequence, head) per workgroup ([P2] §3.3 /
 // §4.1 split-context kernel; the merge rule is the exact recombination of softmax
 // partial sums): M = max_p m_p, w_p = exp2(m_p - M), out = sum_p w_p o_p / sum_p w_p l_p.
-// Scores are in log2 units, as the decode kernel wrote them.
+// Scores are in log2 units, as the decode kernel wrote them. Thread t reads the 16-byte
+// column group t % (D/4) of the partitions t / (D/4) + k * SL (SL = 1024 / D slices),
+// eight partitions in flight, all issued before the maximum M is known; the slices are
+// summed through LDS at the end.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeDepth = 8;
+
 template <int IO, int D>
-__global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a) {
-  constexpr int PER = D / 64;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int pair = blockIdx.x * 4 + wave;
-  if (pair >= a.num_seqs * a.num_heads) return;
+__global__ void __launch_bounds__(kMergeThreads) merge_kernel(const MergeArgs a) {
+  constexpr int TPR = D / 4;                 // threads per partition row
+  constexpr int SL = kMergeThreads / TPR;    // partitions read side by side
+  __shared__ float sm_max[kMergeThreads / 64];
+  __shared__ float4 sm_acc[SL][TPR];
+  __shared__ float sm_den[SL][TPR];
+  const int pair = blockIdx.x;
   const int s = pair / a.num_heads;
   int L = a.context_lens[s];
   L = min(max(L, 0), a.max_ctx);
   const int n = (L + a.part_tokens - 1) / a.part_tokens;
-  if (n <= 1) return;  // written directly by the decode kernel
+  if (n <= 1) return;  // written directly by the decode kernel (whole workgroup)
   const int64_t NPH = (int64_t)a.num_seqs * a.num_heads * a.num_parts;
   const float* m = a.ws + (int64_t)pair * a.num_parts;
   const float* l = a.ws + NPH + (int64_t)pair * a.num_parts;
-  const float* o = a.ws + 2 * NPH + (int64_t)pair * a.num_parts * D;
+  const float4* o = (const float4*)(a.ws + 2 * NPH + (int64_t)pair * a.num_parts * D);
+  const int t = threadIdx.x;
+  const int col = t % TPR;
+  const int slice = t / TPR;
 
-  float M = -3.0e38f;
-  for (int p = lane; p < n; p += 64) M = fmaxf(M, m[p]);
-  M = rows_max<1>(M);
-
-  float acc[PER];
+  // first group of partitions: loads issued before the maximum is formed
+  float4 ov[kMergeDepth];
+  float mv[kMergeDepth], lv[kMergeDepth];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-  float den = 0.f;
-#pragma unroll 4
-  for (int p = 0; p < n; ++p) {
-    const float w = __builtin_amdgcn_exp2f(m[p] - M);
-    den = fmaf(w, l[p], den);
-#pragma unroll
-    for (int k = 0; k < PER; ++k) acc[k] = fmaf(w, o[(int64_t)p * D + lane + 64 * k], acc[k]);
+  for (int k = 0; k < kMergeDepth; ++k) {
+    const int p = min(slice + k * SL, n - 1);  // past the end: a valid partition, weight 0 below
+    ov[k] = o[(int64_t)p * TPR + col];
+    mv[k] = m[p];
+    lv[k] = l[p];
   }
+  float M = -3.0e38f;
+  for (int p = t; p < n; p += kMergeThreads) M = fmaxf(M, m[p]);
+  M = rows_max<1>(M);
+  if ((t & 63) == 0) sm_max[t >> 6] = M;
+  __syncthreads();
 #pragma unroll
-  for (int k = 0; k < PER; ++k) store_io<IO>(a.out, (int64_t)pair * D + lane + 64 * k, acc[k] / den);
+  for (int w = 0; w < kMergeThreads / 64; ++w) M = fmaxf(M, sm_max[w]);
+
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
+  for (int p0 = slice;; p0 += kMergeDepth * SL) {
+#pragma unroll
+    for (int k = 0; k < kMergeDepth; ++k) {
+      const float w = p0 + k * SL < n ? __builtin_amdgcn_exp2f(mv[k] - M) : 0.f;
+      den = fmaf(w, lv[k], den);
+      acc.x = fmaf(w, ov[k].x, acc.x);
+      acc.y = fmaf(w, ov[k].y, acc.y);
+      acc.z = fmaf(w, ov[k].z, acc.z);
+      acc.w = fmaf(w, ov[k].w, acc.w);
+    }
+    if (p0 + kMergeDepth * SL >= n) break;
+#pragma unroll
+    for (int k = 0; k < kMergeDepth; ++k) {
+      const int p = min(p0 + (kMergeDepth + k) * SL, n - 1);
+      ov[k] = o[(int64_t)p * TPR + col];
+      mv[k] = m[p];
+      lv[k] = l[p];
+    }
+  }
+  sm_acc[slice][col] = acc;
+  sm_den[slice][col] = den;
+  __syncthreads();
+  if (t < TPR) {
+    float4 x = sm_acc[0][t];
+    float dsum = sm_den[0][t];
+#pragma unroll
+    for (int k = 1; k < SL; ++k) {
+      const float4 y = sm_acc[k][t];
+      x.x += y.x;
+      x.y += y.y;
+      x.z += y.z;
+      x.w += y.w;
+      dsum += sm_den[k][t];
+    }
+    const int64_t base = (int64_t)pair * D + 4 * t;
+    store_io<IO>(a.out, base + 0, x.x / dsum);
+    store_io<IO>(a.out, base + 1, x.y / dsum);
+    store_io<IO>(a.out, base + 2, x.z / dsum);
+    store_io<IO>(a.out, base + 3, x.w / dsum);
+  }
 }
 
 // One thread per sequence checks its used block-table entries.
@@ -213,11 +265,11 @@ int launch_pair(int io, int kv, const LaunchSpec& ls) {
 template <int IO>
 int launch_merge_io(int D, const MergeArgs& m, int grid, hipStream_t st) {
   if (D == 64) {
-    hipLaunchKernelGGL((merge_kernel<IO, 64>), dim3(grid), dim3(256), 0, st, m);
+    hipLaunchKernelGGL((merge_kernel<IO, 64>), dim3(grid), dim3(kMergeThreads), 0, st, m);
   } else if (D == 128) {
-    hipLaunchKernelGGL((merge_kernel<IO, 128>), dim3(grid), dim3(256), 0, st, m);
+    hipLaunchKernelGGL((merge_kernel<IO, 128>), dim3(grid), dim3(kMergeThreads), 0, st, m);
   } else {
-    hipLaunchKernelGGL((merge_kernel<IO, 256>), dim3(grid), dim3(256), 0, st, m);
+    hipLaunchKernelGGL((merge_kernel<IO, 256>), dim3(grid), dim3(kMergeThreads), 0, st, m);
   }
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
@@ -325,11 +377,11 @@ int64_t num_parts_for(int max_context_len, int P) {
   return n < 1 ? 1 : n;
 }
 
-// Workgroups the balanced scheduler uses by default: two per compute unit of the current
-// device (queried once per device, thread-safe through the static local).
-int default_balanced_workgroups() {
+// Compute units of the current device (queried once per device, thread-safe through the
+// static local).
+int device_cus() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 512;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
   constexpr int kMaxDev = 64;
   static std::atomic<int> cache[kMaxDev];  // zero-initialised; 0 = not yet queried
   if (dev >= 0 && dev < kMaxDev) {
@@ -339,10 +391,16 @@ int default_balanced_workgroups() {
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  const int n = 2 * cus;
-  if (dev >= 0 && dev < kMaxDev) cache[dev].store(n, std::memory_order_relaxed);
-  return n;
+  if (dev >= 0 && dev < kMaxDev) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
+
+// Workgroups the balanced scheduler uses by default: two per compute unit.
+int default_balanced_workgroups() { return 2 * device_cus(); }
+
+// Split-context grids with at least this many units per compute unit run one unit per wave
+// (two waves per SIMD at least); smaller grids keep four waves per unit.
+constexpr int kWaveUnitsPerCu = 8;
 
 // The balanced scheduler covers the MFMA shapes: 1, 2 or 4 query heads per KV head,
 // io f16 / bf16, KV = io or fp8, 128 or 256 bytes per token row, at most
@@ -442,6 +500,7 @@ int run(const Common& c, Mode mode, int max_context_len, int P, int nwg, void* w
   const int64_t grid = (int64_t)c.Hkv * c.S * NP;
   if (grid > INT_MAX) return PA_ERR_INVALID;
   ls.grid = (int)grid;
+  ls.wave_units = mode == Mode::kPartitioned && grid >= (int64_t)kWaveUnitsPerCu * device_cus();
   rc = launch_pair(c.io, c.kv, ls);
   if (rc != PA_OK || NP <= 1) return rc;
   MergeArgs m{};
@@ -454,7 +513,7 @@ int run(const Common& c, Mode mode, int max_context_len, int P, int nwg, void* w
   m.part_tokens = P;
   m.max_ctx = ls.args.max_ctx;
   const int64_t pairs = (int64_t)c.S * c.H;
-  return launch_merge(c.io, c.D, m, (int)((pairs + 3) / 4), st);
+  return launch_merge(c.io, c.D, m, (int)pairs, st);
 }
 
 }  // namespace

@@ -468,18 +468,30 @@ __device__ __forceinline__ void process_chunk(const DecodeArgs& a, const int32_t
   consume_step<IO, KV, D, BS, G, U, TAIL, DBG>(a, buf, j0, t_end, r, c, s, g, qf, st);
 }
 
-template <int IO, int KV, int D, int BS, int G, int NW, int U, bool DBG>
+// WU (wave units): every wave of the workgroup runs a unit of its own, start to finish,
+// and writes it without any exchange between waves (units WG*NW .. WG*NW + NW-1 of the
+// XCD-aware order); else the NW waves share the workgroup's unit, taking its steps round
+// robin, and merge through LDS. The host takes WU for split-context grids with many
+// units: each wave then streams a whole partition (16 steps at 512 tokens) instead of a
+// quarter of it, and no wave waits for the others of its workgroup.
+template <int IO, int KV, int D, int BS, int G, int NW, int U, bool DBG, bool WU>
 __global__ void __launch_bounds__(NW * 64)
 decode_kernel(const DecodeArgs a) {
   using Geo = Geometry<KV, D, BS, G>;
   static_assert(Geo::ok, "unsupported geometry");
   constexpr int VEC = Geo::VEC, LPT = Geo::LPT;
+  constexpr int NWU = WU ? 1 : NW;  // waves sharing one unit
 
-  __shared__ float sm_m[NW][G];
-  __shared__ float sm_l[NW][G];
-  __shared__ float sm_o[NW][G][D];
+  __shared__ float sm_m[NWU][G];
+  __shared__ float sm_l[NWU][G];
+  __shared__ float sm_o[NWU][G][D];
 
-  const int unit = xcd_unit((int)blockIdx.x, (int)gridDim.x);
+  const int hw_wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int unit = xcd_unit((int)blockIdx.x, (int)gridDim.x);
+  if constexpr (WU) {
+    unit = unit * NW + hw_wave;
+    if (unit >= a.num_seqs * a.num_kv_heads * a.num_parts) return;  // past the last unit (this wave)
+  }
   const int part = unit % a.num_parts;
   const int sg = unit / a.num_parts;
   int s, g;
@@ -488,13 +500,13 @@ decode_kernel(const DecodeArgs a) {
   int L = a.context_lens[s];
   L = min(max(L, 0), a.max_ctx);
   const int t_begin = part * a.part_tokens;
-  if (part > 0 && t_begin >= L) return;  // nothing in this partition (whole workgroup)
+  if (part > 0 && t_begin >= L) return;  // nothing in this partition (whole unit)
   const int t_end = min(L, t_begin + a.part_tokens);
   constexpr int SB = Geo::SB;
   const int j_begin = t_begin / SB;
   const int j_end = (t_end + SB - 1) / SB;
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = WU ? 0 : hw_wave;  // index of this wave among the unit's waves
   const int lane = threadIdx.x & 63;
   const int r = lane / LPT;
   const int c = lane % LPT;
@@ -527,10 +539,10 @@ decode_kernel(const DecodeArgs a) {
   // loads of kVecDepth steps are in flight. Past the last step the issue repeats step
   // nwc - 1 (cached data, never consumed), so that the loop issues unconditionally.
   const int steps = (j_end - j_begin + U - 1) / U;
-  const int nwc = wave < steps ? (steps - wave + NW - 1) / NW : 0;
+  const int nwc = wave < steps ? (steps - wave + NWU - 1) / NWU : 0;
   if (nwc > 0) {
     using Buf = StepBuf<KV, D, BS, G, U>;
-    auto j0_of = [&](int k) { return j_begin + (wave + min(k, nwc - 1) * NW) * U; };
+    auto j0_of = [&](int k) { return j_begin + (wave + min(k, nwc - 1) * NWU) * U; };
     auto consume = [&](const Buf& b, int k) {
       const int j0 = j0_of(k);
       if ((j0 + U) * SB <= t_end) {
@@ -573,6 +585,33 @@ decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) st.acc[gi][e] = rows_sum<LPT>(st.acc[gi][e] * f);
   }
+  const int n_parts_s = (L + a.part_tokens - 1) / a.part_tokens;
+  const bool write_out = n_parts_s <= 1;
+  if constexpr (WU) {
+    // the wave holds its unit's whole state: lanes of row group 0 write their columns
+    if (r == 0) {
+      const int64_t NPH = (int64_t)a.num_seqs * H * a.num_parts;
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        const int h = g * G + gi;
+        if (write_out) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e)
+            store_io<IO>(a.out, ((int64_t)s * H + h) * D + c * VEC + e,
+                         st.l[gi] > 0.f ? (st.acc[gi][e] / st.l[gi]) * a.out_mul : 0.f);
+        } else {
+          const int64_t slot = ((int64_t)s * H + h) * a.num_parts + part;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) a.ws[2 * NPH + slot * D + c * VEC + e] = st.acc[gi][e] * a.out_mul;
+          if (c == 0) {
+            a.ws[slot] = st.m[gi];
+            a.ws[NPH + slot] = st.l[gi];
+          }
+        }
+      }
+    }
+    return;
+  }
   if (r == 0) {
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
@@ -587,17 +626,15 @@ decode_kernel(const DecodeArgs a) {
   __syncthreads();
 
   // merge the waves and write
-  const int n_parts_s = (L + a.part_tokens - 1) / a.part_tokens;
-  const bool write_out = n_parts_s <= 1;
   for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
     const int gi = idx / D;
     const int d = idx % D;
     float M = sm_m[0][gi];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][gi]);
+    for (int w = 1; w < NWU; ++w) M = fmaxf(M, sm_m[w][gi]);
     float o = 0.f, lsum = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
+    for (int w = 0; w < NWU; ++w) {
       const float f = __builtin_amdgcn_exp2f(sm_m[w][gi] - M);
       o = fmaf(f, sm_o[w][gi][d], o);
       lsum = fmaf(f, sm_l[w][gi], lsum);
@@ -724,7 +761,8 @@ struct LaunchSpec {
   int group;
   bool debug;
   bool balanced;   // balanced_decode_kernel (MFMA shapes only)
-  int grid;
+  bool wave_units; // vector kernel: one unit per wave (grid = ceil(units / waves per workgroup))
+  int grid;        // units (workgroups of the balanced kernel)
   hipStream_t stream;
 };
 
@@ -783,11 +821,20 @@ int launch_one(const LaunchSpec& ls) {
       }
       return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
     }
-    if (ls.debug) {
-      hipLaunchKernelGGL((decode_kernel<IO, KV, D, BS, G, NW, U, true>), dim3(ls.grid), dim3(NW * 64),
+    if (ls.wave_units) {
+      const int grid = (ls.grid + NW - 1) / NW;
+      if (ls.debug) {
+        hipLaunchKernelGGL((decode_kernel<IO, KV, D, BS, G, NW, U, true, true>), dim3(grid), dim3(NW * 64),
+                           0, ls.stream, ls.args);
+      } else {
+        hipLaunchKernelGGL((decode_kernel<IO, KV, D, BS, G, NW, U, false, true>), dim3(grid), dim3(NW * 64),
+                           0, ls.stream, ls.args);
+      }
+    } else if (ls.debug) {
+      hipLaunchKernelGGL((decode_kernel<IO, KV, D, BS, G, NW, U, true, false>), dim3(ls.grid), dim3(NW * 64),
                          0, ls.stream, ls.args);
     } else {
-      hipLaunchKernelGGL((decode_kernel<IO, KV, D, BS, G, NW, U, false>), dim3(ls.grid), dim3(NW * 64),
+      hipLaunchKernelGGL((decode_kernel<IO, KV, D, BS, G, NW, U, false, false>), dim3(ls.grid), dim3(NW * 64),
                          0, ls.stream, ls.args);
     }
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
