@@ -398,9 +398,28 @@ int device_cus() {
 // Workgroups the balanced scheduler uses by default: two per compute unit.
 int default_balanced_workgroups() { return 2 * device_cus(); }
 
-// Split-context grids with at least this many units per compute unit run one unit per wave
-// (two waves per SIMD at least); smaller grids keep four waves per unit.
-constexpr int kWaveUnitsPerCu = 8;
+// Waves per compute unit the split-context streaming kernel aims for: each wave takes
+// as many consecutive partitions as keeps the grid at about this many waves per CU.
+#ifndef PA_STREAM_WAVES_PER_CU
+#define PA_STREAM_WAVES_PER_CU 4
+#endif
+
+// Tokens per wave step of the vector kernel (its SB_MAX): 32, fewer for long rows.
+int vector_step_tokens(int D, int kv) {
+  const int t = 8192 / (D * elem_bytes(kv));
+  return t < 32 ? t : 32;
+}
+
+// Shapes that take the vector kernel rather than the matrix-core one (the per-unit kernels'
+// choice in launch_one: matrix cores for 2 to 8 query heads per KV head with 16-bit io, KV
+// of the io type or fp8, head_dim <= 128 and token rows of a multiple of 128 bytes).
+bool vector_shape(const Common& c) {
+  const int g = c.H / c.Hkv;
+  const int row = c.D * elem_bytes(c.kv);
+  const bool mfma = g >= 2 && (c.io == PA_F16 || c.io == PA_BF16) && (c.kv == c.io || c.kv == PA_FP8_E4M3) &&
+                    c.D <= 128 && row >= 128 && row % 128 == 0;
+  return !mfma;
+}
 
 // The balanced scheduler covers the MFMA shapes: 1, 2 or 4 query heads per KV head,
 // io f16 / bf16, KV = io or fp8, 128 or 256 bytes per token row, at most
@@ -500,7 +519,21 @@ int run(const Common& c, Mode mode, int max_context_len, int P, int nwg, void* w
   const int64_t grid = (int64_t)c.Hkv * c.S * NP;
   if (grid > INT_MAX) return PA_ERR_INVALID;
   ls.grid = (int)grid;
-  ls.wave_units = mode == Mode::kPartitioned && grid >= (int64_t)kWaveUnitsPerCu * device_cus();
+  if (mode == Mode::kPartitioned && NP > 1 && vector_shape(c) && P % vector_step_tokens(c.D, c.kv) == 0) {
+    // streaming kernel: runs of k consecutive partitions per wave, about
+    // PA_STREAM_WAVES_PER_CU waves per compute unit; runs of one (sequence, KV head) as
+    // even as the partition count allows
+    const int64_t units = (int64_t)c.Hkv * c.S;
+    const int64_t target = (int64_t)PA_STREAM_WAVES_PER_CU * device_cus();
+    int64_t runs = target / units;
+    runs = runs < 1 ? 1 : (runs > NP ? NP : runs);
+    const int64_t k = (NP + runs - 1) / runs;
+    const int64_t chunks = (NP + k - 1) / k;
+    ls.stream_kernel = true;
+    ls.args.wave_parts = (int)k;
+    ls.args.wave_chunks = (int)chunks;
+    ls.stream_waves = (int)((int64_t)c.Hkv * c.S * chunks);
+  }
   rc = launch_pair(c.io, c.kv, ls);
   if (rc != PA_OK || NP <= 1) return rc;
   MergeArgs m{};

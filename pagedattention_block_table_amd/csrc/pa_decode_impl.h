@@ -80,6 +80,8 @@ struct DecodeArgs {
   float out_mul;         // v_scale for fp8, else 1
   const int32_t* order;  // ordered mode: sequences by descending context length, else null
   int order_hpx;         // ordered mode: KV heads per XCD share of the units (0: not whole)
+  int wave_parts;        // split-context streaming kernel: consecutive partitions per wave
+  int wave_chunks;       // ... and runs of wave_parts partitions per (sequence, KV head)
 };
 
 // ---------------------------------------------------------------------------------
@@ -468,30 +470,18 @@ __device__ __forceinline__ void process_chunk(const DecodeArgs& a, const int32_t
   consume_step<IO, KV, D, BS, G, U, TAIL, DBG>(a, buf, j0, t_end, r, c, s, g, qf, st);
 }
 
-// WU (wave units): every wave of the workgroup runs a unit of its own, start to finish,
-// and writes it without any exchange between waves (units WG*NW .. WG*NW + NW-1 of the
-// XCD-aware order); else the NW waves share the workgroup's unit, taking its steps round
-// robin, and merge through LDS. The host takes WU for split-context grids with many
-// units: each wave then streams a whole partition (16 steps at 512 tokens) instead of a
-// quarter of it, and no wave waits for the others of its workgroup.
-template <int IO, int KV, int D, int BS, int G, int NW, int U, bool DBG, bool WU>
+template <int IO, int KV, int D, int BS, int G, int NW, int U, bool DBG>
 __global__ void __launch_bounds__(NW * 64)
 decode_kernel(const DecodeArgs a) {
   using Geo = Geometry<KV, D, BS, G>;
   static_assert(Geo::ok, "unsupported geometry");
   constexpr int VEC = Geo::VEC, LPT = Geo::LPT;
-  constexpr int NWU = WU ? 1 : NW;  // waves sharing one unit
 
-  __shared__ float sm_m[NWU][G];
-  __shared__ float sm_l[NWU][G];
-  __shared__ float sm_o[NWU][G][D];
+  __shared__ float sm_m[NW][G];
+  __shared__ float sm_l[NW][G];
+  __shared__ float sm_o[NW][G][D];
 
-  const int hw_wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int unit = xcd_unit((int)blockIdx.x, (int)gridDim.x);
-  if constexpr (WU) {
-    unit = unit * NW + hw_wave;
-    if (unit >= a.num_seqs * a.num_kv_heads * a.num_parts) return;  // past the last unit (this wave)
-  }
+  const int unit = xcd_unit((int)blockIdx.x, (int)gridDim.x);
   const int part = unit % a.num_parts;
   const int sg = unit / a.num_parts;
   int s, g;
@@ -500,13 +490,13 @@ decode_kernel(const DecodeArgs a) {
   int L = a.context_lens[s];
   L = min(max(L, 0), a.max_ctx);
   const int t_begin = part * a.part_tokens;
-  if (part > 0 && t_begin >= L) return;  // nothing in this partition (whole unit)
+  if (part > 0 && t_begin >= L) return;  // nothing in this partition (whole workgroup)
   const int t_end = min(L, t_begin + a.part_tokens);
   constexpr int SB = Geo::SB;
   const int j_begin = t_begin / SB;
   const int j_end = (t_end + SB - 1) / SB;
 
-  const int wave = WU ? 0 : hw_wave;  // index of this wave among the unit's waves
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int r = lane / LPT;
   const int c = lane % LPT;
@@ -539,10 +529,10 @@ decode_kernel(const DecodeArgs a) {
   // loads of kVecDepth steps are in flight. Past the last step the issue repeats step
   // nwc - 1 (cached data, never consumed), so that the loop issues unconditionally.
   const int steps = (j_end - j_begin + U - 1) / U;
-  const int nwc = wave < steps ? (steps - wave + NWU - 1) / NWU : 0;
+  const int nwc = wave < steps ? (steps - wave + NW - 1) / NW : 0;
   if (nwc > 0) {
     using Buf = StepBuf<KV, D, BS, G, U>;
-    auto j0_of = [&](int k) { return j_begin + (wave + min(k, nwc - 1) * NWU) * U; };
+    auto j0_of = [&](int k) { return j_begin + (wave + min(k, nwc - 1) * NW) * U; };
     auto consume = [&](const Buf& b, int k) {
       const int j0 = j0_of(k);
       if ((j0 + U) * SB <= t_end) {
@@ -585,12 +575,126 @@ decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) st.acc[gi][e] = rows_sum<LPT>(st.acc[gi][e] * f);
   }
+  if (r == 0) {
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) sm_o[wave][gi][c * VEC + e] = st.acc[gi][e];
+      if (c == 0) {
+        sm_m[wave][gi] = st.m[gi];
+        sm_l[wave][gi] = st.l[gi];
+      }
+    }
+  }
+  __syncthreads();
+
+  // merge the waves and write
   const int n_parts_s = (L + a.part_tokens - 1) / a.part_tokens;
   const bool write_out = n_parts_s <= 1;
-  if constexpr (WU) {
-    // the wave holds its unit's whole state: lanes of row group 0 write their columns
-    if (r == 0) {
+  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
+    const int gi = idx / D;
+    const int d = idx % D;
+    float M = sm_m[0][gi];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][gi]);
+    float o = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = __builtin_amdgcn_exp2f(sm_m[w][gi] - M);
+      o = fmaf(f, sm_o[w][gi][d], o);
+      lsum = fmaf(f, sm_l[w][gi], lsum);
+    }
+    const int h = g * G + gi;
+    if (write_out) {
+      const float v = lsum > 0.f ? (o / lsum) * a.out_mul : 0.f;
+      store_io<IO>(a.out, ((int64_t)s * H + h) * D + d, v);
+    } else {
       const int64_t NPH = (int64_t)a.num_seqs * H * a.num_parts;
+      const int64_t slot = ((int64_t)s * H + h) * a.num_parts + part;
+      a.ws[2 * NPH + slot * D + d] = o * a.out_mul;
+      if (d == 0) {
+        a.ws[slot] = M;
+        a.ws[NPH + slot] = lsum;
+      }
+    }
+  }
+}
+
+// Split-context decode, streaming form. Each wave takes a run of a.wave_parts consecutive
+// partitions of one (sequence, KV head) and streams their tokens as one wave does in
+// decode_kernel, in steps of U (sub-)blocks with the next steps' loads in flight; at the
+// end of every partition it merges its row groups, writes that partition's state (or the
+// output, for a sequence of one partition) and starts the next partition from a fresh
+// state, while the loads of the next partition's first steps are already in flight. The
+// host picks wave_parts so that the grid holds a few waves per SIMD: each wave then has a
+// long, unbroken stream (a whole 4K-token run at 512-token partitions of 32K contexts)
+// instead of one partition between a dependent prologue and a write. Partitions are whole
+// steps (the partition size is a multiple of the step, U * SB tokens), so a step never
+// spans two partitions and only the context end is masked.
+template <int IO, int KV, int D, int BS, int G, int NW, int U, bool DBG>
+__global__ void __launch_bounds__(NW * 64)
+decode_stream_kernel(const DecodeArgs a) {
+  using Geo = Geometry<KV, D, BS, G>;
+  static_assert(Geo::ok, "unsupported geometry");
+  constexpr int VEC = Geo::VEC, LPT = Geo::LPT, SB = Geo::SB;
+  constexpr int ST = U * SB;  // tokens per step
+
+  const int hw_wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = xcd_unit((int)blockIdx.x, (int)gridDim.x) * NW + hw_wave;
+  const int cps = a.wave_chunks;
+  if (gw >= a.num_seqs * a.num_kv_heads * cps) return;  // past the last run (this wave)
+  const int chunk = gw % cps;
+  int s, g;
+  unit_seq_head(a, gw / cps, s, g);
+
+  int L = a.context_lens[s];
+  L = min(max(L, 0), a.max_ctx);
+  const int P = a.part_tokens;
+  const int p0 = chunk * a.wave_parts;
+  const int t0 = p0 * P;
+  if (chunk > 0 && t0 >= L) return;  // nothing in this run
+  const int t_stop = min(L, t0 + a.wave_parts * P);
+  const int n_parts_s = (L + P - 1) / P;
+  const bool write_out = n_parts_s <= 1;
+  const int spp = P / ST;                        // steps per partition
+  const int nsteps = (t_stop - t0 + ST - 1) / ST;
+
+  const int lane = threadIdx.x & 63;
+  const int r = lane / LPT;
+  const int c = lane % LPT;
+  const int H = a.num_heads;
+  const int64_t NPH = (int64_t)a.num_seqs * H * a.num_parts;
+
+  float qf[G][VEC];
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    const int64_t base = ((int64_t)s * H + (int64_t)g * G + gi) * D + c * VEC;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) qf[gi][e] = load_io<IO>(a.q, base + e) * a.q_mul;
+  }
+  RowState<G, VEC> st;
+  auto reset = [&]() {
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      st.m[gi] = -3.0e38f;
+      st.l[gi] = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) st.acc[gi][e] = 0.f;
+    }
+  };
+  // merge the row groups of the wave, then lanes of row group 0 write their columns of
+  // partition `part` (or of the output)
+  auto finish = [&](int part) {
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      const float M = rows_max<LPT>(st.m[gi]);
+      const float f = __builtin_amdgcn_exp2f(st.m[gi] - M);
+      st.m[gi] = M;
+      st.l[gi] = rows_sum<LPT>(st.l[gi] * f);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) st.acc[gi][e] = rows_sum<LPT>(st.acc[gi][e] * f);
+    }
+    if (r == 0) {
 #pragma unroll
       for (int gi = 0; gi < G; ++gi) {
         const int h = g * G + gi;
@@ -610,49 +714,63 @@ decode_kernel(const DecodeArgs a) {
         }
       }
     }
+  };
+  reset();
+  if (nsteps <= 0) {  // empty sequence: its output is zero
+    finish(p0);
     return;
   }
-  if (r == 0) {
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) sm_o[wave][gi][c * VEC + e] = st.acc[gi][e];
-      if (c == 0) {
-        sm_m[wave][gi] = st.m[gi];
-        sm_l[wave][gi] = st.l[gi];
-      }
-    }
-  }
-  __syncthreads();
 
-  // merge the waves and write
-  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
-    const int gi = idx / D;
-    const int d = idx % D;
-    float M = sm_m[0][gi];
-#pragma unroll
-    for (int w = 1; w < NWU; ++w) M = fmaxf(M, sm_m[w][gi]);
-    float o = 0.f, lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < NWU; ++w) {
-      const float f = __builtin_amdgcn_exp2f(sm_m[w][gi] - M);
-      o = fmaf(f, sm_o[w][gi][d], o);
-      lsum = fmaf(f, sm_l[w][gi], lsum);
-    }
-    const int h = g * G + gi;
-    if (write_out) {
-      const float v = lsum > 0.f ? (o / lsum) * a.out_mul : 0.f;
-      store_io<IO>(a.out, ((int64_t)s * H + h) * D + d, v);
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const int64_t blk_stride = (int64_t)a.num_kv_heads * Geo::TILE;
+  const char* kbase = (const char*)a.k_pool + (int64_t)g * Geo::TILE;
+  const char* vbase = (const char*)a.v_pool + (int64_t)g * Geo::TILE;
+  const int j_begin = t0 / SB;
+  const int j_end = (t_stop + SB - 1) / SB;
+
+  using Buf = StepBuf<KV, D, BS, G, U>;
+  auto j0_of = [&](int k) { return j_begin + min(k, nsteps - 1) * U; };
+  auto consume = [&](const Buf& b, int k) {
+    const int j0 = j0_of(k);
+    if ((j0 + U) * SB <= L) {
+      consume_step<IO, KV, D, BS, G, U, false, DBG>(a, b, j0, L, r, c, s, g, qf, st);
     } else {
-      const int64_t NPH = (int64_t)a.num_seqs * H * a.num_parts;
-      const int64_t slot = ((int64_t)s * H + h) * a.num_parts + part;
-      a.ws[2 * NPH + slot * D + d] = o * a.out_mul;
-      if (d == 0) {
-        a.ws[slot] = M;
-        a.ws[NPH + slot] = lsum;
-      }
+      consume_step<IO, KV, D, BS, G, U, true, DBG>(a, b, j0, L, r, c, s, g, qf, st);
+    }
+  };
+  // after step k's successor loads are issued: close the partition if step k ended it
+  auto close = [&](int k) {
+    if ((k + 1) % spp == 0 || k + 1 == nsteps) {
+      finish(p0 + k / spp);
+      reset();
+    }
+  };
+  Buf buf[kVecDepth];
+  int nid[kVecDepth][U];
+#pragma unroll
+  for (int d = 0; d < kVecDepth; ++d) {
+    int bid[U];
+    step_blocks<KV, D, BS, G, U>(a, bt, j0_of(d), j_end, bid);
+    issue_step<KV, D, BS, G, U>(buf[d], kbase, vbase, blk_stride, bid, j0_of(d), L, r, c);
+    step_blocks<KV, D, BS, G, U>(a, bt, j0_of(d + kVecDepth), j_end, nid[d]);
+  }
+  int k = 0;
+  for (; k + kVecDepth <= nsteps; k += kVecDepth) {
+#pragma unroll
+    for (int d = 0; d < kVecDepth; ++d) {
+      consume(buf[d], k + d);
+      const int kn = k + d + kVecDepth;
+      issue_step<KV, D, BS, G, U>(buf[d], kbase, vbase, blk_stride, nid[d], j0_of(kn), L, r, c);
+      step_blocks<KV, D, BS, G, U>(a, bt, j0_of(kn + kVecDepth), j_end, nid[d]);
+      close(k + d);
     }
   }
+#pragma unroll
+  for (int d = 0; d < kVecDepth - 1; ++d)
+    if (k + d < nsteps) {
+      consume(buf[d], k + d);
+      close(k + d);
+    }
 }
 
 // The vector path as an engine of the chunk schedulers (the balanced grid): the same
@@ -761,8 +879,9 @@ struct LaunchSpec {
   int group;
   bool debug;
   bool balanced;   // balanced_decode_kernel (MFMA shapes only)
-  bool wave_units; // vector kernel: one unit per wave (grid = ceil(units / waves per workgroup))
-  int grid;        // units (workgroups of the balanced kernel)
+  bool stream_kernel;  // split-context: the streaming kernel if the shape takes the vector kernel
+  int stream_waves;    // its grid, in waves
+  int grid;            // units (workgroups of the balanced kernel)
   hipStream_t stream;
 };
 
@@ -821,20 +940,22 @@ int launch_one(const LaunchSpec& ls) {
       }
       return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
     }
-    if (ls.wave_units) {
-      const int grid = (ls.grid + NW - 1) / NW;
+    if (ls.stream_kernel && ls.args.part_tokens % (U * Geometry<KV, D, BS, G>::SB) == 0) {
+      const int grid = (ls.stream_waves + NW - 1) / NW;
       if (ls.debug) {
-        hipLaunchKernelGGL((decode_kernel<IO, KV, D, BS, G, NW, U, true, true>), dim3(grid), dim3(NW * 64),
-                           0, ls.stream, ls.args);
+        hipLaunchKernelGGL((decode_stream_kernel<IO, KV, D, BS, G, NW, U, true>), dim3(grid), dim3(NW * 64), 0,
+                           ls.stream, ls.args);
       } else {
-        hipLaunchKernelGGL((decode_kernel<IO, KV, D, BS, G, NW, U, false, true>), dim3(grid), dim3(NW * 64),
-                           0, ls.stream, ls.args);
+        hipLaunchKernelGGL((decode_stream_kernel<IO, KV, D, BS, G, NW, U, false>), dim3(grid), dim3(NW * 64), 0,
+                           ls.stream, ls.args);
       }
-    } else if (ls.debug) {
-      hipLaunchKernelGGL((decode_kernel<IO, KV, D, BS, G, NW, U, true, false>), dim3(ls.grid), dim3(NW * 64),
+      return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+    }
+    if (ls.debug) {
+      hipLaunchKernelGGL((decode_kernel<IO, KV, D, BS, G, NW, U, true>), dim3(ls.grid), dim3(NW * 64),
                          0, ls.stream, ls.args);
     } else {
-      hipLaunchKernelGGL((decode_kernel<IO, KV, D, BS, G, NW, U, false, false>), dim3(ls.grid), dim3(NW * 64),
+      hipLaunchKernelGGL((decode_kernel<IO, KV, D, BS, G, NW, U, false>), dim3(ls.grid), dim3(NW * 64),
                          0, ls.stream, ls.args);
     }
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
