@@ -455,6 +455,56 @@ __device__ __forceinline__ void step_blocks(const DecodeArgs& a, const int32_t* 
   }
 }
 
+// Physical blocks of a wave's steps, fetched ahead with vector loads. Lane l of window w
+// holds the table entries of the wave's step 64 w + l, whose (sub-)blocks are
+// j_first + (64 w + l) j_stride + u, u < U; the wave takes a step's ids with readlane.
+// Window 0 is requested before the context length is known (it needs only the unit's
+// first block), together with it, so the first K/V loads wait for one memory round trip
+// instead of two; window w + 1 is requested when the wave enters window w, 64 steps
+// ahead of its use. A table read that depended on the previous step would sit between
+// that step's compute and the next step's loads, and once the device streams at full
+// rate every such read waits behind the queued K/V requests. Entries are read inside the
+// table row (indices clamped to it); entries of steps past the wave's last step are read
+// but never used, and ids are clamped into the pool when taken, so that a bad table never
+// reads outside it (contract: 0 <= id < num_blocks). A refill is issued right before a
+// step's K/V loads, so waiting for those loads covers it in order.
+template <int U, int SPB>
+struct StepWindow {
+  int win[2][U];
+  int cur;
+  const int32_t* bt;
+  int last, j_first, j_stride;
+
+  __device__ __forceinline__ void load(int w, int (&dst)[U]) const {
+    const int k = 64 * w + (int)(threadIdx.x & 63);
+#pragma unroll
+    for (int u = 0; u < U; ++u) dst[u] = bt[min((j_first + k * j_stride + u) / SPB, last)];
+  }
+  __device__ __forceinline__ void begin(const int32_t* bt_row, int row_len, int j_first_, int j_stride_) {
+    bt = bt_row;
+    last = row_len - 1;
+    j_first = j_first_;
+    j_stride = j_stride_;
+    cur = 0;
+    load(0, win[0]);
+    load(1, win[1]);
+  }
+  // ids of step k (k never decreases between calls)
+  __device__ __forceinline__ void ids(int k, int num_blocks, int (&bid)[U]) {
+    if ((k >> 6) != cur) {
+      cur = k >> 6;
+#pragma unroll
+      for (int u = 0; u < U; ++u) win[0][u] = win[1][u];
+      load(cur + 1, win[1]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int b = __builtin_amdgcn_readlane(win[0][u], k & 63);
+      bid[u] = min(max(b, 0), num_blocks - 1);
+    }
+  }
+};
+
 // One step of U consecutive (sub-)blocks starting at j0, loaded and consumed at once.
 template <int IO, int KV, int D, int BS, int G, int U, bool TAIL, bool DBG>
 __device__ __forceinline__ void process_chunk(const DecodeArgs& a, const int32_t* bt,
@@ -487,16 +537,22 @@ decode_kernel(const DecodeArgs a) {
   int s, g;
   unit_seq_head(a, sg, s, g);
 
+  constexpr int SB = Geo::SB;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t_begin = part * a.part_tokens;
+  const int j_begin = t_begin / SB;
+  // this wave's steps k start at (sub-)block j_begin + (wave + k NW) U; their table
+  // entries are requested together with the context length
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  StepWindow<U, Geo::SPB> tw;
+  tw.begin(bt, a.max_blocks_per_seq, j_begin + wave * U, NW * U);
+
   int L = a.context_lens[s];
   L = min(max(L, 0), a.max_ctx);
-  const int t_begin = part * a.part_tokens;
   if (part > 0 && t_begin >= L) return;  // nothing in this partition (whole workgroup)
   const int t_end = min(L, t_begin + a.part_tokens);
-  constexpr int SB = Geo::SB;
-  const int j_begin = t_begin / SB;
   const int j_end = (t_end + SB - 1) / SB;
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int r = lane / LPT;
   const int c = lane % LPT;
@@ -520,7 +576,6 @@ decode_kernel(const DecodeArgs a) {
     for (int e = 0; e < VEC; ++e) st.acc[gi][e] = 0.f;
   }
 
-  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   const int64_t blk_stride = (int64_t)a.num_kv_heads * Geo::TILE;
   const char* kbase = (const char*)a.k_pool + (int64_t)g * Geo::TILE;
   const char* vbase = (const char*)a.v_pool + (int64_t)g * Geo::TILE;
@@ -541,23 +596,20 @@ decode_kernel(const DecodeArgs a) {
         consume_step<IO, KV, D, BS, G, U, true, DBG>(a, b, j0, t_end, r, c, s, g, qf, st);
       }
     };
-    Buf buf[kVecDepth];
-    int nid[kVecDepth][U];  // block ids of the next step issued into each buffer
-#pragma unroll
-    for (int d = 0; d < kVecDepth; ++d) {
+    auto issue = [&](Buf& b, int k) {
       int bid[U];
-      step_blocks<KV, D, BS, G, U>(a, bt, j0_of(d), j_end, bid);
-      issue_step<KV, D, BS, G, U>(buf[d], kbase, vbase, blk_stride, bid, j0_of(d), t_end, r, c);
-      step_blocks<KV, D, BS, G, U>(a, bt, j0_of(d + kVecDepth), j_end, nid[d]);
-    }
+      tw.ids(min(k, nwc - 1), a.num_blocks, bid);
+      issue_step<KV, D, BS, G, U>(b, kbase, vbase, blk_stride, bid, j0_of(k), t_end, r, c);
+    };
+    Buf buf[kVecDepth];
+#pragma unroll
+    for (int d = 0; d < kVecDepth; ++d) issue(buf[d], d);
     int k = 0;
     for (; k + kVecDepth <= nwc; k += kVecDepth) {
 #pragma unroll
       for (int d = 0; d < kVecDepth; ++d) {
         consume(buf[d], k + d);
-        const int kn = k + d + kVecDepth;
-        issue_step<KV, D, BS, G, U>(buf[d], kbase, vbase, blk_stride, nid[d], j0_of(kn), t_end, r, c);
-        step_blocks<KV, D, BS, G, U>(a, bt, j0_of(kn + kVecDepth), j_end, nid[d]);
+        issue(buf[d], k + d + kVecDepth);
       }
     }
 #pragma unroll
@@ -647,11 +699,18 @@ decode_stream_kernel(const DecodeArgs a) {
   int s, g;
   unit_seq_head(a, gw / cps, s, g);
 
-  int L = a.context_lens[s];
-  L = min(max(L, 0), a.max_ctx);
   const int P = a.part_tokens;
   const int p0 = chunk * a.wave_parts;
   const int t0 = p0 * P;
+  const int j_begin = t0 / SB;
+  // step k starts at (sub-)block j_begin + k U; the first steps' table entries are requested
+  // together with the context length
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  StepWindow<U, Geo::SPB> tw;
+  tw.begin(bt, a.max_blocks_per_seq, j_begin, U);
+
+  int L = a.context_lens[s];
+  L = min(max(L, 0), a.max_ctx);
   if (chunk > 0 && t0 >= L) return;  // nothing in this run
   const int t_stop = min(L, t0 + a.wave_parts * P);
   const int n_parts_s = (L + P - 1) / P;
@@ -721,12 +780,9 @@ decode_stream_kernel(const DecodeArgs a) {
     return;
   }
 
-  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   const int64_t blk_stride = (int64_t)a.num_kv_heads * Geo::TILE;
   const char* kbase = (const char*)a.k_pool + (int64_t)g * Geo::TILE;
   const char* vbase = (const char*)a.v_pool + (int64_t)g * Geo::TILE;
-  const int j_begin = t0 / SB;
-  const int j_end = (t_stop + SB - 1) / SB;
 
   using Buf = StepBuf<KV, D, BS, G, U>;
   auto j0_of = [&](int k) { return j_begin + min(k, nsteps - 1) * U; };
@@ -745,23 +801,20 @@ decode_stream_kernel(const DecodeArgs a) {
       reset();
     }
   };
-  Buf buf[kVecDepth];
-  int nid[kVecDepth][U];
-#pragma unroll
-  for (int d = 0; d < kVecDepth; ++d) {
+  auto issue = [&](Buf& b, int k) {
     int bid[U];
-    step_blocks<KV, D, BS, G, U>(a, bt, j0_of(d), j_end, bid);
-    issue_step<KV, D, BS, G, U>(buf[d], kbase, vbase, blk_stride, bid, j0_of(d), L, r, c);
-    step_blocks<KV, D, BS, G, U>(a, bt, j0_of(d + kVecDepth), j_end, nid[d]);
-  }
+    tw.ids(min(k, nsteps - 1), a.num_blocks, bid);
+    issue_step<KV, D, BS, G, U>(b, kbase, vbase, blk_stride, bid, j0_of(k), L, r, c);
+  };
+  Buf buf[kVecDepth];
+#pragma unroll
+  for (int d = 0; d < kVecDepth; ++d) issue(buf[d], d);
   int k = 0;
   for (; k + kVecDepth <= nsteps; k += kVecDepth) {
 #pragma unroll
     for (int d = 0; d < kVecDepth; ++d) {
       consume(buf[d], k + d);
-      const int kn = k + d + kVecDepth;
-      issue_step<KV, D, BS, G, U>(buf[d], kbase, vbase, blk_stride, nid[d], j0_of(kn), L, r, c);
-      step_blocks<KV, D, BS, G, U>(a, bt, j0_of(kn + kVecDepth), j_end, nid[d]);
+      issue(buf[d], k + d + kVecDepth);
       close(k + d);
     }
   }

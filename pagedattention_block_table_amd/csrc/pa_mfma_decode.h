@@ -899,6 +899,292 @@ struct MfmaPvEngine {
   }
 };
 
+// Per-wave engine with both products on the matrix cores in transposed form, for G = 2, 4
+// or 8 query heads per KV head (any supported KV type). Scores run as S^T = K Q^T
+// (16x16x32: A = the chunk's K rows straight from the lanes' 16-byte loads, B = the query
+// rows; row rho of the 16 holds head rho % G), so that lane l receives the scores of query
+// row l % 16 for tokens 4 (l / 16) .. +3 of each 16-token tile: after the softmax these are
+// exactly its B operand of O^T += V^T P^T (16x16x16, A = V^T read transposed from the
+// wave's LDS copy of the V tile, the same reads as MfmaPvEngine's B operand). The
+// probabilities never leave the registers (high and low 16-bit halves, fp32 accuracy), and
+// each lane keeps the running max and exp-sum of its own row; the four lanes of a row take
+// identical decisions. The lazy raise of the running max is decided per row, so a row's
+// arithmetic depends only on its own scores. fp8 K is converted to the MFMA type in
+// registers and fp8 V while it is written to LDS (both exact). Chunks are NT 16-token tiles.
+template <int IO, int KV, int D, int BS, int G, int NT, bool DBG>
+struct MfmaTEngine {
+  using Geo = MfmaGeo<KV, D>;
+  static constexpr int CT = 16 * NT;
+  static constexpr int NBC = CT >= BS ? CT / BS : 1;
+  static constexpr int RB = Geo::RB;
+  static constexpr int TILE_BYTES = BS * RB;
+  static constexpr int NDT = D / 16;
+  static constexpr int NV = VTileRegs<KV, D>::NV;  // V loads per lane per 16-token tile
+  static constexpr int VT_ROW = D + 16;             // 16-bit elements per LDS tile row (32 B pad)
+  static constexpr int VT_BYTES = 16 * VT_ROW * 2;
+  static constexpr int kLdsBytes = NT * VT_BYTES;
+  using vec = typename Mma<IO>::vec;
+  using M16 = Mma16<IO>;
+  using v4 = typename M16::v4;
+  static_assert(G == 2 || G == 4 || G == 8, "group");
+  static_assert(mfma_supported<IO, KV, D, G>(), "unsupported MFMA decode geometry");
+  static_assert(NV >= 1 && 16 * RB % 1024 == 0, "V tile of whole wave loads");
+  static_assert(CT % BS == 0 || BS % CT == 0, "chunks and blocks nest");
+
+  struct Buf {
+    uint4 kr[NT][Geo::CPL];
+    VTileRegs<KV, D> vt[NT];
+  };
+
+  LaneIds li;
+  int s, g, t_end, j_end;
+  int base, k0, len, rot, wave, nw;
+  const int32_t* bt;
+  const char* kbase;
+  const char* vbase;
+  int64_t blk_stride;
+  int win[2][NBC];
+  int cur_win;
+  vec qa[Geo::NST];
+  float m, l;       // running max (log2 units) of row li.n, this lane's part of its exp-sum
+  f32x4_t o[NDT];   // O^T: register r of tile dt holds column 16 dt + 4 lg + r of row li.n
+  char* lds;        // this wave's V tiles
+
+  __device__ __forceinline__ MfmaTEngine(int lane, char* wave_lds) : li(lane), lds(wave_lds) {}
+
+  __device__ __forceinline__ int chunk_token(int k) const {
+    return base + CT * (k0 + rotated(wave + k * nw, rot, len));
+  }
+
+  // Raw table entries of the wave's chunks 64w .. 64w+63 (lane l: chunk 64w + l); entries
+  // of chunks or blocks past the end read entry 0 of the row instead (never used for a
+  // valid token). Ids are clamped into the pool when they are taken (block_off).
+  __device__ __forceinline__ void load_window(const DecodeArgs& a, int w, int (&dst)[NBC]) {
+    const int k = 64 * w + li.lane;
+    const bool live = wave + k * nw < len;
+    const int j = live ? chunk_token(k) / BS : 0;
+#pragma unroll
+    for (int u = 0; u < NBC; ++u) dst[u] = bt[live && j + u < j_end ? j + u : 0];
+  }
+
+  // Byte offset of the u-th block of chunk k (k in the current window), its id clamped
+  // into the pool so that a bad table never reads outside it (contract: 0 <= id < num_blocks).
+  __device__ __forceinline__ int64_t block_off(const DecodeArgs& a, int u, int k) const {
+    const int b = __builtin_amdgcn_readlane(win[0][u], k & 63);
+    return (int64_t)min(max(b, 0), a.num_blocks - 1) * blk_stride;
+  }
+
+  __device__ __forceinline__ void begin(const DecodeArgs& a, int s_, int g_, int t_end_, int base_,
+                                        int k0_, int len_, int rot_, int wave_, int nw_) {
+    s = s_;
+    g = g_;
+    t_end = t_end_;
+    j_end = (t_end + BS - 1) / BS;
+    base = base_;
+    k0 = k0_;
+    len = len_;
+    rot = rot_;
+    wave = wave_;
+    nw = nw_;
+    bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    blk_stride = (int64_t)a.num_kv_heads * TILE_BYTES;
+    kbase = (const char*)a.k_pool + (int64_t)g * TILE_BYTES;
+    vbase = (const char*)a.v_pool + (int64_t)g * TILE_BYTES;
+    load_window(a, 0, win[0]);
+    load_window(a, 1, win[1]);
+    cur_win = 0;
+    load_q<IO, KV, D, G>(a, s, g, li, qa);
+    m = -3.0e38f;
+    l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Block offset of token t of the chunk starting at c0 (jb = c0 / BS).
+  __device__ __forceinline__ int64_t tok_block(const int64_t (&off)[NBC], int t, int jb) const {
+    int64_t bo = off[0];
+#pragma unroll
+    for (int u = 1; u < NBC; ++u) bo = t / BS - jb == u ? off[u] : bo;
+    return bo;
+  }
+
+  __device__ __forceinline__ void issue(const DecodeArgs& a, Buf& b, int k) {
+    if ((k >> 6) != cur_win) {
+      cur_win = k >> 6;
+#pragma unroll
+      for (int u = 0; u < NBC; ++u) win[0][u] = win[1][u];
+      load_window(a, cur_win + 1, win[1]);
+    }
+    int64_t off[NBC];
+#pragma unroll
+    for (int u = 0; u < NBC; ++u) off[u] = block_off(a, u, k);
+    const int c0 = chunk_token(k);
+    const int jb = c0 / BS;
+    // Rows at or past t_end read token c0's row instead (finite data already being
+    // fetched; their scores are excluded by select): every load is unconditional.
+#pragma unroll
+    for (int tau = 0; tau < NT; ++tau) {
+      int to = c0 + 16 * tau + li.n;  // K: lane (n, lg) loads chunks 4i + lg of token n
+      to = to < t_end ? to : c0;
+      const char* krow = kbase + tok_block(off, to, jb) + (to % BS) * RB;
+#pragma unroll
+      for (int i = 0; i < Geo::CPL; ++i) b.kr[tau][i] = load16(krow + 16 * (4 * i + li.lg));
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {  // V: instruction i covers bytes 1024 i .. of the tile's 16 rows
+        const int byte = 1024 * i + 16 * li.lane;
+        int t = c0 + 16 * tau + byte / RB;
+        t = t < t_end ? t : c0;
+        b.vt[tau].v[i] = load16(vbase + tok_block(off, t, jb) + (t % BS) * RB + byte % RB);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void trace(const DecodeArgs& a, const Buf& b, int c0) {
+    const int Hkv = a.num_kv_heads;
+    const int64_t row0 = ((int64_t)s * Hkv + g) * a.dbg_max_ctx;
+#pragma unroll
+    for (int tau = 0; tau < NT; ++tau) {
+      const int to = c0 + 16 * tau + li.n;
+      if (to < t_end) {
+#pragma unroll
+        for (int i = 0; i < Geo::CPL; ++i)
+          *(uint4*)((char*)a.dbg_k + (row0 + to) * RB + 16 * (4 * i + li.lg)) = b.kr[tau][i];
+        if (li.lg == 0) atomicAdd(a.dbg_counts + row0 + to, 1);
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int byte = 1024 * i + 16 * li.lane;
+        const int t = c0 + 16 * tau + byte / RB;
+        if (t < t_end) *(uint4*)((char*)a.dbg_v + (row0 + t) * RB + byte % RB) = b.vt[tau].v[i];
+      }
+    }
+  }
+
+  // Lanes of one wave exchange data through LDS: a wave-scope fence keeps the compiler
+  // from moving a lane's LDS reads above other lanes' writes (the hardware executes one
+  // wave's LDS instructions in order).
+  static __device__ __forceinline__ void lds_exchange() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  __device__ __forceinline__ void consume(const DecodeArgs& a, const Buf& b, int k) {
+    const int c0 = chunk_token(k);
+    if constexpr (DBG) trace(a, b, c0);
+
+    // the previous chunk's transposed reads of the tiles come before these writes
+    lds_exchange();
+#pragma unroll
+    for (int tau = 0; tau < NT; ++tau) {
+      uint16_t* vt = (uint16_t*)(lds + tau * VT_BYTES);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int byte = 1024 * i + 16 * li.lane;
+        const int t = byte / RB;
+        const int col = (byte % RB) / ElemBytes<KV>::value;
+        if constexpr (KV == kFP8) {
+          const uint4 r = b.vt[tau].v[i];
+          const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+          uint32_t packed[8];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            packed[2 * q] = fp8x2_to_mt<IO, false>(w[q]);
+            packed[2 * q + 1] = fp8x2_to_mt<IO, true>(w[q]);
+          }
+          *(uint4*)(vt + t * VT_ROW + col) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+          *(uint4*)(vt + t * VT_ROW + col + 8) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+        } else {
+          *(uint4*)(vt + t * VT_ROW + col) = b.vt[tau].v[i];
+        }
+      }
+    }
+    // the tiles are read back by other lanes of the wave (transposed)
+    lds_exchange();
+
+    // S^T: lane l gets row li.n's scores of tokens 4 lg + r of each tile (log2 units)
+    float z[NT][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tau = 0; tau < NT; ++tau) {
+      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < Geo::CPL; ++i)
+#pragma unroll
+        for (int hf = 0; hf < Geo::VEC / 8; ++hf)
+          c = Mma<IO>::mma(k_operand<IO, KV>(b.kr[tau][i], hf), qa[i * (Geo::VEC / 8) + hf], c);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = c0 + 16 * tau + 4 * li.lg + r < t_end;
+        z[tau][r] = ok ? c[r] * a.q_mul : -INFINITY;
+        mx = fmaxf(mx, z[tau][r]);
+      }
+    }
+    // the row's maximum over its four lanes
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool raise = mx > m + kLazyRescale;
+    if (__any(raise)) {
+      const float mn = raise ? mx : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      m = mn;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[dt][r] *= alpha;
+    }
+
+    // probabilities as the B operand (high and low halves), then O^T += V^T P^T
+    const int vrow = 4 * li.lg + (li.n >> 2);
+    const int vcol = 4 * (li.n & 3);
+#pragma unroll
+    for (int tau = 0; tau < NT; ++tau) {
+      v4 phi, plo;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = __builtin_amdgcn_exp2f(z[tau][r] - m);
+        l += p;
+        uint16_t hi, lo;
+        M16::split(p, hi, lo);
+        phi[r] = __builtin_bit_cast(typename std::remove_reference<decltype(phi[0])>::type, hi);
+        plo[r] = __builtin_bit_cast(typename std::remove_reference<decltype(plo[0])>::type, lo);
+      }
+      const uint16_t* vt = (const uint16_t*)(lds + tau * VT_BYTES);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const v4 av = __builtin_bit_cast(
+            v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t*)(vt + vrow * VT_ROW + 16 * dt + vcol)));
+        o[dt] = M16::mma(av, phi, o[dt]);
+        o[dt] = M16::mma(av, plo, o[dt]);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void run(const DecodeArgs& a) {
+    const int nwc = wave < len ? (len - wave + nw - 1) / nw : 0;
+    run_pipelined(*this, a, nwc);
+  }
+
+  // Row li.n < G is head li.n: its four lanes store their columns; lane lg 0 the max and sum.
+  template <int NW>
+  __device__ __forceinline__ void finish(float (&sm_m)[NW][G], float (&sm_l)[NW][G],
+                                         float (&sm_o)[NW][G][D]) {
+    float lt = l + __shfl_xor(l, 16);
+    lt += __shfl_xor(lt, 32);
+    if (li.n < G) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm_o[wave][li.n][16 * dt + 4 * li.lg + r] = o[dt][r];
+      if (li.lg == 0) {
+        sm_m[wave][li.n] = m;
+        sm_l[wave][li.n] = lt;
+      }
+    }
+  }
+};
+
 // Engine used for a shape: the V product on the matrix cores when 2 or 4 query heads
 // share a 16-bit KV head; on the vector ALUs for one query head per KV head (one FMA
 // per V element) and for fp8 KV, where widening the tile for the matrix cores costs
@@ -909,18 +1195,32 @@ struct MfmaPvEngine {
 #ifndef PA_BAL_VALU
 #define PA_BAL_VALU 1
 #endif
+#ifndef PA_T_ENGINE
+#define PA_T_ENGINE 1
+#endif
+#ifndef PA_T_TILES
+#define PA_T_TILES 1
+#endif
+#ifndef PA_T_TILES_FP8
+#define PA_T_TILES_FP8 2
+#endif
 template <int IO, int KV, int D, int BS, int G, bool DBG>
 struct EngineFor {
-  // 8 heads per KV head always take the matrix-core V product (eight FMAs per V element
-  // on the vector ALUs would bound the kernel); one head per KV head takes the vector
-  // engine (whole 1 KiB rows per wave load, no MFMA rows wasted)
-  static constexpr bool pv = (PA_MFMA_PV && (G == 2 || G == 4) && KV != kFP8) || G == 8;
+  // one head per KV head takes the vector engine (whole 1 KiB rows per wave load, no MFMA
+  // rows wasted); 2, 4 or 8 take the transposed matrix-core engine
   static constexpr bool valu = PA_BAL_VALU && G == 1;
+  static constexpr bool te = PA_T_ENGINE && (G == 2 || G == 4 || G == 8);
+  static constexpr bool pv = !te && ((PA_MFMA_PV && (G == 2 || G == 4) && KV != kFP8) || G == 8);
+  static constexpr int TNT = KV == kFP8 ? PA_T_TILES_FP8 : PA_T_TILES;
   using type = typename std::conditional<
       valu, ValuEngine<IO, KV, D, BS, G, DBG>,
-      typename std::conditional<pv, MfmaPvEngine<IO, KV, D, BS, G, DBG>,
-                                MfmaEngine<IO, KV, D, BS, G, PA_MFMA_TILES, DBG>>::type>::type;
-  static constexpr int lds_bytes = pv ? MfmaPvEngine<IO, KV, D, BS, (pv ? G : 4), DBG>::kLdsBytes : 16;
+      typename std::conditional<
+          te, MfmaTEngine<IO, KV, D, BS, (te ? G : 2), TNT, DBG>,
+          typename std::conditional<pv, MfmaPvEngine<IO, KV, D, BS, G, DBG>,
+                                    MfmaEngine<IO, KV, D, BS, G, PA_MFMA_TILES, DBG>>::type>::type>::type;
+  static constexpr int lds_bytes =
+      te ? MfmaTEngine<IO, KV, D, BS, (te ? G : 2), TNT, DBG>::kLdsBytes
+         : (pv ? MfmaPvEngine<IO, KV, D, BS, (pv ? G : 4), DBG>::kLdsBytes : 16);
 };
 
 template <class Eng> struct EngineMaker;  // builds an engine with or without its LDS tile
@@ -934,6 +1234,12 @@ template <int IO, int KV, int D, int BS, int G, bool DBG>
 struct EngineMaker<ValuEngine<IO, KV, D, BS, G, DBG>> {
   static __device__ __forceinline__ ValuEngine<IO, KV, D, BS, G, DBG> make(int lane, char*) {
     return ValuEngine<IO, KV, D, BS, G, DBG>(lane);
+  }
+};
+template <int IO, int KV, int D, int BS, int G, int NT, bool DBG>
+struct EngineMaker<MfmaTEngine<IO, KV, D, BS, G, NT, DBG>> {
+  static __device__ __forceinline__ MfmaTEngine<IO, KV, D, BS, G, NT, DBG> make(int lane, char* lds) {
+    return MfmaTEngine<IO, KV, D, BS, G, NT, DBG>(lane, lds);
   }
 };
 template <int IO, int KV, int D, int BS, int G, bool DBG>
