@@ -175,19 +175,19 @@ int pa_decode_balanced(const void* q, const void* k_pool, const void* v_pool,
                        int num_workgroups, void* workspace, size_t workspace_bytes,
                        void* out, void* stream);
 
-/* Workspace for pa_decode_ordered, in bytes (0 on invalid sizes): one int32 per
- * sequence, padded to 256 bytes. */
+/* Workspace for pa_decode_ordered, in bytes: 0, it needs none (the decode launch derives
+ * the order itself). Kept so that callers sizing a workspace for it need no change. */
 size_t pa_ordered_workspace_bytes(int num_seqs);
 
 /* Longest-first decode. Same result as pa_decode, bit for bit (the same kernels compute
- * every (KV head, sequence)); only the dispatch order differs. A first one-workgroup
- * launch sorts the sequences by context-length class (four classes per doubling of the
- * length, longest first) into the workspace; the decode launch then hands each XCD its
- * share of the (KV head, sequence) units longest sequence first, so that batches mixing
- * short and long contexts ([P2] §5.3's length mix) do not end with a few long sequences
- * running alone. Workspace: pa_ordered_workspace_bytes(num_seqs) bytes, 16-byte aligned,
- * overwritten by every call (calls sharing it must be ordered on one stream). Errors as
- * pa_decode, plus PA_ERR_WORKSPACE when the workspace is missing or too small. */
+ * every (KV head, sequence)); only the dispatch order differs. Every workgroup of the one
+ * decode launch finds its sequence by rank in the order "context-length class descending
+ * (four classes per doubling of the length), then sequence index ascending", from the
+ * context lengths alone (a class histogram and a prefix sum in LDS), and each XCD's share
+ * of the (KV head, sequence) units is handed out longest sequence first, so that batches
+ * mixing short and long contexts ([P2] §5.3's length mix) do not end with a few long
+ * sequences running alone. workspace and workspace_bytes are not used (NULL and 0 are
+ * fine). Errors as pa_decode. */
 int pa_decode_ordered(const void* q, const void* k_pool, const void* v_pool,
                       const int32_t* block_tables, const int32_t* context_lens,
                       int num_seqs, int max_blocks_per_seq, int num_blocks,

@@ -288,23 +288,19 @@ def pa_ordered_workspace_bytes(num_seqs: int) -> int:
 
 
 def ordered_workspace(q):
-    """Workspace for pa_decode_ordered (overwritten by every call)."""
-    torch = _torch()
-    need = pa_ordered_workspace_bytes(q.shape[0])
-    return torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    """Workspace for pa_decode_ordered: it needs none (the decode launch derives the order
+    itself), so this is None; kept for callers that size one."""
+    return None
 
 
 def pa_decode_ordered(q, k_pool, v_pool, block_tables, context_lens, scale: Optional[float] = None,
                       workspace=None, k_scale: float = 1.0, v_scale: float = 1.0, out=None,
                       stream=None):
-    """Longest-first paged decode (same result as pa_decode); returns out."""
+    """Longest-first paged decode (same result as pa_decode, one launch); returns out.
+    workspace is accepted and ignored (the launch needs none)."""
     args, out, _ = _common(q, k_pool, v_pool, block_tables, context_lens, scale, k_scale, v_scale, out)
-    if workspace is None:
-        workspace = ordered_workspace(q)
-    _check_dev("workspace", workspace)
-    nbytes = workspace.numel() * workspace.element_size()
     _raise("pa_decode_ordered",
-           lib().pa_decode_ordered(*args, workspace.data_ptr(), nbytes, out.data_ptr(), _stream(stream)))
+           lib().pa_decode_ordered(*args, None, 0, out.data_ptr(), _stream(stream)))
     return out
 
 
@@ -362,13 +358,8 @@ class DecodePlan:
             tail = [int(num_workgroups), workspace.data_ptr(),
                     workspace.numel() * workspace.element_size(), out.data_ptr(), st]
         elif ordered:
-            if workspace is None:
-                workspace = ordered_workspace(q)
-            _check_dev("workspace", workspace)
-            self._keep.append(workspace)
             self._fn = lib().pa_decode_ordered
-            tail = [workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                    out.data_ptr(), st]
+            tail = [None, 0, out.data_ptr(), st]
         elif max_context_len is None:
             self._fn = lib().pa_decode
             tail = [out.data_ptr(), st]

@@ -302,53 +302,6 @@ DecodeArgs base_args(const Common& c) {
   return a;
 }
 
-// Length classes of the ordered mode: four per doubling of the context length
-// (4 floor(log2 L) plus the next two bits of L), longest class dispatched first.
-constexpr int kOrderClasses = 128;
-
-__device__ __forceinline__ int length_class(int L) {
-  if (L <= 1) return 0;
-  const int e = 31 - __builtin_clz((unsigned)L);
-  const int frac = e >= 2 ? (L >> (e - 2)) & 3 : (L << (2 - e)) & 3;
-  return min(4 * e + frac, kOrderClasses - 1);
-}
-
-// Ordered mode, first launch (one workgroup): a counting sort of the sequences by length
-// class, longest class first, into order[0 .. S-1]. Within a class the order is that of
-// the atomics; it only decides when a sequence is scheduled, never what is computed.
-__global__ void __launch_bounds__(1024) order_kernel(const int32_t* context_lens, int S, int max_ctx,
-                                                     int32_t* order) {
-  __shared__ int count[kOrderClasses];
-  for (int i = threadIdx.x; i < kOrderClasses; i += blockDim.x) count[i] = 0;
-  __syncthreads();
-  for (int s = threadIdx.x; s < S; s += blockDim.x) {
-    const int L = min(max(context_lens[s], 0), max_ctx);
-    atomicAdd(&count[length_class(L)], 1);
-  }
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    // exclusive prefix sums from the longest class down, one wave: lane l takes the
-    // classes 127 - 2l and 126 - 2l
-    static_assert(kOrderClasses == 128, "two classes per lane of one wave");
-    const int lane = threadIdx.x;
-    const int c0 = count[kOrderClasses - 1 - 2 * lane];
-    const int c1 = count[kOrderClasses - 2 - 2 * lane];
-    int v = c0 + c1;
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) {
-      const int y = __shfl_up(v, k);
-      if (lane >= k) v += y;
-    }
-    const int excl = v - c0 - c1;
-    count[kOrderClasses - 1 - 2 * lane] = excl;
-    count[kOrderClasses - 2 - 2 * lane] = excl + c0;
-  }
-  __syncthreads();
-  for (int s = threadIdx.x; s < S; s += blockDim.x) {
-    const int L = min(max(context_lens[s], 0), max_ctx);
-    order[atomicAdd(&count[length_class(L)], 1)] = s;
-  }
-}
 
 // Device address of the current device's copy of `scratch`, looked up once per device
 // (with that device current) and kept.
@@ -369,8 +322,6 @@ int scratch_ptr(void** out) {
   *out = g_scratch_ptr[dev];
   return PA_OK;
 }
-
-size_t ordered_workspace_bytes(int S) { return (size_t)((((int64_t)S * 4) + 255) / 256 * 256); }
 
 int64_t num_parts_for(int max_context_len, int P) {
   const int64_t n = ((int64_t)max_context_len + P - 1) / P;
@@ -507,13 +458,8 @@ int run(const Common& c, Mode mode, int max_context_len, int P, int nwg, void* w
     return launch_pair(c.io, c.kv, ls);
   }
   if (mode == Mode::kOrdered) {
-    if (!workspace || ws_bytes < ordered_workspace_bytes(c.S)) return PA_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return PA_ERR_INVALID;
-    if ((int64_t)c.Hkv * c.S > INT_MAX) return PA_ERR_INVALID;
-    hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, st, c.cl, c.S, ls.args.max_ctx,
-                       (int32_t*)workspace);
-    if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
-    ls.args.order = (const int32_t*)workspace;
+    // the decode launch derives the longest-first order itself (no workspace)
+    ls.args.ordered = 1;
     ls.args.order_hpx = c.Hkv % 8 == 0 ? c.Hkv / 8 : 0;
   }
   const int64_t grid = (int64_t)c.Hkv * c.S * NP;
@@ -659,7 +605,8 @@ int pa_decode_balanced(const void* q, const void* k_pool, const void* v_pool,
 }
 
 size_t pa_ordered_workspace_bytes(int num_seqs) {
-  return num_seqs <= 0 ? 0 : pa::ordered_workspace_bytes(num_seqs);
+  (void)num_seqs;
+  return 0;
 }
 
 int pa_decode_ordered(const void* q, const void* k_pool, const void* v_pool,

@@ -78,7 +78,7 @@ struct DecodeArgs {
   int nwg;               // balanced mode: workgroups sharing the chunks
   float q_mul;           // scale * log2(e) (* k_scale for fp8)
   float out_mul;         // v_scale for fp8, else 1
-  const int32_t* order;  // ordered mode: sequences by descending context length, else null
+  int ordered;           // longest-first dispatch: unit ranks map to sequences by length
   int order_hpx;         // ordered mode: KV heads per XCD share of the units (0: not whole)
   int wave_parts;        // split-context streaming kernel: consecutive partitions per wave
   int wave_chunks;       // ... and runs of wave_parts partitions per (sequence, KV head)
@@ -236,20 +236,30 @@ __device__ __forceinline__ int xcd_unit(int i, int n) {
   return xcd * per + min(xcd, rem) + k;
 }
 
-// Sequence s and KV head g of unit index sg (the partition already factored out).
-// Without an order: KV-head major, sequences in index order. With an order (a
-// permutation of the sequences, longest context first): when each XCD's contiguous share
-// of the units is a whole number of KV heads (order_hpx of them), rank major inside the
-// share, so that every XCD starts its longest sequences first; else KV-head major with
-// the sequences taken by rank.
+// Length classes of the longest-first order: four per doubling of the context length
+// (4 floor(log2 L) plus the next two bits of L).
+constexpr int kOrderClasses = 128;
+
+__device__ __forceinline__ int length_class(int L) {
+  if (L <= 1) return 0;
+  const int e = 31 - __builtin_clz((unsigned)L);
+  const int frac = e >= 2 ? (L >> (e - 2)) & 3 : (L << (2 - e)) & 3;
+  return min(4 * e + frac, kOrderClasses - 1);
+}
+
+// Sequence s and KV head g of unit index sg (the partition already factored out), KV-head
+// major with the sequences in index order.
 __device__ __forceinline__ void unit_seq_head(const DecodeArgs& a, int sg, int& s, int& g) {
+  s = sg % a.num_seqs;
+  g = sg / a.num_seqs;
+}
+
+// Longest-first dispatch: rank and KV head of unit index sg. When each XCD's contiguous
+// share of the units is a whole number of KV heads (order_hpx of them), rank major inside
+// the share, so that every XCD starts its longest sequences first; else KV-head major with
+// the sequences taken by rank.
+__device__ __forceinline__ void unit_rank_head(const DecodeArgs& a, int sg, int& rank, int& g) {
   const int S = a.num_seqs;
-  if (a.order == nullptr) {
-    s = sg % S;
-    g = sg / S;
-    return;
-  }
-  int rank;
   if (a.order_hpx > 0) {
     const int per = S * a.order_hpx;
     const int blk = sg / per;
@@ -260,7 +270,92 @@ __device__ __forceinline__ void unit_seq_head(const DecodeArgs& a, int sg, int& 
     rank = sg % S;
     g = sg / S;
   }
-  s = min(max(a.order[rank], 0), S - 1);
+}
+
+// Batches up to this many sequences keep their length classes in LDS for the selection.
+constexpr int kOrderLdsSeqs = 2048;
+
+// LDS of the in-launch ordering: class counts, the result, and the classes of the batch.
+struct OrderLds {
+  int cnt[kOrderClasses];
+  int res[3];  // class, place in the class, sequence
+  unsigned char cls[kOrderLdsSeqs];
+};
+
+// The sequence of rank `rank` in the longest-first order (length class descending, then
+// sequence index ascending), found by the workgroup from the context lengths alone, so
+// every workgroup agrees on the order without a separate sorting launch: a class histogram
+// in LDS (the classes kept there too), one wave's exclusive prefix sums from the top class
+// down to find the rank's class and its place in it, then that wave walks the classes 64
+// at a time and picks the class member of that place with a ballot. Called by every thread
+// of the workgroup (it holds barriers).
+template <int NTH>
+__device__ __forceinline__ int ordered_seq(const DecodeArgs& a, int rank, OrderLds& sm) {
+  const int S = a.num_seqs;
+  const int tid = threadIdx.x;
+  const bool cached = S <= kOrderLdsSeqs;
+  for (int i = tid; i < kOrderClasses; i += NTH) sm.cnt[i] = 0;
+  __syncthreads();
+  for (int q = tid; q < S; q += NTH) {
+    const int c = length_class(min(max(a.context_lens[q], 0), a.max_ctx));
+    if (cached) sm.cls[q] = (unsigned char)c;
+    atomicAdd(&sm.cnt[c], 1);
+  }
+  __syncthreads();
+  if (tid < 64) {
+    static_assert(kOrderClasses == 128, "two classes per lane of one wave");
+    const int hi = kOrderClasses - 1 - 2 * tid;  // lane l: classes 127 - 2l and 126 - 2l
+    const int c0 = sm.cnt[hi];
+    const int c1 = sm.cnt[hi - 1];
+    int v = c0 + c1;
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) {
+      const int y = __shfl_up(v, k);
+      if (tid >= k) v += y;
+    }
+    const int excl = v - c0 - c1;
+    if (rank >= excl && rank < excl + c0) {
+      sm.res[0] = hi;
+      sm.res[1] = rank - excl;
+    } else if (rank >= excl + c0 && rank < excl + c0 + c1) {
+      sm.res[0] = hi - 1;
+      sm.res[1] = rank - excl - c0;
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int want = sm.res[0];
+    const int place = sm.res[1];
+    int seen = 0;
+    for (int base = 0; base < S; base += 64) {
+      const int q = base + tid;
+      int c = -1;
+      if (q < S) c = cached ? (int)sm.cls[q] : length_class(min(max(a.context_lens[q], 0), a.max_ctx));
+      const bool hit = c == want;
+      const unsigned long long mask = __ballot(hit);
+      const int n = __popcll(mask);
+      if (place < seen + n) {
+        if (hit && __popcll(mask & ((1ull << tid) - 1ull)) == place - seen) sm.res[2] = q;
+        break;
+      }
+      seen += n;
+    }
+  }
+  __syncthreads();
+  return sm.res[2];
+}
+
+// Sequence and KV head of unit index sg for either dispatch (every thread of the workgroup
+// calls it: the ordered form holds barriers).
+template <int NTH>
+__device__ __forceinline__ void unit_seq(const DecodeArgs& a, int sg, OrderLds& sm_ord, int& s, int& g) {
+  if (a.ordered) {
+    int rank;
+    unit_rank_head(a, sg, rank, g);
+    s = ordered_seq<NTH>(a, rank, sm_ord);
+  } else {
+    unit_seq_head(a, sg, s, g);
+  }
 }
 
 // ---------------------------------------------------------------------------------
@@ -531,11 +626,12 @@ decode_kernel(const DecodeArgs a) {
   __shared__ float sm_l[NW][G];
   __shared__ float sm_o[NW][G][D];
 
+  __shared__ OrderLds sm_ord;
   const int unit = xcd_unit((int)blockIdx.x, (int)gridDim.x);
   const int part = unit % a.num_parts;
   const int sg = unit / a.num_parts;
   int s, g;
-  unit_seq_head(a, sg, s, g);
+  unit_seq<NW * 64>(a, sg, sm_ord, s, g);
 
   constexpr int SB = Geo::SB;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -145,16 +145,15 @@ def test_ordered_rejects(over, code):
     assert L.pa_decode_ordered(*good_args(**over), FAKE, 1 << 20, FAKE, None) == code
 
 
-def test_ordered_workspace_checks():
+def test_ordered_needs_no_workspace():
+    # the longest-first decode derives its order inside the launch: no workspace, and the
+    # host checks still reject bad arguments before any HIP call
     L = _lib.lib()
-    a = good_args()
-    need = _lib.pa_ordered_workspace_bytes(4)
-    assert need == 256
-    assert _lib.pa_ordered_workspace_bytes(100) == 512
-    assert _lib.pa_ordered_workspace_bytes(0) == 0
-    assert L.pa_decode_ordered(*a, FAKE, need - 16, FAKE, None) == _lib.PA_ERR_WORKSPACE
-    assert L.pa_decode_ordered(*a, 0, need, FAKE, None) == _lib.PA_ERR_WORKSPACE
-    assert L.pa_decode_ordered(*a, FAKE + 4, need, FAKE, None) == _lib.PA_ERR_INVALID
+    assert _lib.pa_ordered_workspace_bytes(4) == 0
+    assert _lib.pa_ordered_workspace_bytes(100) == 0
+    assert L.pa_decode_ordered(*good_args(q=0), None, 0, FAKE, None) == _lib.PA_ERR_INVALID
+    assert L.pa_decode_ordered(*good_args(H=6, Hkv=4), None, 0, FAKE, None) == _lib.PA_ERR_INVALID
+    assert L.pa_decode_ordered(*good_args(D=96), None, 0, FAKE, None) == _lib.PA_ERR_UNSUPPORTED
 
 
 def test_balanced_workspace_formula():

@@ -68,19 +68,18 @@ def test_graph_replays_match_eager():
 
 
 def test_graph_replays_ordered_decode():
-    """The longest-first decode (ordering launch + decode launch) under graph capture, on
-    a mixed-length fp8 batch: every replay, with eager work in between, is bit-identical
-    to the eager call (the ordering kernel clears its counters itself, in LDS)."""
+    """The longest-first decode (one launch that derives its order in LDS) under graph
+    capture, on a mixed-length fp8 batch: every replay, with eager work in between, is
+    bit-identical to the eager call."""
     import torch
     b = W.make_batch(W.small_variant(4))
     dev = to_device(b)
     kw = dict(scale=float(b.scale), k_scale=float(b.k_scale), v_scale=float(b.v_scale))
-    ws = pa.ordered_workspace(dev["q"])
     out = torch.empty_like(dev["q"])
 
     def step(stream):
         pa.pa_decode_ordered(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"], dev["context_lens"],
-                             workspace=ws, out=out, stream=stream, **kw)
+                             out=out, stream=stream, **kw)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -94,7 +93,6 @@ def test_graph_replays_ordered_decode():
         step(torch.cuda.current_stream())
     for r in range(4):
         out.zero_()
-        ws.zero_()
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()

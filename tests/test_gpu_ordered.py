@@ -48,12 +48,41 @@ def test_ordered_mixed_lengths(H, Hkv):
     check_against_oracle(b, to_f64(outs[0]))
 
 
-def test_ordered_workspace_errors():
+def test_ordered_needs_no_workspace():
+    """The decode launch derives the order itself: a NULL workspace is accepted through the
+    C ABI and gives the bits of pa_decode."""
+    import ctypes
+
     import torch
+    from pagedattention_block_table_amd import _lib
     b = W.make_batch(W.small_variant(4))
     dev = to_device(b)
-    need = pa.pa_ordered_workspace_bytes(b.num_seqs)
-    assert need >= 4 * b.num_seqs and need % 256 == 0
-    small = torch.empty(need - 256 if need > 256 else 4, dtype=torch.uint8, device="cuda")
-    with pytest.raises(pa.PagedAttentionError):
-        run(b, dev, "ordered", workspace=small)
+    sp = b.spec
+    assert pa.pa_ordered_workspace_bytes(b.num_seqs) == 0
+    out = torch.empty_like(dev["q"])
+    rc = _lib.lib().pa_decode_ordered(
+        dev["q"].data_ptr(), dev["k_pool"].data_ptr(), dev["v_pool"].data_ptr(), dev["block_tables"].data_ptr(),
+        dev["context_lens"].data_ptr(), sp.num_seqs, b.block_tables.shape[1], b.num_blocks, sp.num_heads,
+        sp.num_kv_heads, sp.head_dim, sp.block_size, ctypes.c_float(float(b.scale)), _lib.dtype_code(dev["q"]),
+        _lib.dtype_code(dev["k_pool"]), ctypes.c_float(float(b.k_scale)), ctypes.c_float(float(b.v_scale)),
+        None, 0, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert rc == _lib.PA_OK
+    ref = run(b, dev, "direct")
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("S", [1, 63, 64, 65, 300])
+def test_ordered_rank_selection_edges(S):
+    """Batch sizes around the 64-sequence steps of the in-launch selection, all lengths in
+    one class and spread over many, each (sequence, KV head) computed exactly once (bits of
+    pa_decode)."""
+    import torch
+    for kind in (("const", 100), ("choice", (1, 16, 17, 100, 1000, 3000), (0.1, 0.1, 0.2, 0.2, 0.2, 0.2))):
+        sp = W.Spec(f"ordered_edges_{S}", S, 8, 2, 64, 16, "f16", "f16", kind, seed=300 + S)
+        b = W.make_batch(sp)
+        dev = to_device(b)
+        got = run(b, dev, "ordered")
+        ref = run(b, dev, "direct")
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), (S, kind[0])
