@@ -355,6 +355,11 @@ int default_balanced_workgroups() { return 2 * device_cus(); }
 #define PA_STREAM_WAVES_PER_CU 4
 #endif
 
+// Runs of the streaming kernel: every cps-th partition (1) or consecutive partitions (0).
+#ifndef PA_STREAM_INTERLEAVE
+#define PA_STREAM_INTERLEAVE 0
+#endif
+
 // Tokens per wave step of the vector kernel (its SB_MAX): 32, fewer for long rows.
 int vector_step_tokens(int D, int kv) {
   const int t = 8192 / (D * elem_bytes(kv));
@@ -478,6 +483,7 @@ int run(const Common& c, Mode mode, int max_context_len, int P, int nwg, void* w
     ls.stream_kernel = true;
     ls.args.wave_parts = (int)k;
     ls.args.wave_chunks = (int)chunks;
+    ls.args.wave_interleave = PA_STREAM_INTERLEAVE;
     ls.stream_waves = (int)((int64_t)c.Hkv * c.S * chunks);
   }
   rc = launch_pair(c.io, c.kv, ls);

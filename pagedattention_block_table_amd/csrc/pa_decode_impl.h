@@ -80,8 +80,9 @@ struct DecodeArgs {
   float out_mul;         // v_scale for fp8, else 1
   int ordered;           // longest-first dispatch: unit ranks map to sequences by length
   int order_hpx;         // ordered mode: KV heads per XCD share of the units (0: not whole)
-  int wave_parts;        // split-context streaming kernel: consecutive partitions per wave
-  int wave_chunks;       // ... and runs of wave_parts partitions per (sequence, KV head)
+  int wave_parts;        // split-context streaming kernel: partitions per wave (at most)
+  int wave_chunks;       // ... and runs per (sequence, KV head)
+  int wave_interleave;   // run c takes partitions c, c + wave_chunks, ... (else consecutive)
 };
 
 // ---------------------------------------------------------------------------------
@@ -568,18 +569,24 @@ struct StepWindow {
   int win[2][U];
   int cur;
   const int32_t* bt;
-  int last, j_first, j_stride;
+  int last, j_first, j_stride, spp, jump;
 
+  // first (sub-)block of step k: j_first + (k / spp) jump + (k % spp) j_stride
+  __device__ __forceinline__ int step_first(int k) const { return j_first + (k / spp) * jump + (k % spp) * j_stride; }
   __device__ __forceinline__ void load(int w, int (&dst)[U]) const {
-    const int k = 64 * w + (int)(threadIdx.x & 63);
+    const int j = step_first(64 * w + (int)(threadIdx.x & 63));
 #pragma unroll
-    for (int u = 0; u < U; ++u) dst[u] = bt[min((j_first + k * j_stride + u) / SPB, last)];
+    for (int u = 0; u < U; ++u) dst[u] = bt[min((j + u) / SPB, last)];
   }
-  __device__ __forceinline__ void begin(const int32_t* bt_row, int row_len, int j_first_, int j_stride_) {
+  // steps k at j_first + k j_stride, or, with spp > 0, groups of spp such steps jump apart
+  __device__ __forceinline__ void begin(const int32_t* bt_row, int row_len, int j_first_, int j_stride_,
+                                        int spp_ = 0, int jump_ = 0) {
     bt = bt_row;
     last = row_len - 1;
     j_first = j_first_;
     j_stride = j_stride_;
+    spp = spp_ > 0 ? spp_ : 0x7fffffff;
+    jump = jump_;
     cur = 0;
     load(0, win[0]);
     load(1, win[1]);
@@ -795,24 +802,29 @@ decode_stream_kernel(const DecodeArgs a) {
   int s, g;
   unit_seq_head(a, gw / cps, s, g);
 
+  // the run's partitions: pf, pf + ps, pf + 2 ps, ... (consecutive, or every cps-th)
   const int P = a.part_tokens;
-  const int p0 = chunk * a.wave_parts;
-  const int t0 = p0 * P;
-  const int j_begin = t0 / SB;
-  // step k starts at (sub-)block j_begin + k U; the first steps' table entries are requested
-  // together with the context length
+  const int pf = a.wave_interleave ? chunk : chunk * a.wave_parts;
+  const int ps = a.wave_interleave ? cps : 1;
+  const int spp = P / ST;  // steps per partition
+  const int psb = P / SB;  // (sub-)blocks per partition
+  // step k starts at (sub-)block (pf + (k / spp) ps) psb + (k % spp) U; the first steps'
+  // table entries are requested together with the context length
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   StepWindow<U, Geo::SPB> tw;
-  tw.begin(bt, a.max_blocks_per_seq, j_begin, U);
+  tw.begin(bt, a.max_blocks_per_seq, pf * psb, U, spp, ps * psb);
 
   int L = a.context_lens[s];
   L = min(max(L, 0), a.max_ctx);
-  if (chunk > 0 && t0 >= L) return;  // nothing in this run
-  const int t_stop = min(L, t0 + a.wave_parts * P);
+  if (chunk > 0 && pf * P >= L) return;  // nothing in this run
   const int n_parts_s = (L + P - 1) / P;
   const bool write_out = n_parts_s <= 1;
-  const int spp = P / ST;                        // steps per partition
-  const int nsteps = (t_stop - t0 + ST - 1) / ST;
+  // partitions of the run inside the context, and the steps of its last one
+  const int n_run = a.wave_interleave ? (n_parts_s > pf ? (n_parts_s - pf + ps - 1) / ps : 0)
+                                      : min(a.wave_parts, n_parts_s - pf);
+  const int p_last = pf + (max(n_run, 1) - 1) * ps;
+  const int last_steps = (min(L, (p_last + 1) * P) - p_last * P + ST - 1) / ST;
+  const int nsteps = n_run > 0 ? (n_run - 1) * spp + last_steps : 0;
 
   const int lane = threadIdx.x & 63;
   const int r = lane / LPT;
@@ -872,7 +884,7 @@ decode_stream_kernel(const DecodeArgs a) {
   };
   reset();
   if (nsteps <= 0) {  // empty sequence: its output is zero
-    finish(p0);
+    finish(pf);
     return;
   }
 
@@ -881,7 +893,7 @@ decode_stream_kernel(const DecodeArgs a) {
   const char* vbase = (const char*)a.v_pool + (int64_t)g * Geo::TILE;
 
   using Buf = StepBuf<KV, D, BS, G, U>;
-  auto j0_of = [&](int k) { return j_begin + min(k, nsteps - 1) * U; };
+  auto j0_of = [&](int k) { return tw.step_first(min(k, nsteps - 1)); };
   auto consume = [&](const Buf& b, int k) {
     const int j0 = j0_of(k);
     if ((j0 + U) * SB <= L) {
@@ -893,7 +905,7 @@ decode_stream_kernel(const DecodeArgs a) {
   // after step k's successor loads are issued: close the partition if step k ended it
   auto close = [&](int k) {
     if ((k + 1) % spp == 0 || k + 1 == nsteps) {
-      finish(p0 + k / spp);
+      finish(pf + (k / spp) * ps);
       reset();
     }
   };
