@@ -544,6 +544,7 @@ struct MfmaEngine {
 // 16x16x32 product.
 template <int MT> struct Mma16;
 template <> struct Mma16<kF16> {
+  typedef _Float16 elem;
   typedef _Float16 v4 __attribute__((ext_vector_type(4)));
   static __device__ __forceinline__ f32x4_t mma(const v4& a, const v4& b, const f32x4_t& c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
@@ -556,6 +557,7 @@ template <> struct Mma16<kF16> {
   }
 };
 template <> struct Mma16<kBF16> {
+  typedef short elem;
   typedef short v4 __attribute__((ext_vector_type(4)));
   static __device__ __forceinline__ f32x4_t mma(const v4& a, const v4& b, const f32x4_t& c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -957,11 +959,19 @@ struct MfmaTEngine {
   static constexpr int TILE_BYTES = BS * RB;
   static constexpr int NDT = D / 16;
   static constexpr int NV = VTileRegs<KV, D>::NV;  // V loads per lane per 16-token tile
-  static constexpr int VT_ROW = D + 16;             // 16-bit elements per LDS tile row (32 B pad)
+  // 16-bit elements per LDS tile row: rows padded by 32 B spread the transposed reads of
+  // four rows over the banks (other pads measured the same or worse for fp8 KV)
+  static constexpr int VT_ROW = D + 16;
   static constexpr int VT_BYTES = 16 * VT_ROW * 2;
+  // Type of the V product. bf16 V keeps bf16 with the probabilities split into a high and
+  // a low half (fp32 accuracy). f16 V, and fp8 V widened to f16 (exact: every e4m3 value is
+  // an f16 value), take the probabilities rounded to f16 in one product: relative error at
+  // most 2^-12 per weight, below 1.2e-3 of the largest |V| in the output.
+  static constexpr int PVT = KV == kBF16 ? kBF16 : kF16;
+  static constexpr bool SPLIT_P = PVT == kBF16;
   static constexpr int kLdsBytes = NT * VT_BYTES;
   using vec = typename Mma<IO>::vec;
-  using M16 = Mma16<IO>;
+  using M16 = Mma16<PVT>;
   using v4 = typename M16::v4;
   static_assert(G == 2 || G == 4 || G == 8, "group");
   static_assert(mfma_supported<IO, KV, D, G>(), "unsupported MFMA decode geometry");
@@ -1125,8 +1135,8 @@ struct MfmaTEngine {
           uint32_t packed[8];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            packed[2 * q] = fp8x2_to_mt<IO, false>(w[q]);
-            packed[2 * q + 1] = fp8x2_to_mt<IO, true>(w[q]);
+            packed[2 * q] = fp8x2_to_mt<PVT, false>(w[q]);
+            packed[2 * q + 1] = fp8x2_to_mt<PVT, true>(w[q]);
           }
           *(uint4*)(vt + t * VT_ROW + col) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
           *(uint4*)(vt + t * VT_ROW + col + 8) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
@@ -1170,9 +1180,10 @@ struct MfmaTEngine {
         for (int r = 0; r < 4; ++r) o[dt][r] *= alpha;
     }
 
-    // probabilities as the B operand (high and low halves), then O^T += V^T P^T
+    // probabilities as the B operand (bf16: high and low halves), then O^T += V^T P^T
     const int vrow = 4 * li.lg + (li.n >> 2);
     const int vcol = 4 * (li.n & 3);
+    using elem = typename M16::elem;
 #pragma unroll
     for (int tau = 0; tau < NT; ++tau) {
       v4 phi, plo;
@@ -1180,10 +1191,14 @@ struct MfmaTEngine {
       for (int r = 0; r < 4; ++r) {
         const float p = __builtin_amdgcn_exp2f(z[tau][r] - m);
         l += p;
-        uint16_t hi, lo;
-        M16::split(p, hi, lo);
-        phi[r] = __builtin_bit_cast(typename std::remove_reference<decltype(phi[0])>::type, hi);
-        plo[r] = __builtin_bit_cast(typename std::remove_reference<decltype(plo[0])>::type, lo);
+        if constexpr (SPLIT_P) {
+          uint16_t hi, lo;
+          M16::split(p, hi, lo);
+          phi[r] = __builtin_bit_cast(elem, hi);
+          plo[r] = __builtin_bit_cast(elem, lo);
+        } else {
+          phi[r] = (_Float16)p;
+        }
       }
       const uint16_t* vt = (const uint16_t*)(lds + tau * VT_BYTES);
 #pragma unroll
@@ -1192,7 +1207,7 @@ struct MfmaTEngine {
             v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) i16x4_t*)(vt + vrow * VT_ROW + 16 * dt + vcol)));
         o[dt] = M16::mma(av, phi, o[dt]);
-        o[dt] = M16::mma(av, plo, o[dt]);
+        if constexpr (SPLIT_P) o[dt] = M16::mma(av, plo, o[dt]);
       }
     }
   }
