@@ -45,10 +45,12 @@ HEADLINE_CONFIG = 3
 DEFAULT_MODE = {0: "direct", 1: "ordered", 2: "direct", 3: "partitioned", 4: "ordered",
                 "llama7b_fp16_bs128": "direct", "shared_prefix_bf16_bs256": "direct",
                 "long_ctx_fp16_bs512": "ordered", "mixed_fp8_bs256": "ordered",
-                "llama70b_gqa8_bf16": "ordered", "d256_gqa2_bf16": "direct"}
+                "llama70b_gqa8_bf16": "ordered", "d256_gqa2_bf16": "direct",
+                "shared_prefix_long_bf16": "grouped"}
 SUB_CONFIGS = (1, 2, 4)
 KERNEL_SOURCES = ["pagedattention_block_table_amd/csrc/pa_decode_impl.h",
                   "pagedattention_block_table_amd/csrc/pa_mfma_decode.h",
+                  "pagedattention_block_table_amd/csrc/pa_group_decode.h",
                   "pagedattention_block_table_amd/csrc/pa_api.hip"]
 KV_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
 IO_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
@@ -215,6 +217,9 @@ class DeviceBatch:
                                  num_workgroups=workgroups, **kw)
         if mode == "ordered":
             return pa.DecodePlan(self.q, self.ks[0], self.vs[0], self.bt, self.cl, ordered=True, **kw)
+        if mode == "grouped":
+            return pa.DecodePlan(self.q, self.ks[0], self.vs[0], self.bt, self.cl, grouped=True,
+                                 num_splits=workgroups, **kw)
         return pa.DecodePlan(self.q, self.ks[0], self.vs[0], self.bt, self.cl,
                              max_context_len=max(b.max_context_len, 1), partition_size=P, **kw)
 
@@ -283,6 +288,8 @@ def graph_replay(torch, pa, db: DeviceBatch, mode, P, workgroups, steps):
             ws = pa.balanced_workspace(db.q, db.ks[0], workgroups)
         elif mode == "ordered":
             ws = pa.ordered_workspace(db.q)
+        elif mode == "grouped":
+            ws = pa.grouped_workspace(db.q, db.ks[0], workgroups)
         elif mode == "partitioned":
             sp = b.spec
             need = pa.pa_partitioned_workspace_bytes(sp.num_seqs, sp.num_heads, sp.head_dim,
@@ -508,10 +515,12 @@ def main():
     ap.add_argument("--workload", default="",
                     help="a named variant of a config (larger blocks) or an extend workload "
                          "(extend_*), instead of --config")
-    ap.add_argument("--mode", default="auto", choices=["auto", "direct", "partitioned", "balanced", "ordered"])
+    ap.add_argument("--mode", default="auto", choices=["auto", "direct", "partitioned", "balanced", "ordered",
+                                                    "grouped"])
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--workgroups", type=int, default=0,
-                    help="balanced mode: workgroup count (0 = library default)")
+                    help="balanced mode: workgroup count; grouped mode: splits per group "
+                         "(0 = library default)")
     ap.add_argument("--replica-bytes", type=float, default=2 * 2**30)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -629,6 +638,7 @@ def main():
         "config": {"workload": sp.name, "mode": mode,
                    "partition_size": P if mode == "partitioned" else None,
                    "workgroups": (args.workgroups or "library default") if mode == "balanced" else None,
+                   "splits": (args.workgroups or "library default") if mode == "grouped" else None,
                    "num_seqs": sp.num_seqs, "num_heads": sp.num_heads,
                    "num_kv_heads": sp.num_kv_heads, "head_dim": sp.head_dim,
                    "block_size": sp.block_size, "io_dtype": sp.io_dtype, "kv_dtype": sp.kv_dtype,

@@ -195,6 +195,40 @@ int pa_decode_ordered(const void* q, const void* k_pool, const void* v_pool,
                       float scale, int io_dtype, int kv_dtype, float k_scale, float v_scale,
                       void* workspace, size_t workspace_bytes, void* out, void* stream);
 
+/* Workspace for pa_decode_grouped, in bytes (0 when none is needed or on invalid sizes):
+ * fp32 partial states (running maximum, exp-sum, head_dim partial outputs) for every
+ * (sequence, query head) and split, when the call runs more than one split. num_splits 0
+ * means the library's choice (about two workgroups per compute unit of the current device,
+ * at most 16). */
+size_t pa_grouped_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                  int num_splits);
+
+/* Shared-prefix decode. Same result as pa_decode up to rounding order. Sequences whose
+ * block tables name the same physical blocks (a shared prompt, [P1] §2 and §5: shared
+ * blocks with reference counts; parallel samples of one prompt) read each shared block
+ * once per KV head: a workgroup takes one KV head and a group of 16 / G consecutive
+ * sequences (G = num_heads / num_kv_heads, 2, 4 or 8), walks their block tables side by
+ * side, and runs the scores and the value products of one physical block for all group
+ * members that name it at the same logical position together, on the matrix cores
+ * (16 query rows = the members' query heads). Blocks a member does not share are read
+ * for it alone. A group's logical blocks are cut in num_splits interleaved parts (0 =
+ * library choice) run by separate workgroups; with more than one split a second launch
+ * merges the parts by log-sum-exp weighting ([P2] §3.3 / §4.1), using the workspace
+ * (pa_grouped_workspace_bytes(...) bytes, 16-byte aligned; NULL allowed when that is 0).
+ * Sharing is found only between sequences of one group (consecutive indices) at equal
+ * logical block positions: order a batch so that sequences with a common prefix are
+ * adjacent. Shapes the grouped kernel does not take run the single-pass kernel of
+ * pa_decode instead (same result; workspace unused): G not in {2, 4, 8}, fp32 io or KV,
+ * head_dim above 128, token rows (head_dim times the KV element size) that are not a
+ * multiple of 128 bytes, block_size below 16. */
+int pa_decode_grouped(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      int num_seqs, int max_blocks_per_seq, int num_blocks,
+                      int num_heads, int num_kv_heads, int head_dim, int block_size,
+                      float scale, int io_dtype, int kv_dtype, float k_scale, float v_scale,
+                      int num_splits, void* workspace, size_t workspace_bytes,
+                      void* out, void* stream);
+
 /* Instrumented decode for tests ([P1] §2 block-table reading; every cached position
  * is read exactly once). Runs the same kernels as pa_decode (partition_size == 0 and
  * num_workgroups == 0), pa_decode_partitioned (partition_size > 0, workspace required) or
@@ -213,6 +247,21 @@ int pa_debug_trace(const void* q, const void* k_pool, const void* v_pool,
                    int max_context_len, int partition_size, int num_workgroups,
                    void* workspace, size_t workspace_bytes, void* out,
                    void* k_rows, void* v_rows, int32_t* read_counts, void* stream);
+
+/* Instrumented pa_decode_grouped for tests: the trace of pa_debug_trace (k_rows, v_rows,
+ * read_counts, per (sequence, KV head, token) consumed), and in addition
+ *   adds 1 to block_reads[b * num_kv_heads + g]
+ * for every load of 16 cached rows of physical block b for KV head g, however many
+ * sequences of the group use that load. block_reads [num_blocks][num_kv_heads] int32 must
+ * be zeroed by the caller. PA_ERR_UNSUPPORTED for shapes the grouped kernel does not take. */
+int pa_debug_trace_grouped(const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int num_seqs, int max_blocks_per_seq, int num_blocks,
+                           int num_heads, int num_kv_heads, int head_dim, int block_size,
+                           float scale, int io_dtype, int kv_dtype, float k_scale, float v_scale,
+                           int max_context_len, int num_splits, void* workspace,
+                           size_t workspace_bytes, void* out, void* k_rows, void* v_rows,
+                           int32_t* read_counts, int32_t* block_reads, void* stream);
 
 /* Appends new tokens' keys and values to the paged cache ([P1] §2 block table; [P3]
  * paged pool: a growing request writes into its last block and gets blocks appended;

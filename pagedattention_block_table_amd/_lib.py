@@ -35,6 +35,9 @@ SIGNATURES = {
     "pa_decode_partitioned_noalloc": (_I, _DECODE_ARGS + [_I, _I, _P, _P]),
     "pa_balanced_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "pa_decode_balanced": (_I, _DECODE_ARGS + [_I, _P, _SZ, _P, _P]),
+    "pa_grouped_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "pa_decode_grouped": (_I, _DECODE_ARGS + [_I, _P, _SZ, _P, _P]),
+    "pa_debug_trace_grouped": (_I, _DECODE_ARGS + [_I, _I, _P, _SZ, _P, _P, _P, _P, _P, _P]),
     "pa_ordered_workspace_bytes": (_SZ, [_I]),
     "pa_decode_ordered": (_I, _DECODE_ARGS + [_P, _SZ, _P, _P]),
     "pa_debug_trace": (_I, _DECODE_ARGS + [_I, _I, _I, _P, _SZ, _P, _P, _P, _P, _P]),
@@ -283,6 +286,58 @@ def pa_decode_balanced(q, k_pool, v_pool, block_tables, context_lens, scale: Opt
     return out
 
 
+def pa_grouped_workspace_bytes(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                               num_splits: int = 0) -> int:
+    return int(lib().pa_grouped_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                num_splits))
+
+
+def grouped_workspace(q, k_pool, num_splits: int = 0):
+    """Workspace for pa_decode_grouped (None when the call needs none)."""
+    torch = _torch()
+    S, H, D = q.shape
+    need = pa_grouped_workspace_bytes(S, H, k_pool.shape[1], D, num_splits)
+    return torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+
+
+def pa_decode_grouped(q, k_pool, v_pool, block_tables, context_lens, scale: Optional[float] = None,
+                      num_splits: int = 0, workspace=None, k_scale: float = 1.0,
+                      v_scale: float = 1.0, out=None, stream=None):
+    """Shared-prefix paged decode: blocks shared by consecutive sequences are read once per
+    group and KV head (same result as pa_decode up to rounding order); returns out."""
+    args, out, _ = _common(q, k_pool, v_pool, block_tables, context_lens, scale, k_scale, v_scale, out)
+    if workspace is None:
+        workspace = grouped_workspace(q, k_pool, num_splits)
+    ptr, nbytes = None, 0
+    if workspace is not None:
+        _check_dev("workspace", workspace)
+        ptr, nbytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _raise("pa_decode_grouped",
+           lib().pa_decode_grouped(*args, int(num_splits), ptr, nbytes, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def pa_debug_trace_grouped(q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
+                           scale: Optional[float] = None, num_splits: int = 0, k_scale: float = 1.0,
+                           v_scale: float = 1.0, stream=None):
+    """Instrumented grouped decode; returns (out, k_rows, v_rows, read_counts, block_reads)."""
+    torch = _torch()
+    args, out, (S, H, D, NB, Hkv, BS, MB) = _common(q, k_pool, v_pool, block_tables, context_lens,
+                                                   scale, k_scale, v_scale, None)
+    workspace = grouped_workspace(q, k_pool, num_splits)
+    ptr = workspace.data_ptr() if workspace is not None else None
+    nbytes = workspace.numel() if workspace is not None else 0
+    k_rows = torch.zeros((S, Hkv, max_context_len, D), dtype=k_pool.dtype, device=q.device)
+    v_rows = torch.zeros_like(k_rows)
+    counts = torch.zeros((S, Hkv, max_context_len), dtype=torch.int32, device=q.device)
+    block_reads = torch.zeros((NB, Hkv), dtype=torch.int32, device=q.device)
+    _raise("pa_debug_trace_grouped",
+           lib().pa_debug_trace_grouped(*args, int(max_context_len), int(num_splits), ptr, nbytes,
+                                        out.data_ptr(), k_rows.data_ptr(), v_rows.data_ptr(),
+                                        counts.data_ptr(), block_reads.data_ptr(), _stream(stream)))
+    return out, k_rows, v_rows, counts, block_reads
+
+
 def pa_ordered_workspace_bytes(num_seqs: int) -> int:
     return int(lib().pa_ordered_workspace_bytes(num_seqs))
 
@@ -341,7 +396,7 @@ class DecodePlan:
                  k_scale: float = 1.0, v_scale: float = 1.0, out=None,
                  max_context_len: Optional[int] = None, partition_size: int = 0,
                  workspace=None, stream=None, balanced: bool = False, num_workgroups: int = 0,
-                 ordered: bool = False):
+                 ordered: bool = False, grouped: bool = False, num_splits: int = 0):
         torch = _torch()
         args, out, (S, H, D, *_r) = _common(q, k_pool, v_pool, block_tables, context_lens,
                                             scale, k_scale, v_scale, out)
@@ -360,6 +415,16 @@ class DecodePlan:
         elif ordered:
             self._fn = lib().pa_decode_ordered
             tail = [None, 0, out.data_ptr(), st]
+        elif grouped:
+            if workspace is None:
+                workspace = grouped_workspace(q, k_pool, num_splits)
+            ptr, nbytes = None, 0
+            if workspace is not None:
+                _check_dev("workspace", workspace)
+                self._keep.append(workspace)
+                ptr, nbytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+            self._fn = lib().pa_decode_grouped
+            tail = [int(num_splits), ptr, nbytes, out.data_ptr(), st]
         elif max_context_len is None:
             self._fn = lib().pa_decode
             tail = [out.data_ptr(), st]

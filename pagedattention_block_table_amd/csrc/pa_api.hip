@@ -36,6 +36,7 @@ struct MergeArgs {
   int num_parts;
   int part_tokens;
   int max_ctx;
+  int fixed_parts;  // > 0: every sequence has this many partial states (grouped splits)
 };
 
 // Log-sum-exp merge of the partitions of one (sequence, head) per workgroup ([P2] §3.3 /
@@ -59,8 +60,8 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(const MergeArgs a)
   const int s = pair / a.num_heads;
   int L = a.context_lens[s];
   L = min(max(L, 0), a.max_ctx);
-  const int n = (L + a.part_tokens - 1) / a.part_tokens;
-  if (n <= 1) return;  // written directly by the decode kernel (whole workgroup)
+  const int n = a.fixed_parts > 0 ? a.fixed_parts : (L + a.part_tokens - 1) / a.part_tokens;
+  if (a.fixed_parts == 0 && n <= 1) return;  // written directly by the decode kernel (whole workgroup)
   const int64_t NPH = (int64_t)a.num_seqs * a.num_heads * a.num_parts;
   const float* m = a.ws + (int64_t)pair * a.num_parts;
   const float* l = a.ws + NPH + (int64_t)pair * a.num_parts;
@@ -123,11 +124,13 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(const MergeArgs a)
       x.w += y.w;
       dsum += sm_den[k][t];
     }
+    // dsum is 0 only when every state is empty (a context of length 0); x is 0 then too
+    const float d = dsum > 0.f ? dsum : 1.f;
     const int64_t base = (int64_t)pair * D + 4 * t;
-    store_io<IO>(a.out, base + 0, x.x / dsum);
-    store_io<IO>(a.out, base + 1, x.y / dsum);
-    store_io<IO>(a.out, base + 2, x.z / dsum);
-    store_io<IO>(a.out, base + 3, x.w / dsum);
+    store_io<IO>(a.out, base + 0, x.x / d);
+    store_io<IO>(a.out, base + 1, x.y / d);
+    store_io<IO>(a.out, base + 2, x.z / d);
+    store_io<IO>(a.out, base + 3, x.w / d);
   }
 }
 
@@ -405,12 +408,37 @@ BalancedLayout balanced_layout(int S, int H, int Hkv, int D, int nwg) {
   return b;
 }
 
-enum class Mode { kSingle, kPartitioned, kBalanced, kOrdered };
+// Shapes of the grouped (shared-prefix) kernel: 2, 4 or 8 query heads per KV head on the
+// matrix cores (16-bit io, KV of the io type or fp8, head_dim <= 128, token rows of a
+// multiple of 128 bytes) and blocks of at least 16 tokens.
+bool grouped_shape(const Common& c) {
+  const int g = c.H / c.Hkv;
+  const int row = c.D * elem_bytes(c.kv);
+  return (g == 2 || g == 4 || g == 8) && (c.io == PA_F16 || c.io == PA_BF16) &&
+         (c.kv == c.io || c.kv == PA_FP8_E4M3) && c.D <= 128 && row >= 128 && row % 128 == 0 && c.BS >= 16;
+}
+
+// Splits of each (KV head, group) for the grouped kernel: num_splits, or for 0 as many as
+// give about two workgroups per compute unit (at most 16).
+int grouped_splits(int S, int H, int Hkv, int num_splits) {
+  if (num_splits > 0) return num_splits;
+  const int64_t ng = 16 / (H / Hkv);
+  const int64_t units = (int64_t)Hkv * ((S + ng - 1) / ng);
+  const int64_t want = (2 * (int64_t)device_cus() + units - 1) / units;
+  return (int)(want < 1 ? 1 : (want > 16 ? 16 : want));
+}
+
+size_t grouped_workspace_bytes(int S, int H, int D, int nsplit) {
+  return nsplit <= 1 ? 0 : (size_t)((int64_t)S * H * nsplit * (D + 2) * 4);
+}
+
+enum class Mode { kSingle, kPartitioned, kBalanced, kOrdered, kGrouped };
 
 // Shared body of every entry point. P is the partition size (partitioned mode), nwg the
 // workgroup count (balanced mode).
 int run(const Common& c, Mode mode, int max_context_len, int P, int nwg, void* workspace,
-        size_t ws_bytes, void* dk, void* dv, int32_t* dcounts, bool debug, hipStream_t st) {
+        size_t ws_bytes, void* dk, void* dv, int32_t* dcounts, bool debug, hipStream_t st,
+        int32_t* dblock_reads = nullptr) {
   int rc = validate(c);
   if (rc != PA_OK) return rc;
   LaunchSpec ls{};
@@ -422,6 +450,7 @@ int run(const Common& c, Mode mode, int max_context_len, int P, int nwg, void* w
   ls.stream = st;
   const int cap = c.MB * c.BS;  // a table row covers at most this many tokens
   if (mode == Mode::kBalanced && !balanced_shape(c)) mode = Mode::kSingle;  // same result
+  if (mode == Mode::kGrouped && !grouped_shape(c)) mode = Mode::kSingle;    // same result
   int64_t NP = 1;
   if (mode == Mode::kPartitioned) {
     if (max_context_len < 0) return PA_ERR_INVALID;
@@ -446,6 +475,7 @@ int run(const Common& c, Mode mode, int max_context_len, int P, int nwg, void* w
     ls.args.dbg_k = dk;
     ls.args.dbg_v = dv;
     ls.args.dbg_counts = dcounts;
+    ls.args.dbg_block_reads = dblock_reads;
     ls.args.dbg_max_ctx = max_context_len;
     if (ls.args.max_ctx > max_context_len) ls.args.max_ctx = max_context_len;
   }
@@ -461,6 +491,33 @@ int run(const Common& c, Mode mode, int max_context_len, int P, int nwg, void* w
     ls.balanced = true;
     ls.grid = nwg;
     return launch_pair(c.io, c.kv, ls);
+  }
+  if (mode == Mode::kGrouped) {
+    const int nsplit = grouped_splits(c.S, c.H, c.Hkv, nwg);
+    const int64_t ng = 16 / (c.H / c.Hkv);
+    const int64_t grid = (int64_t)c.Hkv * ((c.S + ng - 1) / ng) * nsplit;
+    if (grid > INT_MAX) return PA_ERR_INVALID;
+    if (nsplit > 1) {
+      if (!workspace || ws_bytes < grouped_workspace_bytes(c.S, c.H, c.D, nsplit)) return PA_ERR_WORKSPACE;
+      if (!aligned16(workspace)) return PA_ERR_INVALID;
+    }
+    ls.args.ws = (float*)workspace;
+    ls.args.num_parts = nsplit;
+    ls.grouped = true;
+    ls.grid = (int)grid;
+    rc = launch_pair(c.io, c.kv, ls);
+    if (rc != PA_OK || nsplit <= 1) return rc;
+    MergeArgs m{};
+    m.ws = (const float*)workspace;
+    m.context_lens = c.cl;
+    m.out = c.out;
+    m.num_seqs = c.S;
+    m.num_heads = c.H;
+    m.num_parts = nsplit;
+    m.part_tokens = 1;
+    m.max_ctx = ls.args.max_ctx;
+    m.fixed_parts = nsplit;
+    return launch_merge(c.io, c.D, m, c.S * c.H, st);
   }
   if (mode == Mode::kOrdered) {
     // the decode launch derives the longest-first order itself (no workspace)
@@ -605,6 +662,61 @@ int pa_decode_balanced(const void* q, const void* k_pool, const void* v_pool,
                  kv_dtype, k_scale, v_scale, out};
     return pa::run(c, pa::Mode::kBalanced, -1, 0, num_workgroups, workspace, workspace_bytes,
                    nullptr, nullptr, nullptr, false, (hipStream_t)stream);
+  } catch (...) {
+    return PA_ERR_LAUNCH;
+  }
+}
+
+size_t pa_grouped_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                  int num_splits) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_splits < 0 ||
+      num_heads % num_kv_heads != 0)
+    return 0;
+  try {
+    const int G = num_heads / num_kv_heads;
+    if (G != 2 && G != 4 && G != 8) return 0;
+    const int nsplit = pa::grouped_splits(num_seqs, num_heads, num_kv_heads, num_splits);
+    return pa::grouped_workspace_bytes(num_seqs, num_heads, head_dim, nsplit);
+  } catch (...) {
+    return 0;
+  }
+}
+
+int pa_decode_grouped(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                      const int32_t* context_lens, int num_seqs, int max_blocks_per_seq, int num_blocks,
+                      int num_heads, int num_kv_heads, int head_dim, int block_size, float scale, int io_dtype,
+                      int kv_dtype, float k_scale, float v_scale, int num_splits, void* workspace,
+                      size_t workspace_bytes, void* out, void* stream) {
+  try {
+    if (num_splits < 0) return PA_ERR_INVALID;
+    pa::Common c{q, k_pool, v_pool, block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                 num_blocks, num_heads, num_kv_heads, head_dim, block_size, scale, io_dtype,
+                 kv_dtype, k_scale, v_scale, out};
+    return pa::run(c, pa::Mode::kGrouped, -1, 0, num_splits, workspace, workspace_bytes, nullptr, nullptr,
+                   nullptr, false, (hipStream_t)stream);
+  } catch (...) {
+    return PA_ERR_LAUNCH;
+  }
+}
+
+int pa_debug_trace_grouped(const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                           int max_blocks_per_seq, int num_blocks, int num_heads, int num_kv_heads,
+                           int head_dim, int block_size, float scale, int io_dtype, int kv_dtype,
+                           float k_scale, float v_scale, int max_context_len, int num_splits,
+                           void* workspace, size_t workspace_bytes, void* out, void* k_rows,
+                           void* v_rows, int32_t* read_counts, int32_t* block_reads, void* stream) {
+  try {
+    if (num_splits < 0) return PA_ERR_INVALID;
+    pa::Common c{q, k_pool, v_pool, block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                 num_blocks, num_heads, num_kv_heads, head_dim, block_size, scale, io_dtype,
+                 kv_dtype, k_scale, v_scale, out};
+    const int rc = pa::validate(c);
+    if (rc != PA_OK) return rc;
+    if (!pa::grouped_shape(c)) return PA_ERR_UNSUPPORTED;
+    if (!block_reads) return PA_ERR_INVALID;
+    return pa::run(c, pa::Mode::kGrouped, max_context_len, 0, num_splits, workspace, workspace_bytes,
+                   k_rows, v_rows, read_counts, true, (hipStream_t)stream, block_reads);
   } catch (...) {
     return PA_ERR_LAUNCH;
   }

@@ -65,6 +65,7 @@ struct DecodeArgs {
   void* dbg_k;           // debug: raw K rows [S][Hkv][dbg_max_ctx][D]
   void* dbg_v;
   int32_t* dbg_counts;   // debug: [S][Hkv][dbg_max_ctx]
+  int32_t* dbg_block_reads;  // debug (grouped kernel): 16-token loads per [block][Hkv], or null
   int num_seqs;
   int max_blocks_per_seq;
   int num_blocks;
@@ -1029,6 +1030,7 @@ struct ValuEngine {
 }  // namespace pa
 
 #include "pa_mfma_decode.h"
+#include "pa_group_decode.h"
 
 namespace pa {
 
@@ -1040,6 +1042,7 @@ struct LaunchSpec {
   int group;
   bool debug;
   bool balanced;   // balanced_decode_kernel (MFMA shapes only)
+  bool grouped;        // grouped_decode_kernel (shared prefixes; grid = Hkv x groups x splits)
   bool stream_kernel;  // split-context: the streaming kernel if the shape takes the vector kernel
   int stream_waves;    // its grid, in waves
   int grid;            // units (workgroups of the balanced kernel)
@@ -1082,6 +1085,20 @@ int launch_one(const LaunchSpec& ls) {
         } else {
           hipLaunchKernelGGL((balanced_decode_kernel<IO, KV, D, BS, G, NW, false>), dim3(ls.grid),
                              dim3(NW * 64), 0, ls.stream, ls.args);
+        }
+        return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+      } else {
+        return PA_ERR_UNSUPPORTED;
+      }
+    }
+    if (ls.grouped) {
+      if constexpr (GroupShape<IO, KV, D, BS, G, NW, false>::ok) {
+        if (ls.debug) {
+          hipLaunchKernelGGL((grouped_decode_kernel<IO, KV, D, BS, G, NW, true>), dim3(ls.grid), dim3(NW * 64), 0,
+                             ls.stream, ls.args);
+        } else {
+          hipLaunchKernelGGL((grouped_decode_kernel<IO, KV, D, BS, G, NW, false>), dim3(ls.grid), dim3(NW * 64), 0,
+                             ls.stream, ls.args);
         }
         return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
       } else {

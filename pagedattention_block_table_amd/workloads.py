@@ -114,6 +114,10 @@ VARIANTS = {
     # head_dim 256 (16 query heads over 8 KV heads, bf16, 32 requests of 0.5K-2K tokens)
     "d256_gqa2_bf16": Spec("d256_gqa2_bf16", 32, 16, 8, 256, 16, "bf16", "bf16",
                            ("uniform_sum", ((512, 2048),)), seed=1006),
+    # the prefix-caching shape with a long shared prompt: 64 requests share an 8000-token
+    # prefix (~33 MB of K/V, more than the chip's L2) and hold 500 private tokens each
+    "shared_prefix_long_bf16": CONFIGS[2].replace(name="shared_prefix_long_bf16", lengths=("const", 8500),
+                                                  shared_prefix=8000, seed=1007),
 }
 
 

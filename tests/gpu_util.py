@@ -38,8 +38,13 @@ def to_device(b, device="cuda"):
 def run(b, dev, mode="direct", partition_size=None, stream=None, num_workgroups=0, workspace=None):
     """HIP decode of a batch; returns the output tensor (io dtype, on the device).
     mode: "direct" (pa_decode), "partitioned" (partition_size), "balanced"
-    (num_workgroups, 0 = library default) or "ordered" (pa_decode_ordered)."""
+    (num_workgroups, 0 = library default), "ordered" (pa_decode_ordered) or "grouped"
+    (pa_decode_grouped, num_workgroups = number of splits, 0 = library default)."""
     kw = dict(scale=float(b.scale), k_scale=float(b.k_scale), v_scale=float(b.v_scale), stream=stream)
+    if mode == "grouped":
+        return pa.pa_decode_grouped(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"],
+                                    dev["context_lens"], num_splits=num_workgroups,
+                                    workspace=workspace, **kw)
     if mode == "direct":
         return pa.pa_decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"],
                             dev["context_lens"], **kw)

@@ -156,6 +156,49 @@ def test_ordered_needs_no_workspace():
     assert L.pa_decode_ordered(*good_args(D=96), None, 0, FAKE, None) == _lib.PA_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("over,code", BAD, ids=[str(b[0]) for b in BAD])
+def test_grouped_rejects(over, code):
+    L = _lib.lib()
+    assert L.pa_decode_grouped(*good_args(**over), 4, FAKE, 1 << 20, FAKE, None) == code
+
+
+def test_grouped_workspace_checks():
+    L = _lib.lib()
+    # a shape the grouped kernel takes: bf16, 8 query heads over 2 KV heads, head_dim 128
+    a = good_args(io=_lib.PA_BF16, kv=_lib.PA_BF16, H=8, Hkv=2, D=128)
+    need = _lib.pa_grouped_workspace_bytes(4, 8, 2, 128, 3)
+    assert need == 4 * 8 * 3 * 130 * 4
+    assert L.pa_decode_grouped(*a, 3, FAKE, need - 4, FAKE, None) == _lib.PA_ERR_WORKSPACE
+    assert L.pa_decode_grouped(*a, 3, None, need, FAKE, None) == _lib.PA_ERR_WORKSPACE
+    assert L.pa_decode_grouped(*a, 3, FAKE + 4, need, FAKE, None) == _lib.PA_ERR_INVALID
+    assert L.pa_decode_grouped(*a, -1, FAKE, need, FAKE, None) == _lib.PA_ERR_INVALID
+
+
+def test_grouped_workspace_formula():
+    # fp32 (max, exp-sum, head_dim partial outputs) per (sequence, query head, split);
+    # none for one split or for group sizes the grouped kernel does not take
+    assert _lib.pa_grouped_workspace_bytes(64, 32, 8, 128, 4) == 64 * 32 * 4 * 130 * 4
+    assert _lib.pa_grouped_workspace_bytes(64, 32, 8, 128, 1) == 0
+    assert _lib.pa_grouped_workspace_bytes(64, 32, 32, 128, 4) == 0
+    assert _lib.pa_grouped_workspace_bytes(64, 48, 8, 128, 4) == 0
+    assert _lib.pa_grouped_workspace_bytes(0, 32, 8, 128, 4) == 0
+    assert _lib.pa_grouped_workspace_bytes(64, 32, 8, 128, -1) == 0
+
+
+def test_grouped_debug_trace_checks():
+    L = _lib.lib()
+    a = good_args(io=_lib.PA_BF16, kv=_lib.PA_BF16, H=8, Hkv=2, D=128)
+    # no block-read counters
+    assert L.pa_debug_trace_grouped(*a, 100, 1, None, 0, FAKE, FAKE, FAKE, FAKE, None, None) == \
+        _lib.PA_ERR_INVALID
+    # a shape the grouped kernel does not take
+    b = good_args(io=_lib.PA_F32, kv=_lib.PA_F32, H=8, Hkv=2, D=128)
+    assert L.pa_debug_trace_grouped(*b, 100, 1, None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == \
+        _lib.PA_ERR_UNSUPPORTED
+    assert L.pa_debug_trace_grouped(*good_args(q=0), 100, 1, None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == \
+        _lib.PA_ERR_INVALID
+
+
 def test_balanced_workspace_formula():
     # counters: one int32 per (KV head, sequence), padded to 256 bytes; then per workgroup
     # two slots of G maxima, G sums and G x head_dim partial outputs, fp32
