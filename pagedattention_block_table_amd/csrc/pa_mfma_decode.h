@@ -1,38 +1,34 @@
-// Decode kernels for gfx950 with the score product on the matrix cores.
+// Decode kernels for gfx950 with both products on the matrix cores.
 //
 // Same computation as decode_kernel (pages cited there): for a KV head g and the G query
-// heads that share it (G = 1, 2 or 4), scores z = scale * q.K^T over the cached tokens,
-// online softmax, and the softmax-weighted sum of V rows, in fp32. The score product
-// [G x D] x [D x tokens] runs as v_mfma_f32_16x16x32_{f16,bf16}; the V product runs on
-// the vector ALUs.
+// heads that share it (G = 2, 4 or 8), scores z = scale * q.K^T over the cached tokens,
+// online softmax, and the softmax-weighted sum of V rows, accumulated in fp32.
 //
-// MFMA operand layout (16x16x32, wave64): lane l supplies row l%16 of A and column
-// l%16 of B, each as the 8 consecutive k values 8*(l/16) .. 8*(l/16)+7; lane l receives
-// D[4*(l/16) + r][l%16] in result register r. Here A = the query heads (row m holds
-// head m % G, so the G heads repeat down the 16 rows), B = K^T (column n = token n of a
-// 16-token tile) and k runs over head_dim. The k order inside the product is free, so
-// each lane feeds the MFMA straight from its own 16-byte K loads: lane (n = l%16,
-// lg = l/16) loads the 16-byte chunks 4i + lg of token n's row. Result register r of
-// every lane then holds the score of head r % G for token n.
+// MFMA operand layout (wave64): for v_mfma_f32_16x16x32, lane l supplies row l%16 of A
+// and column l%16 of B, each as the 8 consecutive k values 8*(l/16) .. 8*(l/16)+7, and
+// receives D[4*(l/16) + r][l%16] in result register r; the 16x16x16 form takes four k
+// values per lane (4*(l/16) .. +3) with the same result layout. The k order inside a
+// product is free, so each lane feeds the score product straight from its own 16-byte
+// K loads: lane (n = l%16, lg = l/16) loads the 16-byte chunks 4i + lg of token n's row.
 //
-// V product: lane (n, lg) with half h = n/8 loads, for token n and its partner n^8, the
-// chunks 4*(VPL*h + k) + lg (k < VPL = chunks-per-lane / 2), so each V row of the tile
-// is read exactly once per wave. The partner's probabilities come from lane n^8 with
-// one DPP rotate. Each lane accumulates G heads x VPL chunks; at the end the 8 lanes of
-// a half-row that hold the same columns are summed with DPP.
+// The per-wave engine (MfmaTEngine below) computes the scores transposed, S^T = K Q^T,
+// so that each lane receives the scores of one query row for four tokens of a 16-token
+// tile: exactly its B operand of O^T += V^T P^T after the softmax. V^T comes from the
+// wave's LDS copy of the tile, read transposed.
 //
-// Softmax: the running max of each head is uniform over the wave. It is only raised
-// when a chunk's max exceeds it by more than kLazyRescale (log2 units); in between the
-// probabilities exp2(z - m) stay <= 2^kLazyRescale, and the final normalisation by the
-// running sum makes the result independent of which m was used.
+// Softmax: each query row keeps a running max in log2 units, raised only when a tile's
+// max exceeds it by more than kLazyRescale; in between the probabilities exp2(z - m) stay
+// <= 2^kLazyRescale, and the final normalisation by the running sum makes the result
+// independent of which m was used.
 //
-// Work is cut into chunks of CT = 16 * NT tokens (NT tiles). Chunks are dealt round
-// robin to the waves of a workgroup, so the order of arithmetic depends only on logical
-// token positions: results are bitwise identical under any block size, physical
-// placement or sharing. Each wave fetches the table entries of its chunks ahead, 64 at a
-// time, and keeps the next chunk's K/V loads in flight while it computes the current one.
+// Work is cut into chunks of 16 * NT tokens. Chunks are dealt round robin to the waves of
+// a workgroup, so the order of arithmetic depends only on logical token positions:
+// results are bitwise identical under any block size, physical placement or sharing.
+// Each wave fetches the table entries of its chunks ahead, 64 at a time, and keeps the
+// next chunk's K/V loads in flight while it computes the current one.
 //
-// Two schedulers use the same chunk math:
+// Two schedulers drive the engines (the vector engine ValuEngine for one query head per
+// KV head in the balanced grid):
 //   mfma_decode_kernel      one workgroup per (KV head, sequence, partition), its waves
 //                           taking the chunks round robin and merging through LDS;
 //   balanced_decode_kernel  a fixed grid of workgroups splits the total chunk count of
@@ -54,9 +50,6 @@ constexpr float kLazyRescale = 8.0f;
 
 #ifndef PA_STAGGER
 #define PA_STAGGER 1
-#endif
-#ifndef PA_MFMA_TILES
-#define PA_MFMA_TILES 2
 #endif
 
 // Fixed work of one segment of the balanced scheduler (engine set-up, wave merge, write),
@@ -186,36 +179,6 @@ struct LaneIds {
   __device__ __forceinline__ explicit LaneIds(int l) : lane(l), n(l & 15), lg(l >> 4), hh((l & 15) >> 3) {}
 };
 
-// K/V registers of one chunk in flight: K rows of the own token of each tile, V rows of
-// the own token and of its partner n^8.
-template <int KV, int D, int NT>
-struct ChunkBuf {
-  using Geo = MfmaGeo<KV, D>;
-  uint4 kr[NT][Geo::CPL];
-  uint4 vo[NT][Geo::VPL];
-  uint4 vp[NT][Geo::VPL];
-};
-
-// Online-softmax state of one wave for one (sequence, KV head): per head the running max
-// (log2 units, wave-uniform), the lane's partial exp-sum and its partial outputs.
-template <int KV, int D, int G>
-struct WaveState {
-  using Geo = MfmaGeo<KV, D>;
-  float m[G], l[G];
-  float acc[G][Geo::VPL][Geo::VEC];
-  __device__ __forceinline__ void reset() {
-#pragma unroll
-    for (int r = 0; r < G; ++r) {
-      m[r] = -3.0e38f;
-      l[r] = 0.f;
-#pragma unroll
-      for (int q = 0; q < Geo::VPL; ++q)
-#pragma unroll
-        for (int e = 0; e < Geo::VEC; ++e) acc[r][q][e] = 0.f;
-    }
-  }
-};
-
 // Query operands of (sequence s, KV head g): row n of A is head g*G + n%G, and the k
 // index (lg, e) of step i*VEC/8 + hf is column VEC*(4i+lg) + 8*hf + e.
 template <int IO, int KV, int D, int G>
@@ -233,310 +196,6 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, int s, int g, const 
     }
   }
 }
-
-// Issue the K/V loads of the chunk whose first token is c0 (a multiple of the block size
-// or of 16, and below t_end), with off[u] = byte offset of the chunk's u-th block and
-// kbase / vbase pointing at the KV head's tile of block 0. A lane whose token is at or
-// past t_end reads token c0's row instead (finite data already being fetched; the score
-// of such a token is excluded by select, so its probability is exactly 0). Every load
-// is unconditional: loads under a branch would make the compiler wait for all
-// outstanding loads (the next chunks' too) at the top of the chunk loop.
-template <int KV, int D, int BS, int NT>
-__device__ __forceinline__ void issue_chunk(ChunkBuf<KV, D, NT>& b, const char* kbase, const char* vbase,
-                                            const int64_t* off, int c0, int t_end, const LaneIds& li) {
-  using Geo = MfmaGeo<KV, D>;
-  constexpr int RB = Geo::RB, CPL = Geo::CPL, VPL = Geo::VPL;
-  constexpr int CT = 16 * NT;
-  constexpr int NBC = CT >= BS ? CT / BS : 1;
-  const int jb = c0 / BS;
-#pragma unroll
-  for (int tau = 0; tau < NT; ++tau) {
-    int to = c0 + 16 * tau + li.n;          // own token
-    int tp = c0 + 16 * tau + (li.n ^ 8);    // partner token
-    to = to < t_end ? to : c0;
-    tp = tp < t_end ? tp : c0;
-    int64_t bo = off[0], bp = off[0];
-#pragma unroll
-    for (int u = 1; u < NBC; ++u) {
-      bo = to / BS - jb == u ? off[u] : bo;
-      bp = tp / BS - jb == u ? off[u] : bp;
-    }
-    const char* krow = kbase + bo + (to % BS) * RB;
-    const char* vrow_o = vbase + bo + (to % BS) * RB;
-    const char* vrow_p = vbase + bp + (tp % BS) * RB;
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) b.kr[tau][i] = load16(krow + 16 * (4 * i + li.lg));
-#pragma unroll
-    for (int q = 0; q < VPL; ++q) {
-      const int vc = 4 * (VPL * li.hh + q) + li.lg;
-      b.vo[tau][q] = load16(vrow_o + 16 * vc);
-      b.vp[tau][q] = load16(vrow_p + 16 * vc);
-    }
-  }
-}
-
-// Test builds: copy the raw K/V rows the wave consumes and count the reads of each
-// (sequence s, KV head g, token).
-template <int KV, int D, int NT>
-__device__ __forceinline__ void trace_chunk(const DecodeArgs& a, const ChunkBuf<KV, D, NT>& b, int s, int g,
-                                            int c0, int t_end, const LaneIds& li) {
-  using Geo = MfmaGeo<KV, D>;
-  constexpr int RB = Geo::RB, CPL = Geo::CPL, VPL = Geo::VPL;
-  const int Hkv = a.num_kv_heads;
-#pragma unroll
-  for (int tau = 0; tau < NT; ++tau) {
-    const int to = c0 + 16 * tau + li.n;
-    const int tp = c0 + 16 * tau + (li.n ^ 8);
-    const int64_t ro = ((int64_t)s * Hkv + g) * a.dbg_max_ctx + to;
-    const int64_t rp = ((int64_t)s * Hkv + g) * a.dbg_max_ctx + tp;
-    if (to < t_end) {
-#pragma unroll
-      for (int i = 0; i < CPL; ++i)
-        *(uint4*)((char*)a.dbg_k + ro * RB + 16 * (4 * i + li.lg)) = b.kr[tau][i];
-#pragma unroll
-      for (int q = 0; q < VPL; ++q)
-        *(uint4*)((char*)a.dbg_v + ro * RB + 16 * (4 * (VPL * li.hh + q) + li.lg)) = b.vo[tau][q];
-      if (li.lg == 0) atomicAdd(a.dbg_counts + ro, 1);
-    }
-    if (tp < t_end) {
-#pragma unroll
-      for (int q = 0; q < VPL; ++q)
-        *(uint4*)((char*)a.dbg_v + rp * RB + 16 * (4 * (VPL * li.hh + q) + li.lg)) = b.vp[tau][q];
-    }
-  }
-}
-
-// Scores, online softmax and V accumulation of one loaded chunk (first token c0).
-template <int IO, int KV, int D, int G, int NT>
-__device__ __forceinline__ void consume_chunk(const DecodeArgs& a, const ChunkBuf<KV, D, NT>& b,
-                                              const typename Mma<IO>::vec (&qa)[MfmaGeo<KV, D>::NST],
-                                              int c0, int t_end, WaveState<KV, D, G>& st,
-                                              const LaneIds& li) {
-  using Geo = MfmaGeo<KV, D>;
-  using M = Mma<IO>;
-  constexpr int VEC = Geo::VEC, CPL = Geo::CPL, VPL = Geo::VPL;
-  // scores of the G heads for the own token of each tile (log2 units)
-  float z[NT][G];
-#pragma unroll
-  for (int tau = 0; tau < NT; ++tau) {
-    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < CPL; ++i)
-#pragma unroll
-      for (int hf = 0; hf < VEC / 8; ++hf)
-        c = M::mma(qa[i * (VEC / 8) + hf], k_operand<IO, KV>(b.kr[tau][i], hf), c);
-    const bool ok = c0 + 16 * tau + li.n < t_end;
-#pragma unroll
-    for (int r = 0; r < G; ++r) z[tau][r] = ok ? c[r] * a.q_mul : -INFINITY;
-  }
-
-  // chunk max per head (all four 16-lane rows hold the same values)
-  float mx[G];
-  bool raise = false;
-#pragma unroll
-  for (int r = 0; r < G; ++r) {
-    float x = z[0][r];
-#pragma unroll
-    for (int tau = 1; tau < NT; ++tau) x = fmaxf(x, z[tau][r]);
-    x = fmaxf(x, dpp<0x128>(x));  // row_ror 8
-    x = fmaxf(x, dpp<0x124>(x));  // row_ror 4
-    x = fmaxf(x, dpp<0x122>(x));  // row_ror 2
-    x = fmaxf(x, dpp<0x121>(x));  // row_ror 1
-    // keep the running max wave-uniform (scalar) even if rows differ in the last bit
-    mx[r] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
-    raise |= mx[r] > st.m[r] + kLazyRescale;
-  }
-  if (raise) {
-#pragma unroll
-    for (int r = 0; r < G; ++r) {
-      const float mn = fmaxf(st.m[r], mx[r]);
-      const float alpha = __builtin_amdgcn_exp2f(st.m[r] - mn);
-      st.m[r] = mn;
-      st.l[r] *= alpha;
-#pragma unroll
-      for (int q = 0; q < VPL; ++q)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) st.acc[r][q][e] *= alpha;
-    }
-  }
-
-#pragma unroll
-  for (int tau = 0; tau < NT; ++tau) {
-    float po[G], pp[G];
-#pragma unroll
-    for (int r = 0; r < G; ++r) {
-      po[r] = __builtin_amdgcn_exp2f(z[tau][r] - st.m[r]);
-      st.l[r] += po[r];
-      pp[r] = dpp<0x128>(po[r]);  // lane n^8 holds the partner token
-    }
-#pragma unroll
-    for (int q = 0; q < VPL; ++q) {
-      float fo[VEC], fq[VEC];
-      widen16<KV>(b.vo[tau][q], fo);
-      widen16<KV>(b.vp[tau][q], fq);
-#pragma unroll
-      for (int r = 0; r < G; ++r)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          st.acc[r][q][e] = fmaf(po[r], fo[e], st.acc[r][q][e]);
-          st.acc[r][q][e] = fmaf(pp[r], fq[e], st.acc[r][q][e]);
-        }
-    }
-  }
-}
-
-// Reduce a wave's state: l over the 16 token lanes of a row (every lane gets the total),
-// acc over the 8 lanes of a half-row (lanes with n % 8 == 0 hold the totals for the
-// columns VEC*(4*(VPL*hh + q) + lg) + e).
-template <int KV, int D, int G>
-__device__ __forceinline__ void reduce_state(WaveState<KV, D, G>& st) {
-  using Geo = MfmaGeo<KV, D>;
-#pragma unroll
-  for (int r = 0; r < G; ++r) {
-    st.l[r] = group_sum<16>(st.l[r]);
-#pragma unroll
-    for (int q = 0; q < Geo::VPL; ++q)
-#pragma unroll
-      for (int e = 0; e < Geo::VEC; ++e) {
-        float x = st.acc[r][q][e];
-        x += dpp<kRowHalfMirror>(x);
-        x += dpp<kQuadXor2>(x);
-        x += dpp<kQuadXor1>(x);
-        st.acc[r][q][e] = x;
-      }
-  }
-}
-
-// Column of head_dim held in a reduced state's acc[r][q][e] by a lane with n % 8 == 0.
-template <int KV, int D>
-__device__ __forceinline__ int acc_column(const LaneIds& li, int q, int e) {
-  using Geo = MfmaGeo<KV, D>;
-  return Geo::VEC * (4 * (Geo::VPL * li.hh + q) + li.lg) + e;
-}
-
-// Per-wave processing of one segment of one (sequence s, KV head g): the wave takes the
-// chunks k0 + rotated(wave + k*NW, rot, len), k = 0, 1, ..., counted in CT-token chunks
-// from token `base`. Their block-table entries are fetched ahead by one vector load per
-// 64 chunks (lane l holds the entries of the wave's chunk 64*w + l; the next window is
-// loaded while the current one is used), and the K/V loads of chunk k+1 are in flight
-// while chunk k is computed.
-template <int IO, int KV, int D, int BS, int G, int NT, bool DBG>
-struct MfmaEngine {
-  using Geo = MfmaGeo<KV, D>;
-  static constexpr int CT = 16 * NT;                 // tokens per chunk
-  static constexpr int NBC = CT >= BS ? CT / BS : 1; // blocks per chunk
-  static constexpr int TILE_BYTES = BS * Geo::RB;
-  using vec = typename Mma<IO>::vec;
-  using Buf = ChunkBuf<KV, D, NT>;
-  static_assert(mfma_supported<IO, KV, D, G>() && G <= 4, "unsupported MFMA decode geometry");
-  static_assert(BS >= 8 && BS <= 512 && (BS & (BS - 1)) == 0, "block size");
-  static_assert(CT % BS == 0 || BS % CT == 0, "chunks and blocks nest");
-
-  LaneIds li;
-  int s, g, t_end, j_end;
-  int base, k0, len, rot, wave, nw;
-  const int32_t* bt;
-  const char* kbase;
-  const char* vbase;
-  int64_t blk_stride;
-  int win[2][NBC];  // block ids of this wave's chunks, windows w and w + 1
-  int cur_win;      // w: the window held in win[0]
-  vec qa[Geo::NST];
-  WaveState<KV, D, G> st;
-
-  __device__ __forceinline__ explicit MfmaEngine(int lane) : li(lane) {}
-
-  __device__ __forceinline__ int chunk_token(int k) const {
-    return base + CT * (k0 + rotated(wave + k * nw, rot, len));
-  }
-
-  // Raw table entries of the wave's chunks 64w .. 64w+63 (lane l: chunk 64w + l); entries
-  // of chunks or blocks past the end read entry 0 of the row instead (never used for a
-  // valid token). Ids are clamped into the pool when they are taken (block_id).
-  __device__ __forceinline__ void load_window(const DecodeArgs& a, int w, int (&dst)[NBC]) {
-    const int k = 64 * w + li.lane;
-    const bool live = wave + k * nw < len;
-    const int j = live ? chunk_token(k) / BS : 0;
-#pragma unroll
-    for (int u = 0; u < NBC; ++u) dst[u] = bt[live && j + u < j_end ? j + u : 0];
-  }
-
-  // Block id of the u-th block of chunk k (k in the current window), clamped into the
-  // pool so that a bad table never reads outside it (contract: 0 <= id < num_blocks).
-  __device__ __forceinline__ int64_t block_off(const DecodeArgs& a, int u, int k) const {
-    const int b = __builtin_amdgcn_readlane(win[0][u], k & 63);
-    return (int64_t)min(max(b, 0), a.num_blocks - 1) * blk_stride;
-  }
-
-  __device__ __forceinline__ void begin(const DecodeArgs& a, int s_, int g_, int t_end_, int base_,
-                                        int k0_, int len_, int rot_, int wave_, int nw_) {
-    s = s_;
-    g = g_;
-    t_end = t_end_;
-    j_end = (t_end + BS - 1) / BS;
-    base = base_;
-    k0 = k0_;
-    len = len_;
-    rot = rot_;
-    wave = wave_;
-    nw = nw_;
-    bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-    blk_stride = (int64_t)a.num_kv_heads * TILE_BYTES;
-    kbase = (const char*)a.k_pool + (int64_t)g * TILE_BYTES;
-    vbase = (const char*)a.v_pool + (int64_t)g * TILE_BYTES;
-    load_window(a, 0, win[0]);
-    load_window(a, 1, win[1]);
-    cur_win = 0;
-    load_q<IO, KV, D, G>(a, s, g, li, qa);
-    st.reset();
-  }
-
-  __device__ __forceinline__ void issue(const DecodeArgs& a, Buf& b, int k) {
-    if ((k >> 6) != cur_win) {
-      // entering window k/64: it was loaded 64 chunks ago; fetch the one after it
-      cur_win = k >> 6;
-#pragma unroll
-      for (int u = 0; u < NBC; ++u) win[0][u] = win[1][u];
-      load_window(a, cur_win + 1, win[1]);
-    }
-    int64_t off[NBC];
-#pragma unroll
-    for (int u = 0; u < NBC; ++u) off[u] = block_off(a, u, k);
-    issue_chunk<KV, D, BS, NT>(b, kbase, vbase, off, chunk_token(k), t_end, li);
-  }
-
-  __device__ __forceinline__ void consume(const DecodeArgs& a, const Buf& b, int k) {
-    const int c0 = chunk_token(k);
-    if constexpr (DBG) trace_chunk<KV, D, NT>(a, b, s, g, c0, t_end, li);
-    consume_chunk<IO, KV, D, G, NT>(a, b, qa, c0, t_end, st, li);
-  }
-
-  // This wave's chunks of the segment, kPipeDepth in flight.
-  __device__ __forceinline__ void run(const DecodeArgs& a) {
-    const int nwc = wave < len ? (len - wave + nw - 1) / nw : 0;
-    run_pipelined(*this, a, nwc);
-  }
-
-  // Reduce the wave's state and store it as wave `wave` of the workgroup's LDS arrays.
-  template <int NW>
-  __device__ __forceinline__ void finish(float (&sm_m)[NW][G], float (&sm_l)[NW][G],
-                                         float (&sm_o)[NW][G][D]) {
-    reduce_state<KV, D, G>(st);
-    if ((li.n & 7) == 0) {
-#pragma unroll
-      for (int r = 0; r < G; ++r) {
-#pragma unroll
-        for (int q = 0; q < Geo::VPL; ++q)
-#pragma unroll
-          for (int e = 0; e < Geo::VEC; ++e) sm_o[wave][r][acc_column<KV, D>(li, q, e)] = st.acc[r][q][e];
-        if (li.lane == 0) {
-          sm_m[wave][r] = st.m[r];
-          sm_l[wave][r] = st.l[r];
-        }
-      }
-    }
-  }
-};
 
 // 16x16x16 products for the V side: A = probabilities, B = V^T tile read transposed
 // from LDS. Operands are four 16-bit values per lane: lane l supplies row l%16 of A and
@@ -577,328 +236,6 @@ template <int KV, int D>
 struct VTileRegs {
   static constexpr int NV = 16 * D * ElemBytes<KV>::value / 1024;
   uint4 v[NV > 0 ? NV : 1];
-};
-
-// Per-wave engine for G = 2 or 4 query heads per KV head with both products on the
-// matrix cores. Scores as in MfmaEngine (16x16x32, K^T straight from the lanes' loads).
-// The V product O[h][d] += sum_t P[h][t] V[t][d] runs as 16x16x16 MFMAs: each chunk's V
-// rows are loaded with contiguous 1 KiB wave loads, written to a per-wave LDS tile in the
-// MFMA type (fp8 widened exactly), and read back transposed (ds_read_b64_tr_b16: lane i
-// of a 16-lane group gets column i of four rows) as the B operand; the probabilities go
-// through LDS as the A operand (row h = head h % G, four tokens per lane), split into a
-// high and a low 16-bit part so that the product keeps fp32 accuracy. The accumulators
-// hold the complete sums over the wave's tokens: lane l, register r of d-tile dt holds
-// head (4*(l/16) + r) % G, column 16*dt + l%16. With G = 8 the heads form two halves of
-// four, each with its own query operand, scores and accumulators; the chunk's K and V
-// loads and its V tile serve both.
-template <int IO, int KV, int D, int BS, int G, bool DBG>
-struct MfmaPvEngine {
-  using Geo = MfmaGeo<KV, D>;
-  static constexpr int NT = 1;
-  static constexpr int CT = 16;
-  static constexpr int NBC = CT >= BS ? CT / BS : 1;
-  static constexpr int RB = Geo::RB;
-  static constexpr int TILE_BYTES = BS * RB;
-  static constexpr int NDT = D / 16;           // 16-column tiles of head_dim
-  static constexpr int NV = VTileRegs<KV, D>::NV;
-  // LDS V tile in the MFMA type, rows padded by 32 bytes: the transposed reads of 16
-  // rows then spread over the 64 banks (two-way at most) instead of sharing 8 banks
-  static constexpr int VT_ROW = D + 16;        // 16-bit elements per tile row
-  static constexpr int VT_BYTES = 16 * VT_ROW * 2;
-  static constexpr int P_BYTES = 2 * G * 16 * 2;
-  static constexpr int kLdsBytes = VT_BYTES + P_BYTES;
-  static constexpr int HG = G < 4 ? G : 4;     // heads per half (rows of A repeat with period HG)
-  static constexpr int NH = G / HG;            // halves: 2 for G = 8, else 1
-  using vec = typename Mma<IO>::vec;
-  using M16 = Mma16<IO>;
-  using v4 = typename M16::v4;
-  static_assert(G == 2 || G == 4 || G == 8, "group");
-  static_assert(mfma_supported<IO, KV, D, G>(), "unsupported MFMA decode geometry");
-  static_assert(NV >= 1 && 16 * RB % 1024 == 0, "V tile of whole wave loads");
-
-  struct Buf {
-    uint4 kr[Geo::CPL];
-    VTileRegs<KV, D> vt;
-  };
-
-  LaneIds li;
-  int s, g, t_end, j_end;
-  int base, k0, len, rot, wave, nw;
-  const int32_t* bt;
-  const char* kbase;
-  const char* vbase;
-  int64_t blk_stride;
-  int win[2][NBC];
-  int cur_win;
-  vec qa[NH][Geo::NST];
-  float m[G], l[G];
-  f32x4_t o[NH][NDT];
-  char* lds;  // this wave's V tile and probability tiles
-
-  __device__ __forceinline__ MfmaPvEngine(int lane, char* wave_lds) : li(lane), lds(wave_lds) {}
-
-  __device__ __forceinline__ int chunk_token(int k) const {
-    return base + CT * (k0 + rotated(wave + k * nw, rot, len));
-  }
-
-  // Raw table entries of the wave's chunks 64w .. 64w+63 (lane l: chunk 64w + l); entries
-  // of chunks or blocks past the end read entry 0 of the row instead (never used for a
-  // valid token). Ids are clamped into the pool when they are taken (block_id).
-  __device__ __forceinline__ void load_window(const DecodeArgs& a, int w, int (&dst)[NBC]) {
-    const int k = 64 * w + li.lane;
-    const bool live = wave + k * nw < len;
-    const int j = live ? chunk_token(k) / BS : 0;
-#pragma unroll
-    for (int u = 0; u < NBC; ++u) dst[u] = bt[live && j + u < j_end ? j + u : 0];
-  }
-
-  // Block id of the u-th block of chunk k (k in the current window), clamped into the
-  // pool so that a bad table never reads outside it (contract: 0 <= id < num_blocks).
-  __device__ __forceinline__ int64_t block_off(const DecodeArgs& a, int u, int k) const {
-    const int b = __builtin_amdgcn_readlane(win[0][u], k & 63);
-    return (int64_t)min(max(b, 0), a.num_blocks - 1) * blk_stride;
-  }
-
-  __device__ __forceinline__ void begin(const DecodeArgs& a, int s_, int g_, int t_end_, int base_,
-                                        int k0_, int len_, int rot_, int wave_, int nw_) {
-    s = s_;
-    g = g_;
-    t_end = t_end_;
-    j_end = (t_end + BS - 1) / BS;
-    base = base_;
-    k0 = k0_;
-    len = len_;
-    rot = rot_;
-    wave = wave_;
-    nw = nw_;
-    bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-    blk_stride = (int64_t)a.num_kv_heads * TILE_BYTES;
-    kbase = (const char*)a.k_pool + (int64_t)g * TILE_BYTES;
-    vbase = (const char*)a.v_pool + (int64_t)g * TILE_BYTES;
-    load_window(a, 0, win[0]);
-    load_window(a, 1, win[1]);
-    cur_win = 0;
-    // half h2 holds heads g*G + 4*h2 + (0..HG-1): those of "KV head" g*NH + h2 at group HG
-#pragma unroll
-    for (int h2 = 0; h2 < NH; ++h2) load_q<IO, KV, D, HG>(a, s, g * NH + h2, li, qa[h2]);
-#pragma unroll
-    for (int r = 0; r < G; ++r) {
-      m[r] = -3.0e38f;
-      l[r] = 0.f;
-    }
-#pragma unroll
-    for (int h2 = 0; h2 < NH; ++h2)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[h2][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-
-  __device__ __forceinline__ void issue(const DecodeArgs& a, Buf& b, int k) {
-    if ((k >> 6) != cur_win) {
-      cur_win = k >> 6;
-#pragma unroll
-      for (int u = 0; u < NBC; ++u) win[0][u] = win[1][u];
-      load_window(a, cur_win + 1, win[1]);
-    }
-    int64_t off[NBC];
-#pragma unroll
-    for (int u = 0; u < NBC; ++u) off[u] = block_off(a, u, k);
-    const int c0 = chunk_token(k);
-    const int jb = c0 / BS;
-    // Rows at or past t_end read token c0's row instead (see issue_chunk): every load is
-    // unconditional.
-    // K: lane (n, lg) loads chunks 4i + lg of token n
-    {
-      int to = c0 + li.n;
-      to = to < t_end ? to : c0;
-      int64_t bo = off[0];
-#pragma unroll
-      for (int u = 1; u < NBC; ++u) bo = to / BS - jb == u ? off[u] : bo;
-      const char* krow = kbase + bo + (to % BS) * RB;
-#pragma unroll
-      for (int i = 0; i < Geo::CPL; ++i) b.kr[i] = load16(krow + 16 * (4 * i + li.lg));
-    }
-    // V: instruction i covers bytes 1024*i .. of the 16 rows, in memory order
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int byte = 1024 * i + 16 * li.lane;
-      int t = c0 + byte / RB;
-      t = t < t_end ? t : c0;
-      int64_t bo = off[0];
-#pragma unroll
-      for (int u = 1; u < NBC; ++u) bo = t / BS - jb == u ? off[u] : bo;
-      b.vt.v[i] = load16(vbase + bo + (t % BS) * RB + byte % RB);
-    }
-  }
-
-  __device__ __forceinline__ void trace(const DecodeArgs& a, const Buf& b, int c0) {
-    const int Hkv = a.num_kv_heads;
-    const int64_t row0 = ((int64_t)s * Hkv + g) * a.dbg_max_ctx;
-    const int to = c0 + li.n;
-    if (to < t_end) {
-#pragma unroll
-      for (int i = 0; i < Geo::CPL; ++i)
-        *(uint4*)((char*)a.dbg_k + (row0 + to) * RB + 16 * (4 * i + li.lg)) = b.kr[i];
-      if (li.lg == 0) atomicAdd(a.dbg_counts + row0 + to, 1);
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int byte = 1024 * i + 16 * li.lane;
-      const int t = c0 + byte / RB;
-      if (t < t_end) *(uint4*)((char*)a.dbg_v + (row0 + t) * RB + byte % RB) = b.vt.v[i];
-    }
-  }
-
-  // Lanes of one wave exchange data through LDS: a wave-scope fence keeps the compiler
-  // from moving a lane's LDS reads above other lanes' writes (the hardware executes one
-  // wave's LDS instructions in order).
-  static __device__ __forceinline__ void lds_exchange() {
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-  }
-
-  __device__ __forceinline__ void consume(const DecodeArgs& a, const Buf& b, int k) {
-    const int c0 = chunk_token(k);
-    if constexpr (DBG) trace(a, b, c0);
-
-    // the previous chunk's transposed reads of the tile come before these writes
-    lds_exchange();
-
-    // V rows -> LDS tile [16][D] in the MFMA type
-    uint16_t* vt = (uint16_t*)lds;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int byte = 1024 * i + 16 * li.lane;
-      const int t = byte / RB;
-      const int col = (byte % RB) / ElemBytes<KV>::value;
-      if constexpr (KV == kFP8) {
-        const uint4 r = b.vt.v[i];
-        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-        uint32_t packed[8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          packed[2 * q] = fp8x2_to_mt<IO, false>(w[q]);
-          packed[2 * q + 1] = fp8x2_to_mt<IO, true>(w[q]);
-        }
-        *(uint4*)(vt + t * VT_ROW + col) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-        *(uint4*)(vt + t * VT_ROW + col + 8) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-      } else {
-        *(uint4*)(vt + t * VT_ROW + col) = b.vt.v[i];
-      }
-    }
-
-    // the tile is read back by other lanes of the wave (transposed): order the writes
-    // before those reads
-    lds_exchange();
-
-    // scores of the G heads for token n (log2 units); register r of half h2 holds head
-    // h2*HG + r % HG
-    const bool ok = c0 + li.n < t_end;
-    float z[G];
-#pragma unroll
-    for (int h2 = 0; h2 < NH; ++h2) {
-      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < Geo::CPL; ++i)
-#pragma unroll
-        for (int hf = 0; hf < Geo::VEC / 8; ++hf)
-          c = Mma<IO>::mma(qa[h2][i * (Geo::VEC / 8) + hf], k_operand<IO, KV>(b.kr[i], hf), c);
-#pragma unroll
-      for (int r = 0; r < HG; ++r) z[h2 * HG + r] = ok ? c[r] * a.q_mul : -INFINITY;
-    }
-
-    float mx[G];
-    bool raise = false;
-#pragma unroll
-    for (int r = 0; r < G; ++r) {
-      float x = z[r];
-      x = fmaxf(x, dpp<0x128>(x));  // row_ror 8
-      x = fmaxf(x, dpp<0x124>(x));  // row_ror 4
-      x = fmaxf(x, dpp<0x122>(x));  // row_ror 2
-      x = fmaxf(x, dpp<0x121>(x));  // row_ror 1
-      mx[r] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
-      raise |= mx[r] > m[r] + kLazyRescale;
-    }
-    if (raise) {
-      float alpha[G];
-#pragma unroll
-      for (int r = 0; r < G; ++r) {
-        const float mn = fmaxf(m[r], mx[r]);
-        alpha[r] = __builtin_amdgcn_exp2f(m[r] - mn);
-        m[r] = mn;
-        l[r] *= alpha[r];
-      }
-#pragma unroll
-      for (int h2 = 0; h2 < NH; ++h2)
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o[h2][dt][r] *= alpha[h2 * HG + r % HG];
-    }
-
-    // probabilities -> LDS as A operands [hi/lo][head][token]
-    uint16_t* pt = (uint16_t*)(lds + VT_BYTES);
-#pragma unroll
-    for (int r = 0; r < G; ++r) {
-      const float p = __builtin_amdgcn_exp2f(z[r] - m[r]);
-      l[r] += p;
-      uint16_t hi, lo;
-      M16::split(p, hi, lo);
-      if (li.lg == 0) {
-        pt[r * 16 + li.n] = hi;
-        pt[G * 16 + r * 16 + li.n] = lo;
-      }
-    }
-    lds_exchange();
-    v4 ahi[NH], alo[NH];
-#pragma unroll
-    for (int h2 = 0; h2 < NH; ++h2) {
-      const int h = h2 * HG + li.n % HG;
-      ahi[h2] = *(const v4*)(pt + h * 16 + 4 * li.lg);
-      alo[h2] = *(const v4*)(pt + G * 16 + h * 16 + 4 * li.lg);
-    }
-
-    // O[h][16dt + i] += sum_t P[h][t] V[t][16dt + i]
-    const int vrow = 4 * li.lg + (li.n >> 2);
-    const int vcol = 4 * (li.n & 3);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const v4 bv = __builtin_bit_cast(
-          v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (__attribute__((address_space(3))) i16x4_t*)(vt + vrow * VT_ROW + 16 * dt + vcol)));
-#pragma unroll
-      for (int h2 = 0; h2 < NH; ++h2) {
-        o[h2][dt] = M16::mma(ahi[h2], bv, o[h2][dt]);
-        o[h2][dt] = M16::mma(alo[h2], bv, o[h2][dt]);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void run(const DecodeArgs& a) {
-    const int nwc = wave < len ? (len - wave + nw - 1) / nw : 0;
-    run_pipelined(*this, a, nwc);
-  }
-
-  template <int NW>
-  __device__ __forceinline__ void finish(float (&sm_m)[NW][G], float (&sm_l)[NW][G],
-                                         float (&sm_o)[NW][G][D]) {
-#pragma unroll
-    for (int r = 0; r < G; ++r) l[r] = group_sum<16>(l[r]);
-    if (li.lg == 0) {
-#pragma unroll
-      for (int h2 = 0; h2 < NH; ++h2)
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int r = 0; r < HG; ++r) sm_o[wave][h2 * HG + r][16 * dt + li.n] = o[h2][dt][r];
-    }
-    if (li.lane == 0) {
-#pragma unroll
-      for (int r = 0; r < G; ++r) {
-        sm_m[wave][r] = m[r];
-        sm_l[wave][r] = l[r];
-      }
-    }
-  }
 };
 
 // Reductions over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48), every
@@ -944,7 +281,8 @@ __device__ __forceinline__ float rows4_sum(float x) {
 // rows; row rho of the 16 holds head rho % G), so that lane l receives the scores of query
 // row l % 16 for tokens 4 (l / 16) .. +3 of each 16-token tile: after the softmax these are
 // exactly its B operand of O^T += V^T P^T (16x16x16, A = V^T read transposed from the
-// wave's LDS copy of the V tile, the same reads as MfmaPvEngine's B operand). The
+// wave's LDS copy of the V tile: ds_read_b64_tr_b16 gives lane i of a 16-lane group
+// column i of four rows). The
 // probabilities never leave the registers (high and low 16-bit halves, fp32 accuracy), and
 // each lane keeps the running max and exp-sum of its own row; the four lanes of a row take
 // identical decisions. The lazy raise of the running max is decided per row, so a row's
@@ -1235,19 +573,9 @@ struct MfmaTEngine {
   }
 };
 
-// Engine used for a shape: the V product on the matrix cores when 2 or 4 query heads
-// share a 16-bit KV head; on the vector ALUs for one query head per KV head (one FMA
-// per V element) and for fp8 KV, where widening the tile for the matrix cores costs
-// more vector work than the FMAs it replaces (measured on the mixed-length fp8 batch).
-#ifndef PA_MFMA_PV
-#define PA_MFMA_PV 1
-#endif
-#ifndef PA_BAL_VALU
-#define PA_BAL_VALU 1
-#endif
-#ifndef PA_T_ENGINE
-#define PA_T_ENGINE 1
-#endif
+// Engine used for a shape: one query head per KV head takes the vector engine (whole
+// 1 KiB rows per wave load, no matrix-core rows wasted); 2, 4 or 8 take the transposed
+// matrix-core engine.
 #ifndef PA_T_TILES
 #define PA_T_TILES 1
 #endif
@@ -1256,30 +584,14 @@ struct MfmaTEngine {
 #endif
 template <int IO, int KV, int D, int BS, int G, bool DBG>
 struct EngineFor {
-  // one head per KV head takes the vector engine (whole 1 KiB rows per wave load, no MFMA
-  // rows wasted); 2, 4 or 8 take the transposed matrix-core engine
-  static constexpr bool valu = PA_BAL_VALU && G == 1;
-  static constexpr bool te = PA_T_ENGINE && (G == 2 || G == 4 || G == 8);
-  static constexpr bool pv = !te && ((PA_MFMA_PV && (G == 2 || G == 4) && KV != kFP8) || G == 8);
+  static constexpr bool valu = G == 1;
   static constexpr int TNT = KV == kFP8 ? PA_T_TILES_FP8 : PA_T_TILES;
-  using type = typename std::conditional<
-      valu, ValuEngine<IO, KV, D, BS, G, DBG>,
-      typename std::conditional<
-          te, MfmaTEngine<IO, KV, D, BS, (te ? G : 2), TNT, DBG>,
-          typename std::conditional<pv, MfmaPvEngine<IO, KV, D, BS, G, DBG>,
-                                    MfmaEngine<IO, KV, D, BS, G, PA_MFMA_TILES, DBG>>::type>::type>::type;
-  static constexpr int lds_bytes =
-      te ? MfmaTEngine<IO, KV, D, BS, (te ? G : 2), TNT, DBG>::kLdsBytes
-         : (pv ? MfmaPvEngine<IO, KV, D, BS, (pv ? G : 4), DBG>::kLdsBytes : 16);
+  using type = typename std::conditional<valu, ValuEngine<IO, KV, D, BS, G, DBG>,
+                                         MfmaTEngine<IO, KV, D, BS, (valu ? 2 : G), TNT, DBG>>::type;
+  static constexpr int lds_bytes = valu ? 16 : MfmaTEngine<IO, KV, D, BS, (valu ? 2 : G), TNT, DBG>::kLdsBytes;
 };
 
 template <class Eng> struct EngineMaker;  // builds an engine with or without its LDS tile
-template <int IO, int KV, int D, int BS, int G, int NT, bool DBG>
-struct EngineMaker<MfmaEngine<IO, KV, D, BS, G, NT, DBG>> {
-  static __device__ __forceinline__ MfmaEngine<IO, KV, D, BS, G, NT, DBG> make(int lane, char*) {
-    return MfmaEngine<IO, KV, D, BS, G, NT, DBG>(lane);
-  }
-};
 template <int IO, int KV, int D, int BS, int G, bool DBG>
 struct EngineMaker<ValuEngine<IO, KV, D, BS, G, DBG>> {
   static __device__ __forceinline__ ValuEngine<IO, KV, D, BS, G, DBG> make(int lane, char*) {
@@ -1290,12 +602,6 @@ template <int IO, int KV, int D, int BS, int G, int NT, bool DBG>
 struct EngineMaker<MfmaTEngine<IO, KV, D, BS, G, NT, DBG>> {
   static __device__ __forceinline__ MfmaTEngine<IO, KV, D, BS, G, NT, DBG> make(int lane, char* lds) {
     return MfmaTEngine<IO, KV, D, BS, G, NT, DBG>(lane, lds);
-  }
-};
-template <int IO, int KV, int D, int BS, int G, bool DBG>
-struct EngineMaker<MfmaPvEngine<IO, KV, D, BS, G, DBG>> {
-  static __device__ __forceinline__ MfmaPvEngine<IO, KV, D, BS, G, DBG> make(int lane, char* lds) {
-    return MfmaPvEngine<IO, KV, D, BS, G, DBG>(lane, lds);
   }
 };
 
