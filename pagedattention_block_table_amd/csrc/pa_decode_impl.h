@@ -209,16 +209,62 @@ template <int N> __device__ __forceinline__ float group_sum(float x) {
   }
 }
 
+// Lane pairs l, l ^ 16 and l, l ^ 32: gfx950's v_permlane16_swap / v_permlane32_swap exchange rows
+// between two registers in one vector instruction, leaving each lane its own value and
+// that of lane l ^ 16 (resp. l ^ 32), with no LDS traffic. Max and + are commutative, so
+// both lanes of a pair get the same bits. The second register starts as a copy of the
+// first; the empty asm keeps the optimizer from treating the two as one value. The pair's
+// elements are copied into plain integers before any bit cast (a bit cast taken straight
+// from an element of the returned pair read element 0 for both).
+__device__ __forceinline__ void rows_pair16(float x, float& a, float& b) {
+  unsigned u = __builtin_bit_cast(unsigned, x), w = u;
+  asm volatile("" : "+v"(w));
+  const auto p = __builtin_amdgcn_permlane16_swap(u, w, false, false);
+  const unsigned p0 = p[0], p1 = p[1];
+  a = __builtin_bit_cast(float, p0);
+  b = __builtin_bit_cast(float, p1);
+}
+__device__ __forceinline__ void rows_pair32(float x, float& a, float& b) {
+  unsigned u = __builtin_bit_cast(unsigned, x), w = u;
+  asm volatile("" : "+v"(w));
+  const auto p = __builtin_amdgcn_permlane32_swap(u, w, false, false);
+  const unsigned p0 = p[0], p1 = p[1];
+  a = __builtin_bit_cast(float, p0);
+  b = __builtin_bit_cast(float, p1);
+}
+// A lane's value and that of lane l ^ K: the pair exchanges above for K = 16 and 32 (no
+// LDS traffic), a lane shuffle below 16.
+template <int K> __device__ __forceinline__ void lane_pair(float x, float& a, float& b) {
+  if constexpr (K == 16) {
+    rows_pair16(x, a, b);
+  } else if constexpr (K == 32) {
+    rows_pair32(x, a, b);
+  } else {
+    a = x;
+    b = __shfl_xor(x, K);
+  }
+}
+
 // Reduce across the row groups of a wave: lanes that differ only in bits >= log2(STRIDE).
+// Both lanes of a pair combine the same two values (max and + commute), so every lane of
+// a row-group set ends with the same bits.
 template <int STRIDE> __device__ __forceinline__ float rows_max(float x) {
-#pragma unroll
-  for (int k = STRIDE; k < 64; k <<= 1) x = fmaxf(x, __shfl_xor(x, k));
-  return x;
+  if constexpr (STRIDE < 64) {
+    float a, b;
+    lane_pair<STRIDE>(x, a, b);
+    return rows_max<2 * STRIDE>(fmaxf(a, b));
+  } else {
+    return x;
+  }
 }
 template <int STRIDE> __device__ __forceinline__ float rows_sum(float x) {
-#pragma unroll
-  for (int k = STRIDE; k < 64; k <<= 1) x += __shfl_xor(x, k);
-  return x;
+  if constexpr (STRIDE < 64) {
+    float a, b;
+    lane_pair<STRIDE>(x, a, b);
+    return rows_sum<2 * STRIDE>(a + b);
+  } else {
+    return x;
+  }
 }
 
 // ---------------------------------------------------------------------------------
@@ -787,6 +833,11 @@ decode_kernel(const DecodeArgs a) {
 // instead of one partition between a dependent prologue and a write. Partitions are whole
 // steps (the partition size is a multiple of the step, U * SB tokens), so a step never
 // spans two partitions and only the context end is masked.
+// Partition states a wave of the streaming kernel buffers before writing them: about
+// 8 KiB of LDS per wave (16 states of one head at head_dim 128), at least one.
+template <int G, int D>
+constexpr int kStreamStates = (2080 / (G * (D + 2))) > 0 ? (2080 / (G * (D + 2))) : 1;
+
 template <int IO, int KV, int D, int BS, int G, int NW, int U, bool DBG>
 __global__ void __launch_bounds__(NW * 64)
 decode_stream_kernel(const DecodeArgs a) {
@@ -850,8 +901,42 @@ decode_stream_kernel(const DecodeArgs a) {
       for (int e = 0; e < VEC; ++e) st.acc[gi][e] = 0.f;
     }
   };
+  // Partition states go to a per-wave LDS buffer and reach the workspace in batches, with
+  // full-wave 16-byte stores, when the buffer is full or the run is done. Stores retire in
+  // order with the loads on the same counter, so a store issued at every partition end
+  // would hold up the consumption of every load issued after it; batched, the wave issues
+  // them once per buffer (at the end of the run for runs that fit).
+  constexpr int SBUF = kStreamStates<G, D>;
+  __shared__ __align__(16) float sm_st[NW][SBUF][G][D];
+  __shared__ float sm_ml[NW][2][SBUF][G];
+  float (*wst)[G][D] = sm_st[hw_wave];
+  int nbuf = 0, pbuf = 0;  // states buffered, partition of the first one
+  auto flush = [&]() {
+    if (nbuf == 0) return;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // buffered state j is partition pbuf + j * ps; its row for head gi is contiguous (8-byte
+    // pieces: the output rows start 8 * NPH bytes into the workspace)
+    for (int idx = lane; idx < nbuf * G * (D / 2); idx += 64) {
+      const int j = idx / (G * (D / 2));
+      const int gi = (idx / (D / 2)) % G;
+      const int d2 = idx % (D / 2);
+      const int64_t slot = ((int64_t)s * H + (int64_t)g * G + gi) * a.num_parts + pbuf + j * ps;
+      *(float2*)(a.ws + 2 * NPH + slot * D + 2 * d2) = *(const float2*)&wst[j][gi][2 * d2];
+    }
+    for (int idx = lane; idx < nbuf * G; idx += 64) {
+      const int j = idx / G;
+      const int gi = idx % G;
+      const int64_t slot = ((int64_t)s * H + (int64_t)g * G + gi) * a.num_parts + pbuf + j * ps;
+      a.ws[slot] = sm_ml[hw_wave][0][j][gi];
+      a.ws[NPH + slot] = sm_ml[hw_wave][1][j][gi];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    nbuf = 0;
+  };
   // merge the row groups of the wave, then lanes of row group 0 write their columns of
-  // partition `part` (or of the output)
+  // the output (a sequence of one partition) or buffer partition `part`'s state
   auto finish = [&](int part) {
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
@@ -862,26 +947,33 @@ decode_stream_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) st.acc[gi][e] = rows_sum<LPT>(st.acc[gi][e] * f);
     }
-    if (r == 0) {
+    if (write_out) {
+      if (r == 0) {
 #pragma unroll
-      for (int gi = 0; gi < G; ++gi) {
-        const int h = g * G + gi;
-        if (write_out) {
+        for (int gi = 0; gi < G; ++gi) {
+          const int h = g * G + gi;
 #pragma unroll
           for (int e = 0; e < VEC; ++e)
             store_io<IO>(a.out, ((int64_t)s * H + h) * D + c * VEC + e,
                          st.l[gi] > 0.f ? (st.acc[gi][e] / st.l[gi]) * a.out_mul : 0.f);
-        } else {
-          const int64_t slot = ((int64_t)s * H + h) * a.num_parts + part;
+        }
+      }
+      return;
+    }
+    if (nbuf == SBUF) flush();
+    if (nbuf == 0) pbuf = part;
+    if (r == 0) {
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) a.ws[2 * NPH + slot * D + c * VEC + e] = st.acc[gi][e] * a.out_mul;
-          if (c == 0) {
-            a.ws[slot] = st.m[gi];
-            a.ws[NPH + slot] = st.l[gi];
-          }
+      for (int gi = 0; gi < G; ++gi) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) wst[nbuf][gi][c * VEC + e] = st.acc[gi][e] * a.out_mul;
+        if (c == 0) {
+          sm_ml[hw_wave][0][nbuf][gi] = st.m[gi];
+          sm_ml[hw_wave][1][nbuf][gi] = st.l[gi];
         }
       }
     }
+    ++nbuf;
   };
   reset();
   if (nsteps <= 0) {  // empty sequence: its output is zero
@@ -933,6 +1025,7 @@ decode_stream_kernel(const DecodeArgs a) {
       consume(buf[d], k + d);
       close(k + d);
     }
+  flush();
 }
 
 // The vector path as an engine of the chunk schedulers (the balanced grid): the same

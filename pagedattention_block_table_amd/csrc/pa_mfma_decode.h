@@ -239,29 +239,7 @@ struct VTileRegs {
 };
 
 // Reductions over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48), every
-// lane receiving the result: gfx950's v_permlane16_swap / v_permlane32_swap exchange rows
-// between two registers in one vector instruction, leaving each lane its own value and
-// that of lane l ^ 16 (resp. l ^ 32), with no LDS traffic. Max and + are commutative, so
-// both lanes of a pair get the same bits. The second register starts as a copy of the
-// first; the empty asm keeps the optimizer from treating the two as one value. The pair's
-// elements are copied into plain integers before any bit cast (a bit cast taken straight
-// from an element of the returned pair read element 0 for both).
-__device__ __forceinline__ void rows_pair16(float x, float& a, float& b) {
-  unsigned u = __builtin_bit_cast(unsigned, x), w = u;
-  asm volatile("" : "+v"(w));
-  const auto p = __builtin_amdgcn_permlane16_swap(u, w, false, false);
-  const unsigned p0 = p[0], p1 = p[1];
-  a = __builtin_bit_cast(float, p0);
-  b = __builtin_bit_cast(float, p1);
-}
-__device__ __forceinline__ void rows_pair32(float x, float& a, float& b) {
-  unsigned u = __builtin_bit_cast(unsigned, x), w = u;
-  asm volatile("" : "+v"(w));
-  const auto p = __builtin_amdgcn_permlane32_swap(u, w, false, false);
-  const unsigned p0 = p[0], p1 = p[1];
-  a = __builtin_bit_cast(float, p0);
-  b = __builtin_bit_cast(float, p1);
-}
+// lane receiving the result (pair exchanges rows_pair16 / rows_pair32).
 __device__ __forceinline__ float rows4_max(float x) {
   float a, b;
   rows_pair16(x, a, b);
