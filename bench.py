@@ -2,8 +2,9 @@
 """Benchmark of the paged-attention decode step on one MI355X.
 
 One step = one pass of the whole decode path (block-table gather, scores, online
-softmax, V product, and for the split-context mode the log-sum-exp merge kernel) over
-the whole synthetic batch. Inputs are resident in HBM before timing starts. So that
+softmax, V product, and for the split-context mode the log-sum-exp merge of the
+partitions: inside the partition launch when each (sequence, KV head) is run by the
+waves of one workgroup, else by a second launch) over the whole synthetic batch. Inputs are resident in HBM before timing starts. So that
 every step reads its K/V from HBM and not from the 256 MB Infinity Cache or the L2s,
 the benchmark keeps R identical replicas of the K and V pools (R x pool >= 2 GiB) and
 step i reads replica i mod R, as a decode over many layers does.
@@ -655,7 +656,9 @@ def main():
                      "kernel_ms": round(gpu_ms, 6),
                      "algorithmic_bytes_per_launch": head["algorithmic_bytes"],
                      "timing": "HIP events on the launch stream around the timed steps; one step = "
-                               + ("the partition kernel plus the log-sum-exp merge kernel"
+                               + ("the split-context launch with the log-sum-exp merge of the partitions "
+                                  "(inside it when every (sequence, KV head) is run by one workgroup, "
+                                  "else a second launch)"
                                   if mode == "partitioned" else "the decode launch(es) of the mode")},
         "cpu_baseline": cpu,
         "alt_modes": alt or None,

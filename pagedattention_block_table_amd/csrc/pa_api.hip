@@ -541,10 +541,14 @@ int run(const Common& c, Mode mode, int max_context_len, int P, int nwg, void* w
     ls.args.wave_parts = (int)k;
     ls.args.wave_chunks = (int)chunks;
     ls.args.wave_interleave = PA_STREAM_INTERLEAVE;
+    // the runs of each unit fill whole workgroups and every run's states fit its wave's
+    // buffer: the workgroups merge the partitions themselves (no merge launch)
+    const int G = c.H / c.Hkv;
+    ls.args.wave_merge = (PA_WAVES % chunks == 0 && k <= stream_states(G, c.D)) ? 1 : 0;
     ls.stream_waves = (int)((int64_t)c.Hkv * c.S * chunks);
   }
   rc = launch_pair(c.io, c.kv, ls);
-  if (rc != PA_OK || NP <= 1) return rc;
+  if (rc != PA_OK || NP <= 1 || ls.args.wave_merge) return rc;
   MergeArgs m{};
   m.ws = (const float*)workspace;
   m.context_lens = c.cl;

@@ -84,6 +84,7 @@ struct DecodeArgs {
   int wave_parts;        // split-context streaming kernel: partitions per wave (at most)
   int wave_chunks;       // ... and runs per (sequence, KV head)
   int wave_interleave;   // run c takes partitions c, c + wave_chunks, ... (else consecutive)
+  int wave_merge;        // ... and each workgroup merges its units' partitions itself
 };
 
 // ---------------------------------------------------------------------------------
@@ -835,8 +836,11 @@ decode_kernel(const DecodeArgs a) {
 // spans two partitions and only the context end is masked.
 // Partition states a wave of the streaming kernel buffers before writing them: about
 // 8 KiB of LDS per wave (16 states of one head at head_dim 128), at least one.
+__host__ __device__ constexpr int stream_states(int G, int D) {
+  return (2080 / (G * (D + 2))) > 0 ? (2080 / (G * (D + 2))) : 1;
+}
 template <int G, int D>
-constexpr int kStreamStates = (2080 / (G * (D + 2))) > 0 ? (2080 / (G * (D + 2))) : 1;
+constexpr int kStreamStates = stream_states(G, D);
 
 template <int IO, int KV, int D, int BS, int G, int NW, int U, bool DBG>
 __global__ void __launch_bounds__(NW * 64)
@@ -848,6 +852,23 @@ decode_stream_kernel(const DecodeArgs a) {
 
   const int hw_wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gw = xcd_unit((int)blockIdx.x, (int)gridDim.x) * NW + hw_wave;
+
+  // Partition states go to a per-wave LDS buffer and reach the workspace in batches, with
+  // full-wave stores, when the buffer is full or the run is done. Stores retire in order
+  // with the loads on the same counter, so a store issued at every partition end would
+  // hold up the consumption of every load issued after it; batched, the wave issues them
+  // once per buffer (at the end of the run for runs that fit). When every (sequence, KV
+  // head) is run by the waves of one workgroup and fits their buffers (wave_merge), the
+  // workgroup merges the states itself and writes the output: no workspace traffic and
+  // no second launch.
+  constexpr int SBUF = kStreamStates<G, D>;
+  __shared__ __align__(16) float sm_st[NW][SBUF][G][D];
+  __shared__ float sm_ml[NW][2][SBUF][G];
+  __shared__ int sm_cnt[NW];
+  const bool wmerge = a.wave_merge != 0;
+  int nbuf = 0, pbuf = 0;  // states buffered, partition of the first one
+
+  auto run = [&]() {
   const int cps = a.wave_chunks;
   if (gw >= a.num_seqs * a.num_kv_heads * cps) return;  // past the last run (this wave)
   const int chunk = gw % cps;
@@ -901,16 +922,7 @@ decode_stream_kernel(const DecodeArgs a) {
       for (int e = 0; e < VEC; ++e) st.acc[gi][e] = 0.f;
     }
   };
-  // Partition states go to a per-wave LDS buffer and reach the workspace in batches, with
-  // full-wave 16-byte stores, when the buffer is full or the run is done. Stores retire in
-  // order with the loads on the same counter, so a store issued at every partition end
-  // would hold up the consumption of every load issued after it; batched, the wave issues
-  // them once per buffer (at the end of the run for runs that fit).
-  constexpr int SBUF = kStreamStates<G, D>;
-  __shared__ __align__(16) float sm_st[NW][SBUF][G][D];
-  __shared__ float sm_ml[NW][2][SBUF][G];
   float (*wst)[G][D] = sm_st[hw_wave];
-  int nbuf = 0, pbuf = 0;  // states buffered, partition of the first one
   auto flush = [&]() {
     if (nbuf == 0) return;
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -1025,7 +1037,40 @@ decode_stream_kernel(const DecodeArgs a) {
       consume(buf[d], k + d);
       close(k + d);
     }
-  flush();
+  if (!wmerge) flush();
+  };
+  run();
+  if (!wmerge) return;
+
+  // log-sum-exp merge of the partition states of this workgroup's (sequence, KV head)
+  // units ([P2] §3.3 / §4.1), from the waves' buffers
+  if ((threadIdx.x & 63) == 0) sm_cnt[hw_wave] = nbuf;
+  __syncthreads();
+  const int cpu = a.wave_chunks;  // waves (runs) per unit
+  const int unit0 = (gw - hw_wave) / cpu;
+  const int P = a.part_tokens;
+  for (int idx = threadIdx.x; idx < (NW / cpu) * G * D; idx += NW * 64) {
+    const int ul = idx / (G * D);
+    const int gi = (idx / D) % G;
+    const int d = idx % D;
+    const int unit = unit0 + ul;
+    if (unit >= a.num_seqs * a.num_kv_heads) continue;
+    int s, g;
+    unit_seq_head(a, unit, s, g);
+    const int L = min(max(a.context_lens[s], 0), a.max_ctx);
+    if ((L + P - 1) / P <= 1) continue;  // one partition: its run wrote the output
+    float M = -3.0e38f;
+    for (int w = ul * cpu; w < (ul + 1) * cpu; ++w)
+      for (int j = 0; j < sm_cnt[w]; ++j) M = fmaxf(M, sm_ml[w][0][j][gi]);
+    float num = 0.f, den = 0.f;
+    for (int w = ul * cpu; w < (ul + 1) * cpu; ++w)
+      for (int j = 0; j < sm_cnt[w]; ++j) {
+        const float f = __builtin_amdgcn_exp2f(sm_ml[w][0][j][gi] - M);
+        num = fmaf(f, sm_st[w][j][gi][d], num);
+        den = fmaf(f, sm_ml[w][1][j][gi], den);
+      }
+    store_io<IO>(a.out, ((int64_t)s * a.num_heads + (int64_t)g * G + gi) * D + d, den > 0.f ? num / den : 0.f);
+  }
 }
 
 // The vector path as an engine of the chunk schedulers (the balanced grid): the same

@@ -278,6 +278,34 @@ def test_split_context_streaming_kernel(io, kv, G, D, BS):
     _trace_check(b, P, 0)
 
 
+# (sequences, longest context) at 8 KV heads, f16, head_dim 128, 32-token partitions. On a
+# 256-CU device the streaming kernel aims at 1024 waves: 32 x 8 units of 64 partitions are
+# runs of 16 (each unit one workgroup, merged there); 69 partitions make runs of 18, more
+# than a wave buffers (flushed mid-run, merge kernel); 64 sequences give two units per
+# workgroup; 128 sequences of at most 16 partitions one run per unit, four per workgroup.
+STREAM_PATHS = [(32, 64 * 32), (32, 69 * 32), (64, 32 * 32), (128, 16 * 32)]
+
+
+@pytest.mark.parametrize("S,Lmax", STREAM_PATHS, ids=[f"s{a}-l{b}" for a, b in STREAM_PATHS])
+def test_split_context_stream_state_paths(S, Lmax):
+    """The streaming kernel's partition states either stay in its waves' buffers and are
+    merged by the workgroup, or go to the workspace (at the end of a run, or whenever a
+    wave's buffer fills) and are merged by the merge kernel. Ragged lengths (empty, one
+    token, partition edges, the longest) against the oracle and through the read trace."""
+    Hkv, P = 8, 32
+    rng = np.random.default_rng(S + Lmax)
+    lens = rng.integers(1, Lmax + 1, size=S)
+    lens[:6] = (0, 1, P, P + 1, Lmax, Lmax - 1)
+    spec = W.Spec(f"stream_paths_{S}_{Lmax}", S, Hkv, Hkv, 128, 32, "f16", "f16",
+                  ("fixed", tuple(int(x) for x in lens)), seed=6300 + S)
+    b = W.make_batch(spec)
+    log(f"[stream-paths] S={S} Lmax={Lmax} parts={-(-Lmax // P)}")
+    got = to_f64(run(b, to_device(b), "partitioned", P))
+    check_against_oracle(b, got, io_rounding=True)
+    assert (got[b.context_lens == 0] == 0).all()
+    _trace_check(b, P, 0)
+
+
 def test_length_one_returns_value_row_exactly():
     spec = W.Spec("len1", 3, 8, 2, 128, 16, "f32", "f32", ("fixed", (1, 1, 1)), seed=11)
     b = W.make_batch(spec)
