@@ -29,9 +29,10 @@
 // free, so k = 8q + j stands for token 4q + j (j < 4) and 16 + 4q + j - 4 (j >= 4) in
 // both operands: the lane's own eight probabilities form its B operand, and its A
 // operand (V^T, row d = n) is two transposed LDS reads (ds_read_b64_tr_b16) of rows
-// 4q .. 4q+3 and 16+4q .. 16+4q+3. Probabilities are split into high and low 16-bit
-// parts (two MFMAs) so that the V product keeps fp32 accuracy. Online softmax per query
-// row in log2 units, the running max shared by the row's four lanes and raised lazily.
+// 4q .. 4q+3 and 16+4q .. 16+4q+3. fp8 V is widened to f16 (exact) and takes the
+// probabilities rounded to f16 in one product (relative error <= 2^-12 per weight). Online
+// softmax per query row in log2 units, the running max shared by the row's four lanes and
+// raised lazily.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -108,7 +109,12 @@ template <int IO, int KV, int D, int G>
 __global__ void __launch_bounds__(kExtWaves * 64) extend_kernel(const ExtendArgs a) {
   using Geo = ExtGeo<IO, KV, D>;
   using vec = typename Mma<IO>::vec;
-  using M16 = Mma16<IO>;
+  // Type of the V product: fp8 V widened to f16 (exact: every e4m3 value is an f16 value)
+  // with the probabilities rounded to f16 in one product (relative error <= 2^-12 per
+  // weight); bf16 V keeps bf16 with the probabilities split in high and low halves.
+  constexpr int PVT = KV == kFP8 ? kF16 : IO;
+  using pvec = typename Mma<PVT>::vec;
+  using M16 = Mma16<PVT>;
   constexpr int QT = kExtRows / G;  // new tokens per workgroup
   static_assert(kExtRows % G == 0 && 16 % G == 0, "group");
 
@@ -206,18 +212,18 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_kernel(const ExtendArgs
         const int r = piece / Geo::PPR;
         const int col = (piece % Geo::PPR) * Geo::VPP;
         put_piece<IO, KV>(kt + r * Geo::KROW + col, kreg[u]);
-        put_piece<IO, KV>(vt + r * Geo::VROW + col, vreg[u]);
+        put_piece<PVT, KV>(vt + r * Geo::VROW + col, vreg[u]);
       }
     }
   };
 
   // probabilities as f16 keep 11 significant bits; bf16 keeps 8, so there they go as
   // high + low halves
-  constexpr bool SPLIT = IO == kBF16;
+  constexpr bool SPLIT = PVT == kBF16;
   float m = -3.0e38f;  // running max of row n (log2 units), same in the row's 4 lanes
   f32x4_t lacc = f32x4_t{0.f, 0.f, 0.f, 0.f};  // softmax denominator of row n
-  constexpr uint32_t kOne2 = IO == kF16 ? 0x3C003C00u : 0x3F803F80u;  // two 16-bit 1.0
-  const vec ones = __builtin_bit_cast(vec, make_uint4(kOne2, kOne2, kOne2, kOne2));
+  constexpr uint32_t kOne2 = PVT == kF16 ? 0x3C003C00u : 0x3F803F80u;  // two 16-bit 1.0
+  const pvec ones = __builtin_bit_cast(pvec, make_uint4(kOne2, kOne2, kOne2, kOne2));
   f32x4_t o[Geo::NDT];
 #pragma unroll
   for (int dt = 0; dt < Geo::NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -275,7 +281,7 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_kernel(const ExtendArgs
       float p[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(z[j], a.q_mul, -m));
-      vec bhi, blo;
+      pvec bhi, blo;
       if constexpr (SPLIT) {
         uint16_t phi[8], plo[8];
 #pragma unroll
@@ -289,15 +295,15 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_kernel(const ExtendArgs
         bl.y = plo[2] | ((uint32_t)plo[3] << 16);
         bl.z = plo[4] | ((uint32_t)plo[5] << 16);
         bl.w = plo[6] | ((uint32_t)plo[7] << 16);
-        bhi = __builtin_bit_cast(vec, bh);
-        blo = __builtin_bit_cast(vec, bl);
+        bhi = __builtin_bit_cast(pvec, bh);
+        blo = __builtin_bit_cast(pvec, bl);
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) bhi[j] = (_Float16)p[j];
       }
       // the softmax denominator as one more tile with V^T = 1
-      lacc = Mma<IO>::mma(ones, bhi, lacc);
-      if constexpr (SPLIT) lacc = Mma<IO>::mma(ones, blo, lacc);
+      lacc = Mma<PVT>::mma(ones, bhi, lacc);
+      if constexpr (SPLIT) lacc = Mma<PVT>::mma(ones, blo, lacc);
       // V^T operand: row d = 16dt + n, tokens 4lq .. 4lq+3 and 16+4lq .. 16+4lq+3
       const int vr = 4 * lq + (n >> 2);
       const int vc = 4 * (n & 3);
@@ -309,9 +315,9 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_kernel(const ExtendArgs
             (__attribute__((address_space(3))) i16x4_t*)(vt + (16 + vr) * Geo::VROW + 16 * dt + vc));
         const uint2 w0 = __builtin_bit_cast(uint2, x0);
         const uint2 w1 = __builtin_bit_cast(uint2, x1);
-        const vec av = __builtin_bit_cast(vec, make_uint4(w0.x, w0.y, w1.x, w1.y));
-        o[dt] = Mma<IO>::mma(av, bhi, o[dt]);
-        if constexpr (SPLIT) o[dt] = Mma<IO>::mma(av, blo, o[dt]);
+        const pvec av = __builtin_bit_cast(pvec, make_uint4(w0.x, w0.y, w1.x, w1.y));
+        o[dt] = Mma<PVT>::mma(av, bhi, o[dt]);
+        if constexpr (SPLIT) o[dt] = Mma<PVT>::mma(av, blo, o[dt]);
       }
     }
     if (c + 1 < nch) store_chunk((c + 1) & 1);
