@@ -421,6 +421,14 @@ __device__ __forceinline__ void unit_seq(const DecodeArgs& a, int sg, OrderLds& 
 #define PA_VEC_DEPTH 1
 #endif
 constexpr int kVecDepth = PA_VEC_DEPTH;
+// Steps in flight per wave in the streaming split-context kernel with one query head per KV
+// head. Its grid holds about four waves per compute unit (one per SIMD), so registers are
+// not what limits its occupancy and the loads of the next step can be issued before the
+// current one is consumed (more query heads keep one: their states fill the registers).
+#ifndef PA_STREAM_DEPTH
+#define PA_STREAM_DEPTH 2
+#endif
+constexpr int kStreamDepth = PA_STREAM_DEPTH;
 
 // Blocks larger than SB tokens (32, or 16 / 8 for 512- / 1024-byte rows) are walked as
 // SB-token sub-blocks: sub-block j covers tokens SB j .. SB j + SB - 1, lies in logical
@@ -849,6 +857,7 @@ decode_stream_kernel(const DecodeArgs a) {
   static_assert(Geo::ok, "unsupported geometry");
   constexpr int VEC = Geo::VEC, LPT = Geo::LPT, SB = Geo::SB;
   constexpr int ST = U * SB;  // tokens per step
+  constexpr int SD = G == 1 ? kStreamDepth : 1;  // steps in flight (more heads: registers)
 
   const int hw_wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gw = xcd_unit((int)blockIdx.x, (int)gridDim.x) * NW + hw_wave;
@@ -1019,20 +1028,20 @@ decode_stream_kernel(const DecodeArgs a) {
     tw.ids(min(k, nsteps - 1), a.num_blocks, bid);
     issue_step<KV, D, BS, G, U>(b, kbase, vbase, blk_stride, bid, j0_of(k), L, r, c);
   };
-  Buf buf[kVecDepth];
+  Buf buf[SD];
 #pragma unroll
-  for (int d = 0; d < kVecDepth; ++d) issue(buf[d], d);
+  for (int d = 0; d < SD; ++d) issue(buf[d], d);
   int k = 0;
-  for (; k + kVecDepth <= nsteps; k += kVecDepth) {
+  for (; k + SD <= nsteps; k += SD) {
 #pragma unroll
-    for (int d = 0; d < kVecDepth; ++d) {
+    for (int d = 0; d < SD; ++d) {
       consume(buf[d], k + d);
-      issue(buf[d], k + d + kVecDepth);
+      issue(buf[d], k + d + SD);
       close(k + d);
     }
   }
 #pragma unroll
-  for (int d = 0; d < kVecDepth - 1; ++d)
+  for (int d = 0; d < SD - 1; ++d)
     if (k + d < nsteps) {
       consume(buf[d], k + d);
       close(k + d);
