@@ -104,12 +104,18 @@ size_t pa_partitioned_workspace_bytes(int num_seqs, int num_heads, int head_dim,
 
 /* Split-context decode for long contexts ([P2] §3.3 and §4.1 second-version kernel).
  * The context of every sequence is cut into partitions of partition_size tokens (a
- * multiple of block_size; 0 = default 512); one workgroup per (sequence, KV head,
- * partition) writes that partition's max, exp-sum and unnormalized output into the
- * workspace, and a second kernel on the same stream merges the partitions of each
- * (sequence, head) by log-sum-exp weighting. Sequences with one partition are written
- * directly. max_context_len is a host-known bound >= every context_lens[s]; it sizes
- * the grid and the workspace. */
+ * multiple of block_size; 0 = default 512); each partition's max, exp-sum and
+ * unnormalized output are combined per (sequence, head) by log-sum-exp weighting.
+ * Sequences with one partition are written directly. How the partitions are scheduled
+ * depends on the shape: with the matrix-core kernels one workgroup per (sequence, KV
+ * head, partition) writes its state into the workspace and a second kernel on the same
+ * stream merges; with the vector kernel (one query head per KV head, fp32, head_dim 256,
+ * fp8 with head_dim 64) each wave streams a run of consecutive partitions, and when the
+ * runs of a (sequence, KV head) are the waves of one workgroup the workgroup merges them
+ * itself (one launch, the workspace untouched), else the states go to the workspace for
+ * the merge kernel.
+ * The workspace is required whenever there is more than one partition. max_context_len
+ * is a host-known bound >= every context_lens[s]; it sizes the grid and the workspace. */
 int pa_decode_partitioned(const void* q, const void* k_pool, const void* v_pool,
                           const int32_t* block_tables, const int32_t* context_lens,
                           int num_seqs, int max_blocks_per_seq, int num_blocks,

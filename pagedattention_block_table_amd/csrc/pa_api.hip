@@ -380,9 +380,8 @@ bool vector_shape(const Common& c) {
   return !mfma;
 }
 
-// The balanced scheduler covers the MFMA shapes: 1, 2 or 4 query heads per KV head,
-// io f16 / bf16, KV = io or fp8, 128 or 256 bytes per token row, at most
-// kMaxBalancedSeqs sequences.
+// The balanced scheduler covers 1, 2, 4 or 8 query heads per KV head, io f16 / bf16, KV
+// = io or fp8, 128 or 256 bytes per token row, at most kMaxBalancedSeqs sequences.
 bool balanced_shape(const Common& c) {
   const int g = c.H / c.Hkv;
   if (g != 1 && g != 2 && g != 4 && g != 8) return false;
