@@ -253,7 +253,7 @@ def make_batch(spec, keep_logical: bool = False, threads: Optional[int] = None) 
             spikes[s] = np.sort(rng_struct.choice(L, size=n, replace=False))
 
     used = int(n_shared + (nblk - n_shared).sum()) if P else int(nblk.sum())
-    NB = int(spec.pool_blocks) if spec.pool_blocks is not None else int(math.ceil(spec.pool_factor * used))
+    NB = int(spec.pool_blocks) if spec.pool_blocks is not None else max(1, int(math.ceil(spec.pool_factor * used)))
     assert NB >= used, (NB, used)
     perm = rng_struct.permutation(NB).astype(np.int32)
     shared_ids = perm[:n_shared]
