@@ -85,6 +85,9 @@ struct DecodeArgs {
   int wave_chunks;       // ... and runs per (sequence, KV head)
   int wave_interleave;   // run c takes partitions c, c + wave_chunks, ... (else consecutive)
   int wave_merge;        // ... and each workgroup merges its units' partitions itself
+  // grouped kernel over the new tokens of short queries (extend): when set, a group is one
+  // sequence and its members are its query_start_loc[s + 1] - query_start_loc[s] new tokens
+  const int32_t* query_start_loc;
 };
 
 // ---------------------------------------------------------------------------------

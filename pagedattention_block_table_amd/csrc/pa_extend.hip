@@ -62,6 +62,7 @@ struct ExtendArgs {
   int q_tiles;    // workgroups per (sequence, KV head)
   float q_mul;    // scale * log2(e) * k_scale
   float v_scale;
+  int skip_q;     // sequences with at most this many new tokens run elsewhere (0: none)
 };
 
 // max of three scores in one instruction, without the canonicalizing moves fmaxf adds
@@ -135,7 +136,8 @@ __global__ void __launch_bounds__(kExtWaves * 64) extend_kernel(const ExtendArgs
   const int q0 = a.query_start_loc[s];
   const int Q = a.query_start_loc[s + 1] - q0;
   const int i0 = qt * QT;
-  if (Q <= 0 || i0 >= Q) return;  // whole workgroup
+  // whole workgroup: no query rows here, or a short query the grouped decode kernel takes
+  if (Q <= 0 || i0 >= Q || Q <= a.skip_q) return;
   const int cap = a.max_blocks_per_seq << a.bs_shift;
   const int L = min(max(a.context_lens[s], 0), cap);
   const int i_end = min(Q, i0 + QT);
@@ -433,7 +435,8 @@ __global__ void __launch_bounds__(NW * 64) extend_dma_kernel(const ExtendArgs a)
   const int q0 = a.query_start_loc[s];
   const int Q = a.query_start_loc[s + 1] - q0;
   const int i0 = qt * QT;
-  if (Q <= 0 || i0 >= Q) return;  // whole workgroup
+  // whole workgroup: no query rows here, or a short query the grouped decode kernel takes
+  if (Q <= 0 || i0 >= Q || Q <= a.skip_q) return;
   const int cap = a.max_blocks_per_seq << a.bs_shift;
   const int L = min(max(a.context_lens[s], 0), cap);
   const int i_end = min(Q, i0 + QT);
@@ -825,6 +828,49 @@ extern "C" int pa_extend(const void* q, const void* k_pool, const void* v_pool,
     if (grid > INT_MAX) return PA_ERR_INVALID;
     hipStream_t st = (hipStream_t)stream;
     const int D = head_dim;
+    // Short queries (at most 16 / G new tokens, e.g. a few tokens checked at once): their
+    // G x Q query rows fill the 16 columns of the grouped decode kernel, which walks the
+    // sequence's blocks once for all of them with the context split over its waves (a
+    // causal end per row) instead of one wave walking it alone.
+    const int row_bytes = D * (kv_dtype == PA_FP8_E4M3 ? 1 : 2);
+    if ((G == 2 || G == 4 || G == 8) && block_size >= 16 && row_bytes >= 128 && row_bytes % 128 == 0) {
+      DecodeArgs d{};
+      d.q = q;
+      d.k_pool = k_pool;
+      d.v_pool = v_pool;
+      d.block_tables = block_tables;
+      d.context_lens = context_lens;
+      d.out = out;
+      d.num_seqs = num_seqs;
+      d.max_blocks_per_seq = max_blocks_per_seq;
+      d.num_blocks = num_blocks;
+      d.num_heads = num_heads;
+      d.num_kv_heads = num_kv_heads;
+      d.max_ctx = max_blocks_per_seq * block_size;
+      d.part_tokens = d.max_ctx;
+      d.num_parts = 1;
+      d.q_mul = a.q_mul;
+      d.out_mul = a.v_scale;
+      d.query_start_loc = query_start_loc;
+      LaunchSpec ls{};
+      ls.args = d;
+      ls.head_dim = D;
+      ls.block_size = block_size;
+      ls.group = G;
+      ls.grouped = true;
+      ls.grid = num_seqs * num_kv_heads;
+      ls.stream = st;
+      const bool large = block_size > 32;
+      int rc;
+      if (io_dtype == PA_F16)
+        rc = kv_dtype == PA_FP8_E4M3 ? (large ? launch_f16_fp8_large(ls) : launch_f16_fp8(ls))
+                                     : (large ? launch_f16_f16_large(ls) : launch_f16_f16(ls));
+      else
+        rc = kv_dtype == PA_FP8_E4M3 ? (large ? launch_bf16_fp8_large(ls) : launch_bf16_fp8(ls))
+                                     : (large ? launch_bf16_bf16_large(ls) : launch_bf16_bf16(ls));
+      if (rc != PA_OK) return rc;
+      a.skip_q = 16 / G;
+    }
     if (io_dtype == PA_F16)
       return kv_dtype == PA_FP8_E4M3 ? launch_ext_d<kF16, kFP8>(a, D, G, (int)grid, st)
                                      : launch_ext_d<kF16, kF16>(a, D, G, (int)grid, st);

@@ -89,14 +89,24 @@ __global__ void __launch_bounds__(NW * 64) grouped_decode_kernel(const DecodeArg
 
   const int S = a.num_seqs;
   const int H = a.num_heads;
-  const int ngroups = (S + NG - 1) / NG;
+  // decode: a group is NG consecutive sequences; short queries (extend): a group is one
+  // sequence and member i is its new token i, at position L - Q + i, attending over
+  // positions 0 .. L - Q + i through the sequence's one block table
+  const bool ext = a.query_start_loc != nullptr;
+  const int ngroups = ext ? S : (S + NG - 1) / NG;
   const int nsplit = a.num_parts;
   const int unit = xcd_unit((int)blockIdx.x, (int)gridDim.x);
   const int q = unit % nsplit;
   const int gg = unit / nsplit;  // KV-head major: gg = g * ngroups + group
   const int grp = gg % ngroups;
   const int g = gg / ngroups;
-  const int s0 = grp * NG;
+  const int s0 = ext ? grp : grp * NG;
+  int q0 = 0, Qs = 0;
+  if (ext) {
+    q0 = a.query_start_loc[grp];
+    Qs = a.query_start_loc[grp + 1] - q0;
+    if (Qs <= 0 || Qs > NG) return;  // whole workgroup: not a short query
+  }
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const LaneIds li(tid & 63);
@@ -106,15 +116,20 @@ __global__ void __launch_bounds__(NW * 64) grouped_decode_kernel(const DecodeArg
   // members' context lengths (uniform), the lane's own, and the group's longest
   int Lm[NG];
   int Lmax = 0;
+  const int Lseq = ext ? min(max(a.context_lens[s0], 0), a.max_ctx) : 0;
 #pragma unroll
   for (int i = 0; i < NG; ++i) {
-    Lm[i] = s0 + i < S ? min(max(a.context_lens[s0 + i], 0), a.max_ctx) : 0;
+    if (ext)
+      Lm[i] = i < Qs ? min(max(Lseq - Qs + i + 1, 0), a.max_ctx) : 0;
+    else
+      Lm[i] = s0 + i < S ? min(max(a.context_lens[s0 + i], 0), a.max_ctx) : 0;
     Lmax = max(Lmax, Lm[i]);
   }
   int L_own = 0;
 #pragma unroll
   for (int i = 0; i < NG; ++i) L_own = mi == i ? Lm[i] : L_own;
-  const int s_own = min(s0 + mi, S - 1);
+  // the query row of this lane: sequence s_own (decode) or new token q0 + mi (extend)
+  const int64_t s_own = ext ? (int64_t)q0 + min(mi, Qs - 1) : (int64_t)min(s0 + mi, S - 1);
 
   const int nch = (Lmax + 15) / 16;                                  // chunks of the group
   const int nk = nch > q ? (nch - q + nsplit - 1) / nsplit : 0;      // chunks of this split
@@ -128,7 +143,7 @@ __global__ void __launch_bounds__(NW * 64) grouped_decode_kernel(const DecodeArg
   // query operand: row rho's head, the same k order as the K rows of the lanes' loads
   vec qa[Geo::NST];
   {
-    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)s_own * H + g * G + rho % G) * D;
+    const uint16_t* qrow = (const uint16_t*)a.q + (s_own * H + g * G + rho % G) * D;
 #pragma unroll
     for (int i = 0; i < Geo::CPL; ++i) {
       const int col = Geo::VEC * (4 * i + li.lg);
@@ -148,6 +163,7 @@ __global__ void __launch_bounds__(NW * 64) grouped_decode_kernel(const DecodeArg
   const char* vbase = (const char*)a.v_pool + (int64_t)g * Sh::TILE_BYTES;
   const int32_t* bt0 = a.block_tables + (int64_t)s0 * a.max_blocks_per_seq;
   const int MB = a.max_blocks_per_seq;
+  const int mstride = ext ? 0 : MB;  // table row of member i: bt0 + i * mstride
   int w0 = 0;  // first chunk of the current window (in this wave's chunk order)
 
   // pass p of the current window: the loads of its chunk from its block
@@ -305,7 +321,7 @@ __global__ void __launch_bounds__(NW * 64) grouped_decode_kernel(const DecodeArg
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
       val[i] = live && 16 * c < Lm[i];
-      bid[i] = val[i] ? bt0[(int64_t)i * MB + (16 * c) / BS] : -1;
+      bid[i] = val[i] ? bt0[(int64_t)i * mstride + (16 * c) / BS] : -1;
     }
     // a pass for each member whose block no earlier member of the chunk maps it to
     bool lead[NG];
@@ -363,7 +379,9 @@ __global__ void __launch_bounds__(NW * 64) grouped_decode_kernel(const DecodeArg
     const int row = idx / D;
     const int d = idx % D;
     const int s = s0 + row / G;
-    if (s >= S) continue;
+    if (ext ? row / G >= Qs : s >= S) continue;
+    // output row: the member's sequence (decode) or its new token (extend)
+    const int64_t orow = ext ? (int64_t)q0 + row / G : (int64_t)s;
     float Mx = sm_m[row];
 #pragma unroll
     for (int w = 1; w < NW; ++w) Mx = fmaxf(Mx, sm_m[w * 16 + row]);
@@ -376,7 +394,7 @@ __global__ void __launch_bounds__(NW * 64) grouped_decode_kernel(const DecodeArg
     }
     const int h = g * G + row % G;
     if (nsplit == 1) {
-      store_io<IO>(a.out, ((int64_t)s * H + h) * D + d, lsum > 0.f ? (ov / lsum) * a.out_mul : 0.f);
+      store_io<IO>(a.out, (orow * H + h) * D + d, lsum > 0.f ? (ov / lsum) * a.out_mul : 0.f);
     } else {
       const int64_t slot = ((int64_t)s * H + h) * nsplit + q;
       a.ws[2 * NPH + slot * D + d] = ov * a.out_mul;

@@ -127,6 +127,36 @@ def test_extend_placement_invariance_bitwise():
         assert torch.equal(got, base), bs
 
 
+SHORT_SHAPES = [("f16", "f16", 2, 128, 16), ("bf16", "bf16", 4, 128, 32), ("bf16", "fp8_e4m3", 4, 128, 16),
+                ("f16", "fp8_e4m3", 8, 128, 256), ("bf16", "bf16", 8, 64, 16), ("f16", "f16", 4, 64, 64)]
+
+
+@pytest.mark.parametrize("io,kv,G,D,BS", SHORT_SHAPES, ids=[f"{a}-{b}-g{c}-d{d}-bs{e}" for a, b, c, d, e in
+                                                             SHORT_SHAPES])
+def test_extend_short_queries(io, kv, G, D, BS):
+    """Queries of at most 16 / G new tokens (several tokens checked at once) run on the
+    grouped decode kernel, one row per (new token, head) with its own causal end; longer
+    ones in the same call on the extend kernels. Query lengths around that cut, contexts
+    inside one block and across many; against the oracle, and the same bits under another
+    placement and block size."""
+    import torch
+    NG = 16 // G
+    Hkv = 2
+    lens = (1, 2, NG, NG + 1, 17, 40, 333, 1000, 2500, 64, 5)
+    qls = (1, 2, NG, NG + 1, max(1, NG - 1), 1, NG, NG + 1, 2, 40, NG)
+    spec = W.Spec(f"ext_short_{io}_{kv}_{G}_{D}_{BS}", len(lens), Hkv * G, Hkv, D, BS, io, kv,
+                  ("fixed", lens), seed=7300 + G + D + BS)
+    e = W.make_extend_batch(spec, ("fixed", qls), keep_logical=True)
+    log(f"[extend-short] {spec.name} Q={e.query_lens.tolist()}")
+    base = run_extend(e)
+    check(e, to_f64(base))
+    for bs, seed in ((16, 3), (64, 4)):
+        nb = W.repage(e.base, block_size=bs, seed=seed)
+        got = run_extend(W.ExtendBatch(base=nb, query_start_loc=e.query_start_loc, q=e.q))
+        torch.cuda.synchronize()
+        assert torch.equal(got, base), bs
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("name", sorted(W.EXTEND))
 def test_full_extend_sampled(name):
