@@ -322,8 +322,11 @@ int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_pairs, int n
  * outside the contract) are written as zeros. fp32 accumulation on the matrix cores:
  * io_dtype F16 or BF16 (F32 is PA_ERR_UNSUPPORTED), kv_dtype == io_dtype or
  * PA_FP8_E4M3, head_dim in {64, 128}, block_size a power of two in [8, 512],
- * num_heads / num_kv_heads in {1, 2, 4, 8}. max_query_len == 0 is a no-op. Asynchronous
- * on `stream`; allocates nothing. */
+ * num_heads / num_kv_heads in {1, 2, 4, 8}. max_query_len == 0 is a no-op. With 2, 4 or
+ * 8 query heads per KV head, block_size >= 16 and token rows of at least 128 bytes, the
+ * sequences with at most 16 / G new tokens are computed by a decode-style kernel (all
+ * their query rows walk the blocks together) enqueued before the prefill kernel, which
+ * then skips them. Asynchronous on `stream`; allocates nothing. */
 int pa_extend(const void* q, const void* k_pool, const void* v_pool,
               const int32_t* block_tables, const int32_t* context_lens,
               const int32_t* query_start_loc, int num_seqs, int max_blocks_per_seq,
