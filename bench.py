@@ -169,7 +169,15 @@ def cpu_baseline(b, seconds: float):
             "single_thread": {"value": round(one[0] / one[3] / 1e9, 6), "unit": "GB/s", "cores": 1,
                               "sample": f"{one[2]} units, {one[3]:.1f} s",
                               "seq_tokens_per_s": round(one[1] / one[3], 3)},
-            "host_cpus": os.cpu_count(), "affinity_cpus": affinity}
+            "host_cpus": os.cpu_count(), "affinity_cpus": affinity, "host_ram_gb": _host_ram_gb()}
+
+
+def _host_ram_gb():
+    try:
+        import psutil
+        return round(psutil.virtual_memory().total / 2**30, 1)
+    except Exception:  # psutil missing: not reported
+        return None
 
 
 # ----------------------------------------------------------------------------------
@@ -495,7 +503,7 @@ def bench_extend(args, name):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA16_PEAK_TFLOPS, 4), "traffic": None,
                      "kernel_ms": round(gpu_ms, 6), "algorithmic_flops_per_launch": flops},
-        "cpu_baseline": cpu,
+        "cpu_baseline": dict(cpu, gpu_over_oracle=round(value / cpu["value"], 1)) if cpu else cpu,
     }
     log(f"[bench] {wall_ms * 1e3:.2f} us/step wall, {gpu_ms * 1e3:.2f} us/step GPU (events): "
         f"{value:.1f} TFLOP/s, {res['kv_GB_per_s']:.0f} GB/s unique KV, mfma frac {achieved / MFMA16_PEAK_TFLOPS:.3f}")
@@ -660,7 +668,7 @@ def main():
                                   "(inside it when every (sequence, KV head) is run by one workgroup, "
                                   "else a second launch)"
                                   if mode == "partitioned" else "the decode launch(es) of the mode")},
-        "cpu_baseline": cpu,
+        "cpu_baseline": dict(cpu, gpu_over_oracle=round(value / cpu["value"], 1)) if cpu else cpu,
         "alt_modes": alt or None,
         "configs": subs or None,
         "stream_read_ceiling": ceiling,
