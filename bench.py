@@ -353,8 +353,9 @@ def measure_append(torch, pa, db: DeviceBatch, steps: int):
 def stream_read_ceiling(torch, pa, sizes, replica_bytes: float, steps: int):
     """Plain streaming read (pa_debug_stream_read: 16-byte loads, 1 KiB per wave
     instruction, nothing else) of buffers of the given sizes, cold like the decode steps
-    (replicas cycled, >= 2 GiB in all). Every (loads per thread, grid) pair of a small sweep
-    is timed with events over `steps` launches; the best is the ceiling for that size."""
+    (replicas cycled, >= 2 GiB in all). Every (load kind, loads per thread, grid) triple of
+    a small sweep is timed with events over `steps` launches; the best is the ceiling for
+    that size (also reported per load kind: plain and non-temporal)."""
     stream = torch.cuda.current_stream()
     sink = torch.zeros(256, dtype=torch.int32, device="cuda")
     out = {}
@@ -366,25 +367,32 @@ def stream_read_ceiling(torch, pa, sizes, replica_bytes: float, steps: int):
         for t in bufs:
             t.fill_(1)
         best = None
+        best_kind = {}
         sweep = []
-        for unroll in (4, 8, 16):
-            for wgs in (0, 2048, 4096, 8192):
-                def step(i, unroll=unroll, wgs=wgs):
-                    rc = pa._lib.lib().pa_debug_stream_read(bufs[i % R].data_ptr(), nbytes, unroll, wgs,
-                                                            sink.data_ptr(), stream.cuda_stream)
-                    if rc != 0:
-                        raise pa.PagedAttentionError("pa_debug_stream_read", rc)
-                _, gpu_ms = time_steps(torch, step, 3, steps, stream)
-                gbs = nbytes / (gpu_ms * 1e-3) / 1e9
-                sweep.append((unroll, wgs, round(gpu_ms * 1e3, 2), round(gbs, 1)))
-                if best is None or gbs > best[3]:
-                    best = (unroll, wgs, gpu_ms, gbs)
+        for nt in (0, 1):
+            for unroll in (4, 8, 16):
+                for wgs in (0, 2048, 4096, 8192):
+                    def step(i, unroll=unroll, wgs=wgs, nt=nt):
+                        rc = pa._lib.lib().pa_debug_stream_read(bufs[i % R].data_ptr(), nbytes, unroll, wgs, nt,
+                                                                sink.data_ptr(), stream.cuda_stream)
+                        if rc != 0:
+                            raise pa.PagedAttentionError("pa_debug_stream_read", rc)
+                    _, gpu_ms = time_steps(torch, step, 3, steps, stream)
+                    gbs = nbytes / (gpu_ms * 1e-3) / 1e9
+                    sweep.append(("nt" if nt else "plain", unroll, wgs, round(gpu_ms * 1e3, 2), round(gbs, 1)))
+                    if best is None or gbs > best[3]:
+                        best = (unroll, wgs, gpu_ms, gbs, nt)
+                    kind = "nontemporal" if nt else "plain"
+                    if kind not in best_kind or gbs > best_kind[kind]["GB_per_s"]:
+                        best_kind[kind] = {"GB_per_s": round(gbs, 1), "us": round(gpu_ms * 1e3, 2)}
         out[label] = {"bytes": nbytes, "GB_per_s": round(best[3], 1),
                       "pct_of_hbm_peak": round(100 * best[3] / HBM_PEAK_GBS, 2),
                       "us": round(best[2] * 1e3, 2), "unroll": best[0], "workgroups": best[1] or "one pass",
-                      "sweep_unroll_wgs_us_GBps": sweep}
-        log(f"[bench] stream read {label}: best {best[3]:.0f} GB/s ({best[2] * 1e3:.1f} us, unroll {best[0]}, "
-            f"wgs {best[1] or 'one pass'})")
+                      "loads": "nontemporal" if best[4] else "plain", "by_load_kind": best_kind,
+                      "sweep_kind_unroll_wgs_us_GBps": sweep}
+        log(f"[bench] stream read {label}: best {best[3]:.0f} GB/s ({best[2] * 1e3:.1f} us, "
+            f"{'non-temporal' if best[4] else 'plain'} loads, unroll {best[0]}, wgs {best[1] or 'one pass'}); "
+            f"plain {best_kind['plain']['GB_per_s']:.0f} GB/s")
         del bufs
     return out
 

@@ -360,9 +360,11 @@ int pa_debug_fp8_to_16bit(const uint8_t* codes, uint16_t* out, int n, int out_dt
  * the loads each thread issues before using any; bytes must be a positive multiple of
  * 4096 * unroll and buf 16-byte aligned. num_workgroups 0 gives every workgroup one
  * iteration (bytes / (4096 * unroll) workgroups), else the workgroups stride over the
- * buffer. sink: 256 uint32 of device memory, almost never written (only when the folded
- * words hit a fixed pattern). PA_ERR_INVALID on other arguments. Asynchronous on `stream`. */
-int pa_debug_stream_read(const void* buf, size_t bytes, int unroll, int num_workgroups,
+ * buffer. nontemporal 1 marks the loads non-temporal (as the split-context stream does),
+ * 0 leaves them plain. sink: 256 uint32 of device memory, almost never written (only when
+ * the folded words hit a fixed pattern). PA_ERR_INVALID on other arguments. Asynchronous on
+ * `stream`. */
+int pa_debug_stream_read(const void* buf, size_t bytes, int unroll, int num_workgroups, int nontemporal,
                          uint32_t* sink, void* stream);
 
 /* ---------------------------------------------------------------------------------

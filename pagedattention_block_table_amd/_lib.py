@@ -47,7 +47,7 @@ SIGNATURES = {
     "pa_extend": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _F, _F, _P, _P]),
     "pa_debug_fp8_to_f32": (_I, [_P, _P, _I, _P]),
     "pa_debug_fp8_to_16bit": (_I, [_P, _P, _I, _I, _P]),
-    "pa_debug_stream_read": (_I, [_P, _SZ, _I, _I, _P, _P]),
+    "pa_debug_stream_read": (_I, [_P, _SZ, _I, _I, _I, _P, _P]),
     "pa_bm_create": (_P, [_I, _I, _I, _I]),
     "pa_bm_destroy": (None, [_P]),
     "pa_bm_num_free": (_I, [_P]),

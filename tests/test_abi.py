@@ -220,13 +220,14 @@ def test_small_entry_points_reject():
     assert L.pa_debug_fp8_to_16bit(FAKE, FAKE, 16, _lib.PA_F32, None) == _lib.PA_ERR_INVALID
     assert L.pa_debug_fp8_to_16bit(FAKE, FAKE, 16, _lib.PA_FP8_E4M3, None) == _lib.PA_ERR_INVALID
     # streaming-read probe: bytes a positive multiple of 4096 * unroll, unroll 4 / 8 / 16
-    assert L.pa_debug_stream_read(0, 4096 * 4, 4, 0, FAKE, None) == _lib.PA_ERR_INVALID
-    assert L.pa_debug_stream_read(FAKE, 4096 * 4, 4, 0, 0, None) == _lib.PA_ERR_INVALID
-    assert L.pa_debug_stream_read(FAKE, 0, 4, 0, FAKE, None) == _lib.PA_ERR_INVALID
-    assert L.pa_debug_stream_read(FAKE, 4096 * 4 + 16, 4, 0, FAKE, None) == _lib.PA_ERR_INVALID
-    assert L.pa_debug_stream_read(FAKE, 4096 * 8, 6, 0, FAKE, None) == _lib.PA_ERR_INVALID
-    assert L.pa_debug_stream_read(FAKE + 8, 4096 * 8, 8, 0, FAKE, None) == _lib.PA_ERR_INVALID
-    assert L.pa_debug_stream_read(FAKE, 4096 * 8, 8, -1, FAKE, None) == _lib.PA_ERR_INVALID
+    assert L.pa_debug_stream_read(0, 4096 * 4, 4, 0, 0, FAKE, None) == _lib.PA_ERR_INVALID
+    assert L.pa_debug_stream_read(FAKE, 4096 * 4, 4, 0, 0, 0, None) == _lib.PA_ERR_INVALID
+    assert L.pa_debug_stream_read(FAKE, 0, 4, 0, 0, FAKE, None) == _lib.PA_ERR_INVALID
+    assert L.pa_debug_stream_read(FAKE, 4096 * 4 + 16, 4, 0, 0, FAKE, None) == _lib.PA_ERR_INVALID
+    assert L.pa_debug_stream_read(FAKE, 4096 * 8, 6, 0, 0, FAKE, None) == _lib.PA_ERR_INVALID
+    assert L.pa_debug_stream_read(FAKE + 8, 4096 * 8, 8, 0, 0, FAKE, None) == _lib.PA_ERR_INVALID
+    assert L.pa_debug_stream_read(FAKE, 4096 * 8, 8, -1, 0, FAKE, None) == _lib.PA_ERR_INVALID
+    assert L.pa_debug_stream_read(FAKE, 4096 * 8, 8, 0, 2, FAKE, None) == _lib.PA_ERR_INVALID
 
 
 def test_noalloc_refuses_requests_beyond_its_scratch():
