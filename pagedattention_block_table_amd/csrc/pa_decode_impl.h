@@ -463,9 +463,11 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // 16-byte K/V load. NT: marked non-temporal (the cache is not to keep the line), for
 // streams that read each byte once: the split-context stream over long contexts reads
-// 4.3 GB in 631 instead of 699 us that way. Where the cache serves repeats (prefix blocks
-// shared by several sequences) or the batch is small, plain loads are faster (shared-prefix
-// batch 33.8 against 39.4 us, LLaMA-7B batch 28.8 against 30.5 us).
+// 4.3 GB in 630 instead of 699 us that way, and the one-workgroup-per-head kernel in 632
+// instead of 698 us with only its K loads so marked. Where the cache serves repeats
+// (prefix blocks shared by several sequences) plain loads are faster (matrix-core engine
+// on a shared-prefix batch: 34.0 against 38.3 us), and on a small batch (LLaMA-7B, 4K
+// contexts) non-temporal V loads cost 7% while non-temporal K loads cost nothing.
 template <bool NT = false>
 __device__ __forceinline__ uint4 load16(const char* p) {
   if constexpr (NT) {
@@ -484,13 +486,14 @@ struct StepBuf {
   uint4 vr[U][Geo::NL];
 };
 
-// Issue the K/V loads of the step whose first (sub-)block is j0 (j0 * SB < t_end), with
-// bid[u] the physical block of (sub-)block j0 + u. A lane whose row is at or past t_end
-// reads row j0 * SB instead (finite data of this step; the score of such a row is
-// excluded by select, so its probability is exactly 0). Every load is unconditional:
+// Issue the K/V loads of the step whose first (sub-)block is j0, with bid[u] the physical
+// block of (sub-)block j0 + u. A lane whose row is at or past t_end reads row j0 * SB
+// instead (finite data of this step; the score of such a row is excluded by select, so its
+// probability is exactly 0; with t_end <= j0 * SB every lane reads that row). Every load is unconditional:
 // loads under a branch make the compiler wait for every outstanding load, those of the
 // next step included, before the step's data is used.
-template <int KV, int D, int BS, int G, int U, bool NT = false>
+// NTK / NTV: K / V loads marked non-temporal.
+template <int KV, int D, int BS, int G, int U, bool NTK = false, bool NTV = NTK>
 __device__ __forceinline__ void issue_step(StepBuf<KV, D, BS, G, U>& b, const char* kbase, const char* vbase,
                                            int64_t blk_stride, const int (&bid)[U], int j0, int t_end,
                                            int r, int c) {
@@ -507,8 +510,8 @@ __device__ __forceinline__ void issue_step(StepBuf<KV, D, BS, G, U>& b, const ch
     for (int i = 0; i < NL; ++i) {
       const int t = (j0 + u) * SB + i * TPL + r;
       const int64_t off = t < t_end ? tile + lane_off + i * TPL * Geo::ROW_BYTES : first;
-      b.kr[u][i] = load16<NT>(kbase + off);
-      b.vr[u][i] = load16<NT>(vbase + off);
+      b.kr[u][i] = load16<NTK>(kbase + off);
+      b.vr[u][i] = load16<NTV>(vbase + off);
     }
   }
 }
@@ -743,8 +746,8 @@ decode_kernel(const DecodeArgs a) {
   const char* vbase = (const char*)a.v_pool + (int64_t)g * Geo::TILE;
 
   // This wave's steps k = 0 .. nwc-1 start at (sub-)block j_begin + (wave + k NW) U; the
-  // loads of kVecDepth steps are in flight. Past the last step the issue repeats step
-  // nwc - 1 (cached data, never consumed), so that the loop issues unconditionally.
+  // loads of kVecDepth steps are in flight. Past the last step the issue reads the first
+  // row of step nwc - 1 (never consumed), so that the loop issues unconditionally.
   const int steps = (j_end - j_begin + U - 1) / U;
   const int nwc = wave < steps ? (steps - wave + NW - 1) / NW : 0;
   if (nwc > 0) {
@@ -761,7 +764,10 @@ decode_kernel(const DecodeArgs a) {
     auto issue = [&](Buf& b, int k) {
       int bid[U];
       tw.ids(min(k, nwc - 1), a.num_blocks, bid);
-      issue_step<KV, D, BS, G, U>(b, kbase, vbase, blk_stride, bid, j0_of(k), t_end, r, c);
+      // a step past the wave's last is never consumed: its lanes all read the step's first
+      // row (one row instead of the step, so that non-temporal loads fetch no step twice)
+      issue_step<KV, D, BS, G, U, true, false>(b, kbase, vbase, blk_stride, bid, j0_of(k), k < nwc ? t_end : 0,
+                                               r, c);
     };
     Buf buf[kVecDepth];
 #pragma unroll
@@ -1029,8 +1035,9 @@ decode_stream_kernel(const DecodeArgs a) {
   auto issue = [&](Buf& b, int k) {
     int bid[U];
     tw.ids(min(k, nsteps - 1), a.num_blocks, bid);
-    // each K/V byte of the run is read once: non-temporal loads
-    issue_step<KV, D, BS, G, U, true>(b, kbase, vbase, blk_stride, bid, j0_of(k), L, r, c);
+    // each K/V byte of the run is read once: non-temporal loads; a step past the run's
+    // last (never consumed) reads only its first row
+    issue_step<KV, D, BS, G, U, true>(b, kbase, vbase, blk_stride, bid, j0_of(k), k < nsteps ? L : 0, r, c);
   };
   Buf buf[SD];
 #pragma unroll

@@ -166,8 +166,9 @@ __global__ void __launch_bounds__(NW * 64) grouped_decode_kernel(const DecodeArg
   const int mstride = ext ? 0 : MB;  // table row of member i: bt0 + i * mstride
   int w0 = 0;  // first chunk of the current window (in this wave's chunk order)
 
-  // pass p of the current window: the loads of its chunk from its block
-  auto issue = [&](Buf& b, int p) {
+  // pass p of the current window: the loads of its chunk from its block (live = false:
+  // not consumed, every lane reads the chunk's first row)
+  auto issue = [&](Buf& b, int p, bool live) {
     const int2 d = wl.pass[p];
     const int bid = min(max(__builtin_amdgcn_readfirstlane(d.x), 0), a.num_blocks - 1);
     const int dy = __builtin_amdgcn_readfirstlane(d.y);
@@ -185,8 +186,9 @@ __global__ void __launch_bounds__(NW * 64) grouped_decode_kernel(const DecodeArg
     const char* vb = vbase + (int64_t)bid * blk_stride;
     // rows at or past every member's context end read the chunk's first row instead
     // (finite data of this block; those rows are masked for every member)
+    const int lim = live ? lmax : 0;
     int to = c0 + li.n;
-    to = to < lmax ? to : c0;
+    to = to < lim ? to : c0;
     const char* krow = kb + (to % BS) * RB;
 #pragma unroll
     for (int i = 0; i < Geo::CPL; ++i) b.kr[i] = load16(krow + 16 * (4 * i + li.lg));
@@ -194,7 +196,7 @@ __global__ void __launch_bounds__(NW * 64) grouped_decode_kernel(const DecodeArg
     for (int i = 0; i < NV; ++i) {
       const int byte = 1024 * i + 16 * li.lane;
       int t = c0 + byte / RB;
-      t = t < lmax ? t : c0;
+      t = t < lim ? t : c0;
       b.vt.v[i] = load16(vb + (t % BS) * RB + byte % RB);
     }
   };
@@ -309,7 +311,7 @@ __global__ void __launch_bounds__(NW * 64) grouped_decode_kernel(const DecodeArg
     using Buf = GroupBuf<KV, D>;
     decltype(issue)& iss;
     decltype(consume)& con;
-    __device__ __forceinline__ void issue(const DecodeArgs&, Buf& b, int k) { iss(b, k); }
+    __device__ __forceinline__ void issue(const DecodeArgs&, Buf& b, int k, bool live) { iss(b, k, live); }
     __device__ __forceinline__ void consume(const DecodeArgs&, const Buf& b, int k) { con(b, k); }
   };
   for (; w0 < nwk; w0 += 64) {

@@ -141,22 +141,24 @@ constexpr int kPipeDepth = PA_PIPE_DEPTH;
 
 // Drive an engine's issue / consume over a wave's nwc chunks with kPipeDepth register
 // buffers (the buffer index is a compile-time constant after unrolling). The steady-state
-// loop issues unconditionally: past the last chunk it re-issues chunk nwc - 1 (cached
-// data, never consumed). With every path into the loop header issuing the same loads in
-// the same order, the compiler waits only for the buffer being consumed; a conditional
-// issue would make it wait for the loads of the following chunks as well.
+// loop issues unconditionally: past the last chunk it issues chunk nwc - 1 again with
+// live = false, for which the engine reads only the chunk's first row (never consumed).
+// With every path into the loop header issuing the same loads in the same order, the
+// compiler waits only for the buffer being consumed; a conditional issue would make it
+// wait for the loads of the following chunks as well.
 template <class Eng>
 __device__ __forceinline__ void run_pipelined(Eng& eng, const DecodeArgs& a, int nwc) {
   if (nwc <= 0) return;
   typename Eng::Buf b[kPipeDepth];
 #pragma unroll
-  for (int d = 0; d < kPipeDepth; ++d) eng.issue(a, b[d], min(d, nwc - 1));
+  for (int d = 0; d < kPipeDepth; ++d) eng.issue(a, b[d], min(d, nwc - 1), d < nwc);
   int k = 0;
   for (; k + kPipeDepth <= nwc; k += kPipeDepth) {
 #pragma unroll
     for (int d = 0; d < kPipeDepth; ++d) {
       eng.consume(a, b[d], k + d);
-      eng.issue(a, b[d], min(k + d + kPipeDepth, nwc - 1));
+      const int kn = k + d + kPipeDepth;
+      eng.issue(a, b[d], min(kn, nwc - 1), kn < nwc);
     }
   }
 #pragma unroll
@@ -371,7 +373,8 @@ struct MfmaTEngine {
     return bo;
   }
 
-  __device__ __forceinline__ void issue(const DecodeArgs& a, Buf& b, int k) {
+  // live = false: the chunk is not consumed and every lane reads its first row
+  __device__ __forceinline__ void issue(const DecodeArgs& a, Buf& b, int k, bool live) {
     if ((k >> 6) != cur_win) {
       cur_win = k >> 6;
 #pragma unroll
@@ -385,10 +388,11 @@ struct MfmaTEngine {
     const int jb = c0 / BS;
     // Rows at or past t_end read token c0's row instead (finite data already being
     // fetched; their scores are excluded by select): every load is unconditional.
+    const int te = live ? t_end : 0;
 #pragma unroll
     for (int tau = 0; tau < NT; ++tau) {
       int to = c0 + 16 * tau + li.n;  // K: lane (n, lg) loads chunks 4i + lg of token n
-      to = to < t_end ? to : c0;
+      to = to < te ? to : c0;
       const char* krow = kbase + tok_block(off, to, jb) + (to % BS) * RB;
 #pragma unroll
       for (int i = 0; i < Geo::CPL; ++i) b.kr[tau][i] = load16(krow + 16 * (4 * i + li.lg));
@@ -396,7 +400,7 @@ struct MfmaTEngine {
       for (int i = 0; i < NV; ++i) {  // V: instruction i covers bytes 1024 i .. of the tile's 16 rows
         const int byte = 1024 * i + 16 * li.lane;
         int t = c0 + 16 * tau + byte / RB;
-        t = t < t_end ? t : c0;
+        t = t < te ? t : c0;
         b.vt[tau].v[i] = load16(vbase + tok_block(off, t, jb) + (t % BS) * RB + byte % RB);
       }
     }
