@@ -387,7 +387,10 @@ struct MfmaTEngine {
     const int c0 = chunk_token(k);
     const int jb = c0 / BS;
     // Rows at or past t_end read token c0's row instead (finite data already being
-    // fetched; their scores are excluded by select): every load is unconditional.
+    // fetched; their scores are excluded by select): every load is unconditional. V loads
+    // are non-temporal, K loads plain: the mixed fp8 batch takes 196 instead of 213 us and
+    // the 8-head batch 99 instead of 108, while the shared-prefix batch, whose K rows L2
+    // serves to every sequence, keeps its time (non-temporal K: 38.7 against 34.6 us).
     const int te = live ? t_end : 0;
 #pragma unroll
     for (int tau = 0; tau < NT; ++tau) {
@@ -401,7 +404,7 @@ struct MfmaTEngine {
         const int byte = 1024 * i + 16 * li.lane;
         int t = c0 + 16 * tau + byte / RB;
         t = t < te ? t : c0;
-        b.vt[tau].v[i] = load16(vbase + tok_block(off, t, jb) + (t % BS) * RB + byte % RB);
+        b.vt[tau].v[i] = load16<true>(vbase + tok_block(off, t, jb) + (t % BS) * RB + byte % RB);
       }
     }
   }
