@@ -192,8 +192,10 @@ size_t pa_ordered_workspace_bytes(int num_seqs);
  * context lengths alone (a class histogram and a prefix sum in LDS), and each XCD's share
  * of the (KV head, sequence) units is handed out longest sequence first, so that batches
  * mixing short and long contexts ([P2] §5.3's length mix) do not end with a few long
- * sequences running alone. workspace and workspace_bytes are not used (NULL and 0 are
- * fine). Errors as pa_decode. */
+ * sequences running alone. Batches of more than 2048 sequences are dispatched in index
+ * order, as by pa_decode: every workgroup reads all the lengths to find its rank, which
+ * costs more there than the tail it removes. workspace and workspace_bytes are not used
+ * (NULL and 0 are fine). Errors as pa_decode. */
 int pa_decode_ordered(const void* q, const void* k_pool, const void* v_pool,
                       const int32_t* block_tables, const int32_t* context_lens,
                       int num_seqs, int max_blocks_per_seq, int num_blocks,

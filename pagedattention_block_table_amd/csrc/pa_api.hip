@@ -518,8 +518,9 @@ int run(const Common& c, Mode mode, int max_context_len, int P, int nwg, void* w
     m.fixed_parts = nsplit;
     return launch_merge(c.io, c.D, m, c.S * c.H, st);
   }
-  if (mode == Mode::kOrdered) {
-    // the decode launch derives the longest-first order itself (no workspace)
+  if (mode == Mode::kOrdered && c.S <= kOrderLdsSeqs) {
+    // the decode launch derives the longest-first order itself (no workspace); larger
+    // batches keep the index order (same result)
     ls.args.ordered = 1;
     ls.args.order_hpx = c.Hkv % 8 == 0 ? c.Hkv / 8 : 0;
   }

@@ -86,3 +86,20 @@ def test_ordered_rank_selection_edges(S):
         ref = run(b, dev, "direct")
         torch.cuda.synchronize()
         assert torch.equal(got, ref), (S, kind[0])
+
+
+@pytest.mark.parametrize("S", [2047, 2048, 2049, 4100])
+def test_ordered_large_batches(S):
+    """Batch sizes at and past the 2048 sequences that take the longest-first dispatch
+    (larger batches keep the index order), with one length class and with several: each
+    (sequence, KV head) computed exactly once (bits of pa_decode)."""
+    import torch
+    for kind in (("const", 16), ("choice", (1, 7, 16, 17, 40, 100), (0.1, 0.1, 0.3, 0.2, 0.2, 0.1))):
+        sp = W.Spec(f"ordered_large_{S}", S, 4, 1, 64, 16, "f16", "f16", kind, seed=700 + S % 97)
+        b = W.make_batch(sp)
+        dev = to_device(b)
+        log(f"[ordered-large] S={S} {kind[0]} sumL={int(b.context_lens.sum())}")
+        got = run(b, dev, "ordered")
+        ref = run(b, dev, "direct")
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), (S, kind[0])
