@@ -50,6 +50,7 @@ struct GroupShape {
   static constexpr int NV = VTileRegs<KV, D>::NV;
   static constexpr int VT_ROW = D + 16;
   static constexpr int VT_BYTES = 16 * VT_ROW * 2;
+  static constexpr int KT_ROW = RB + 16;  // bytes per K row staged in the V tile's LDS
   static constexpr int MAXP = 64 * NG;  // passes of one window of 64 chunks
   static constexpr int PVT = KV == kBF16 ? kBF16 : kF16;
   static constexpr bool SPLIT_P = PVT == kBF16;
@@ -61,10 +62,12 @@ struct GroupShape {
   static constexpr int MERGE_BYTES = NW * 16 * (D + 2) * 4;
   static constexpr int LDS_BYTES = LOOP_BYTES > MERGE_BYTES ? LOOP_BYTES : MERGE_BYTES;
   static constexpr bool ok = (G == 2 || G == 4 || G == 8) && BS >= 16 && mfma_supported<IO, KV, D, G>();
+  static_assert(!ok || 16 * KT_ROW <= VT_BYTES, "K tile fits the V tile's LDS");
 };
 
-// Registers of one pass in flight: the chunk's K rows of the lane's token and its share of
-// the V rows, plus the pass's chunk start, member mask and load bound.
+// Registers of one pass in flight: the lane's share of the chunk's K rows and of its V
+// rows, both in memory order (instruction i, lane l: bytes 1024 i + 16 l of the chunk's 16
+// rows), plus the pass's chunk start, member mask and load bound.
 template <int KV, int D>
 struct GroupBuf {
   uint4 kr[MfmaGeo<KV, D>::CPL];
@@ -185,13 +188,16 @@ __global__ void __launch_bounds__(NW * 64) grouped_decode_kernel(const DecodeArg
     const char* kb = kbase + (int64_t)bid * blk_stride;
     const char* vb = vbase + (int64_t)bid * blk_stride;
     // rows at or past every member's context end read the chunk's first row instead
-    // (finite data of this block; those rows are masked for every member)
+    // (finite data of this block; those rows are masked for every member). K, like V, in
+    // whole 1 KiB runs of the chunk's 16 contiguous rows (put into the MFMA layout through
+    // LDS when consumed)
     const int lim = live ? lmax : 0;
-    int to = c0 + li.n;
-    to = to < lim ? to : c0;
-    const char* krow = kb + (to % BS) * RB;
+    const char* kchunk = kb + (c0 % BS) * RB;
 #pragma unroll
-    for (int i = 0; i < Geo::CPL; ++i) b.kr[i] = load16(krow + 16 * (4 * i + li.lg));
+    for (int i = 0; i < Geo::CPL; ++i) {
+      const int byte = 1024 * i + 16 * li.lane;
+      b.kr[i] = load16(kchunk + (c0 + byte / RB < lim ? byte : byte % RB));
+    }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int byte = 1024 * i + 16 * li.lane;
@@ -213,12 +219,14 @@ __global__ void __launch_bounds__(NW * 64) grouped_decode_kernel(const DecodeArg
       for (int i = 0; i < NG; ++i) {
         if (!((mask >> i) & 1)) continue;
         const int64_t row0 = ((int64_t)(s0 + i) * a.num_kv_heads + g) * a.dbg_max_ctx;
-        const int to = c0 + li.n;
-        if (to < Lm[i]) {
 #pragma unroll
-          for (int k = 0; k < Geo::CPL; ++k)
-            *(uint4*)((char*)a.dbg_k + (row0 + to) * RB + 16 * (4 * k + li.lg)) = b.kr[k];
-          if (li.lg == 0) atomicAdd(a.dbg_counts + row0 + to, 1);
+        for (int k = 0; k < Geo::CPL; ++k) {
+          const int byte = 1024 * k + 16 * li.lane;
+          const int t = c0 + byte / RB;
+          if (t < Lm[i]) {
+            *(uint4*)((char*)a.dbg_k + (row0 + t) * RB + byte % RB) = b.kr[k];
+            if (byte % RB == 0) atomicAdd(a.dbg_counts + row0 + t, 1);
+          }
         }
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
@@ -229,6 +237,18 @@ __global__ void __launch_bounds__(NW * 64) grouped_decode_kernel(const DecodeArg
       }
     }
     // the previous pass's transposed reads come before these writes
+    MfmaTEngine<IO, KV, D, BS, G, 1, DBG>::lds_exchange();
+    // K into the MFMA layout (lane (n, lg): row n, chunks 4i + lg) through the tile,
+    // read back before V overwrites it
+    uint4 kr[Geo::CPL];
+#pragma unroll
+    for (int i = 0; i < Geo::CPL; ++i) {
+      const int byte = 1024 * i + 16 * li.lane;
+      *(uint4*)(wl.vt + (byte / RB) * Sh::KT_ROW + byte % RB) = b.kr[i];
+    }
+    MfmaTEngine<IO, KV, D, BS, G, 1, DBG>::lds_exchange();
+#pragma unroll
+    for (int i = 0; i < Geo::CPL; ++i) kr[i] = *(const uint4*)(wl.vt + li.n * Sh::KT_ROW + 16 * (4 * i + li.lg));
     MfmaTEngine<IO, KV, D, BS, G, 1, DBG>::lds_exchange();
     uint16_t* vt = (uint16_t*)wl.vt;
 #pragma unroll
@@ -260,7 +280,7 @@ __global__ void __launch_bounds__(NW * 64) grouped_decode_kernel(const DecodeArg
     for (int i = 0; i < Geo::CPL; ++i)
 #pragma unroll
       for (int hf = 0; hf < Geo::VEC / 8; ++hf)
-        cs = Mma<IO>::mma(k_operand<IO, KV>(b.kr[i], hf), qa[i * (Geo::VEC / 8) + hf], cs);
+        cs = Mma<IO>::mma(k_operand<IO, KV>(kr[i], hf), qa[i * (Geo::VEC / 8) + hf], cs);
     float z[4];
     float mx = -INFINITY;
 #pragma unroll
