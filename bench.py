@@ -43,7 +43,7 @@ MFMA16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 matrix peak, AMD publish
 EXTEND_METRIC = "paged extend (chunked prefill) attention TFLOP/s, causal algorithmic flops"
 METRIC = "paged-attn decode KV GB/s read and % of MI355X HBM peak; seqs·tokens/s"
 HEADLINE_CONFIG = 3
-DEFAULT_MODE = {0: "direct", 1: "ordered", 2: "direct", 3: "partitioned", 4: "ordered",
+DEFAULT_MODE = {0: "direct", 1: "direct", 2: "direct", 3: "partitioned", 4: "ordered",
                 "llama7b_fp16_bs128": "direct", "shared_prefix_bf16_bs256": "direct",
                 "long_ctx_fp16_bs512": "ordered", "mixed_fp8_bs256": "ordered",
                 "llama70b_gqa8_bf16": "ordered", "d256_gqa2_bf16": "direct",
